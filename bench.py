@@ -1,0 +1,400 @@
+#!/usr/bin/env python3
+"""Benchmark of DDTree tree-verify MLA attention on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload kimi5553|long200k|full61|sweep]
+
+A step is one pass of the whole hot path over one batch of synthetic input: the ancestor mask of the draft
+tree (kdv_build_tree_mask) and tree-verify attention for one layer (kdv_verify_mla_attn: q absorption,
+split-KV MFMA pass, split combine, W_UV up-projection); for `full61` a step is one mask and 61 layers.
+
+Timing: W eager warm-up steps, then the K timed steps are captured in one HIP graph (so host launch cost is
+not counted) and replayed once between two device synchronisations, timed with HIP events on the stream the
+kernels run on.  "Cold" rotates the steps over distinct copies of the layer's buffers totalling more than
+512 MiB (twice the 256 MiB Infinity Cache) as a real multi-layer model would; "hot" reuses one copy.
+The split-KV kernel's own time comes from HIP events recorded between the four kernels (eager launches of
+the same steps, queued behind a spin kernel so that no host gap falls between the events).  Work counts are algorithmic: masked tree entries and padding are not counted.
+
+Prints ONE JSON line.  Inputs are seeded synthetic data with the shapes of the pages' workloads.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "tree-verify MLA attn µs/layer + TFLOP/s (% MFMA peak), 64 heads, 15 nodes, ctx 5553"
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, vendor figure
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, vendor figure
+COLD_BYTES = 576 << 20
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------------------------------------ work model
+def depths(parent):
+    d = []
+    for t in range(len(parent)):
+        k, j = 0, t
+        while parent[j] != -1:
+            j = int(parent[j])
+            k += 1
+        d.append(k)
+    return np.array(d)
+
+
+def work(H, Dn, Dr, R, Dv, L, T, parent):
+    """Algorithmic FLOPs and HBM bytes of one layer (visible rows only)."""
+    n_t = L + depths(parent) + 1
+    sn = float(n_t.sum())
+    f_absorb = 2.0 * H * T * Dn * R
+    f_scores = 2.0 * H * sn * (R + Dr)
+    f_pv = 2.0 * H * sn * R
+    f_up = 2.0 * H * T * R * Dv
+    N = L + T
+    b = N * (R + Dr) * 2 + H * (Dn + Dv) * R * 2 + T * H * (Dn + Dr) * 2 + T * H * Dv * 2 + 4 * N
+    return dict(flops=f_absorb + f_scores + f_pv + f_up, flops_splitkv=f_scores + f_pv, bytes=float(b),
+                bytes_splitkv=float(N * (R + Dr) * 2 + T * H * (R + Dr) * 2 + 4 * N))
+
+
+# ------------------------------------------------------------------------------------------------ HIP events
+class Hip:
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so.7")  # by soname: the runtime torch already loaded
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        rc = self.lib.hipEventCreate(ctypes.byref(e))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed ({rc})")
+        return e.value
+
+    def record(self, e, stream):
+        rc = self.lib.hipEventRecord(e, stream)
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_ms(self, a, b):
+        self.lib.hipEventSynchronize(b)
+        ms = ctypes.c_float()
+        rc = self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(ms.value)
+
+
+# ------------------------------------------------------------------------------------------------ workloads
+class Layer:
+    """Device buffers of one layer + the raw pointers the C ABI takes."""
+
+    def __init__(self, t, pool_slots):
+        self.t = t
+        self.pool_slots = pool_slots
+
+    def ptrs(self):
+        t = self.t
+        return [t["q_nope"].data_ptr(), t["q_rope"].data_ptr(), t["w_uk"].data_ptr(), t["w_uv"].data_ptr(),
+                t["c_kv"].data_ptr(), t["k_pe"].data_ptr()]
+
+
+def clone_layer(t):
+    return {k: v.clone() for k, v in t.items()}
+
+
+def build_workload(name, torch, si):
+    """Returns (description, dims, L, T, parent, page_table tensor, [layers], layers_per_step, numpy inputs)."""
+    if name == "kimi5553":
+        inp = si.kimi(L=5553, T=15, seed=0, dist="literal")
+        desc = ("tree-verify MLA attention (absorbed), 64 heads, 15-node random tree, 5553-token prefix, "
+                "contiguous bf16 latent cache, dims nope/rope/rank/v = 128/64/512/128")
+        return desc, inp, 1
+    if name == "long200k":
+        inp = si.long_fragmented(seed=0, dist="literal")
+        desc = ("tree-verify MLA attention (absorbed), 64 heads, 15-node random tree, 200000-token prefix "
+                "scattered over a 262144-slot page_size=1 pool")
+        return desc, inp, 1
+    if name == "full61":
+        desc = ("verify-step attention, 61 layers x 8 heads, 32-node tree (depth <= 16), 131072-token prefix "
+                "scattered over a 262144-slot pool, per-layer buffers")
+        return desc, None, 61
+    raise SystemExit(f"unknown workload {name}")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="kimi5553", choices=["kimi5553", "long200k", "full61"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of one HIP graph")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build measures one GPU only: the tree-verify attention of one layer "
+                                   "runs on a single MI355X; multi-GPU sharding is described in DESIGN.md, "
+                                   "not run", "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+
+    import torch
+    import synth_inputs as si
+    import speculative_decoding_tree_parent_amd as kdv
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU (gfx950)")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    hip = Hip()
+    stream = torch.cuda.Stream(device=dev)      # default priority; graphs cannot capture the null stream
+    sh = stream.cuda_stream
+    with torch.cuda.stream(stream):
+        run(args, torch, si, kdv, dev, hip, stream, sh)
+
+
+def run(args, torch, si, kdv, dev, hip, stream, sh):
+
+    desc, inp, layers_per_step = build_workload(args.workload, torch, si)
+    log(f"[bench] workload {args.workload}: building inputs")
+    if args.workload == "full61":
+        parent_np, table_np = si.full61_shared()
+        H, Dn, Dr, R, Dv = 8, 128, 64, 512, 128
+        L, T, P = 131072, 32, 262144
+        scale = 1.0 / math.sqrt(Dn + Dr)
+        gen = torch.Generator(device=dev)
+        layers = []
+        for layer in range(61):
+            gen.manual_seed(1000 + layer)
+
+            def rnd(shape, std):
+                x = torch.randn(shape, generator=gen, device=dev, dtype=torch.float32) * std
+                return x.to(torch.bfloat16).view(torch.int16)
+            layers.append(dict(q_nope=rnd((T, H, Dn), Dn ** -0.5), q_rope=rnd((T, H, Dr), Dr ** -0.5),
+                               w_uk=rnd((H, Dn, R), R ** -0.5), w_uv=rnd((H, Dv, R), R ** -0.5),
+                               c_kv=rnd((P, R), R ** -0.5), k_pe=rnd((P, Dr), Dr ** -0.5)))
+        hot_layers = layers[:1] * 61
+        cold_sets = [layers]
+        hot_sets = [hot_layers]
+        parent_t = torch.from_numpy(parent_np.astype(np.int32)).to(dev)
+        table_t = torch.from_numpy(table_np.astype(np.int32)).to(dev)
+        pool_slots = P
+    else:
+        H, Dn, Dr, R, Dv, L, T = inp.H, inp.Dn, inp.Dr, inp.R, inp.Dv, inp.L, inp.T
+        parent_np = inp.parent
+        scale = inp.sm_scale
+        d0 = si.to_device(inp, dev)
+        parent_t, table_t = d0.pop("parent"), d0.pop("page_table")
+        per_set = sum(v.numel() * v.element_size() for v in d0.values())
+        n_cold = max(2, math.ceil(COLD_BYTES / per_set))
+        cold = [d0] + [clone_layer(d0) for _ in range(n_cold - 1)]
+        cold_sets = [[c] for c in cold]
+        hot_sets = [[d0]]
+        pool_slots = inp.pool_slots
+        log(f"[bench] cold rotation: {n_cold} buffer sets x {per_set / 2**20:.1f} MiB")
+
+    dims = kdv.make_dims(H, Dn, Dr, R, Dv, scale)
+    W = (T + 31) // 32
+    mask_t = torch.empty((T, W), dtype=torch.int32, device=dev)
+    status_t = torch.zeros((1,), dtype=torch.int32, device=dev)
+    out_t = torch.empty((T, H, Dv), dtype=torch.bfloat16, device=dev)
+    lse_t = torch.empty((T, H), dtype=torch.float32, device=dev)
+    ws_bytes = kdv.verify_workspace_bytes(dims, T, L)
+    ws_t = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
+    splits = kdv.kdv_verify_num_splits(dims, T, L)
+    wk = work(H, Dn, Dr, R, Dv, L, T, parent_np)
+
+    cold_ptrs = [[(Layer(t, pool_slots).ptrs()) for t in s] for s in cold_sets]
+    hot_ptrs = [[(Layer(t, pool_slots).ptrs()) for t in s] for s in hot_sets]
+    fixed = dict(pt=table_t.data_ptr(), mask=mask_t.data_ptr(), out=out_t.data_ptr(), lse=lse_t.data_ptr(),
+                 ws=ws_t.data_ptr(), parent=parent_t.data_ptr(), status=status_t.data_ptr())
+
+    def step(set_ptrs, ev=None):
+        rc = kdv.kdv_build_tree_mask(fixed["parent"], T, fixed["mask"], fixed["status"], sh)
+        if rc:
+            raise kdv.KdvError(rc, "kdv_build_tree_mask")
+        for lp in set_ptrs:
+            if ev is None:
+                rc = kdv.kdv_verify_mla_attn(dims, *lp, pool_slots, fixed["pt"], L, T, fixed["mask"], fixed["out"],
+                                             fixed["lse"], fixed["ws"], ws_bytes, sh)
+            else:
+                rc = kdv.kdv_verify_mla_attn_profiled(dims, *lp, pool_slots, fixed["pt"], L, T, fixed["mask"],
+                                                      fixed["out"], fixed["lse"], fixed["ws"], ws_bytes, sh,
+                                                      ctypes.addressof(ev))
+            if rc:
+                raise kdv.KdvError(rc, "kdv_verify_mla_attn")
+
+    def run_steps(sets, K, evs=None):
+        for i in range(K):
+            step(sets[i % len(sets)], None if evs is None else evs[i])
+
+    def timed(sets, K, evs=None):
+        """Device time (ms) of K steps: graph-captured unless --no-graph."""
+        e0, e1 = hip.event(), hip.event()
+        if args.no_graph:
+            torch.cuda.synchronize()
+            hip.record(e0, sh)
+            run_steps(sets, K, evs)
+            hip.record(e1, sh)
+            return hip.elapsed_ms(e0, e1)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            run_steps(sets, K, evs)
+        g.replay()                       # untimed replay: graph upload, first-touch
+        torch.cuda.synchronize()
+        hip.record(e0, sh)
+        g.replay()
+        hip.record(e1, sh)
+        ms = hip.elapsed_ms(e0, e1)
+        torch.cuda.synchronize()
+        return ms
+
+    K, Wm = args.steps, args.warmup
+    log(f"[bench] warmup {Wm} steps")
+    torch.cuda.synchronize()
+    run_steps(cold_ptrs, Wm)
+    torch.cuda.synchronize()
+    if int(status_t.item()) != 0:
+        raise SystemExit("tree status not OK")
+    log(f"[bench] timing {K} steps (cold)")
+    ms_cold = timed(cold_ptrs, K)
+    log(f"[bench] timing {K} steps (hot)")
+    ms_hot = timed(hot_ptrs, K)
+
+    # per-kernel split with events between the four kernels of every layer call
+    log("[bench] per-kernel timing")
+    EvArr = ctypes.c_void_p * 5
+    Kp = min(K, max(1, 400 // layers_per_step))
+    n_calls = Kp * layers_per_step
+    ev_list = [EvArr(*[hip.event() for _ in range(5)]) for _ in range(n_calls)]
+    per_step_evs = []
+    for i in range(Kp):
+        per_step_evs.append(ev_list[i * layers_per_step:(i + 1) * layers_per_step])
+
+    def step_ev(set_ptrs, evs):
+        rc = kdv.kdv_build_tree_mask(fixed["parent"], T, fixed["mask"], fixed["status"], sh)
+        if rc:
+            raise kdv.KdvError(rc, "kdv_build_tree_mask")
+        for lp, ev in zip(set_ptrs, evs):
+            rc = kdv.kdv_verify_mla_attn_profiled(dims, *lp, pool_slots, fixed["pt"], L, T, fixed["mask"],
+                                                  fixed["out"], fixed["lse"], fixed["ws"], ws_bytes, sh,
+                                                  ctypes.addressof(ev))
+            if rc:
+                raise kdv.KdvError(rc, "kdv_verify_mla_attn_profiled")
+
+    # Eager launches queued behind a spin kernel: the host enqueues every launch while the device is busy, so
+    # the events bracket back-to-back kernels with no host gaps.  (Events recorded inside a captured graph
+    # cannot be timed.)
+    kern_mode = "eager, queued behind a spin kernel"
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(2.4e9 * 0.05))
+    for i in range(Kp):
+        step_ev(cold_ptrs[i % len(cold_ptrs)], per_step_evs[i])
+    torch.cuda.synchronize()
+    names = ["q_absorb", "splitkv", "combine", "up_proj"]
+    tot = {n: 0.0 for n in names}
+    for ev in ev_list:
+        for k, n in enumerate(names):
+            tot[n] += hip.elapsed_ms(ev[k], ev[k + 1])
+    kern_us = {n: 1e3 * tot[n] / n_calls for n in names}
+
+    us_layer_cold = 1e3 * ms_cold / (K * layers_per_step)
+    us_layer_hot = 1e3 * ms_hot / (K * layers_per_step)
+    tflops_cold = wk["flops"] / (us_layer_cold * 1e-6) / 1e12
+    tflops_hot = wk["flops"] / (us_layer_hot * 1e-6) / 1e12
+    sk_tflops = wk["flops_splitkv"] / (kern_us["splitkv"] * 1e-6) / 1e12
+
+    result = {
+        "metric": METRIC,
+        "value": round(tflops_cold, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": Wm,
+        "ms_per_step": round(ms_cold / K, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": desc, "heads": H, "tree_nodes": T, "prefix_len": L, "kv_lora_rank": R,
+                   "qk_rope_dim": Dr, "qk_nope_dim": Dn, "v_head_dim": Dv, "layers_per_step": layers_per_step,
+                   "kv_splits": splits, "timing": "one HIP graph of K steps" if not args.no_graph else "eager",
+                   "buffers": "cold: rotation over > 512 MiB of distinct layer buffers"},
+        "us_per_layer": round(us_layer_cold, 3),
+        "frac_bf16_peak": round(tflops_cold / PEAK_BF16_TFLOPS, 4),
+        "hbm_gbs": round(wk["bytes"] / (us_layer_cold * 1e-6) / 1e9, 1),
+        "hot": {"us_per_layer": round(us_layer_hot, 3), "tflops": round(tflops_hot, 3),
+                "frac_bf16_peak": round(tflops_hot / PEAK_BF16_TFLOPS, 4)},
+        "kernels_us": {k: round(v, 3) for k, v in kern_us.items()},
+        "kernel_timing": kern_mode,
+        "work_per_layer": {"gflop": round(wk["flops"] / 1e9, 4), "mbytes": round(wk["bytes"] / 1e6, 3)},
+        "roofline": {"bound": "mfma", "kernel": "splitkv", "achieved": round(sk_tflops, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(sk_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None,
+                     "work_per_launch_gflop": round(wk["flops_splitkv"] / 1e9, 4)},
+        "cpu_baseline": None,
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(args, inp, wk, layers_per_step)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(args, inp, wk, layers_per_step):
+    """The fp64 oracle, as it stands, on the host cores, over a bounded sample of the same workload."""
+    import oracle
+    import synth_inputs as si
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = os.cpu_count()
+    if inp is None:  # full61: one layer of the same shape, generated on the host
+        parent, table = si.full61_shared()
+        inp = si.full61_layer(0, parent, table)
+        heads = [0, 1]
+        frac = len(heads) / inp.H
+        sample = f"oracle on heads {heads} of one 8-head layer (all 32 nodes, 131072-token prefix)"
+    elif inp.L > 100000:
+        heads = [0, 1]
+        frac = len(heads) / inp.H
+        sample = f"oracle on heads {heads} of the layer (all nodes)"
+    else:
+        heads = None
+        frac = 1.0
+        sample = "oracle on whole layers of the timed workload"
+    log("[bench] cpu baseline (oracle)")
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        oracle.verify_inputs(inp, heads=heads)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= args.cpu_seconds or n >= 200:
+            break
+    s_per_layer = el / n / frac
+    wk1 = work(inp.H, inp.Dn, inp.Dr, inp.R, inp.Dv, inp.L, inp.T, inp.parent)
+    return {"value": round(wk1["flops"] / s_per_layer / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle", "sample": f"{sample}; {n} calls in {el:.1f} s",
+            "seconds_per_layer": round(s_per_layer, 4), "host_cpus": os.cpu_count()}
+
+
+if __name__ == "__main__":
+    main()

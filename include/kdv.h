@@ -1,0 +1,138 @@
+/*
+ * kdv.h -- C ABI of libkdv: DDTree tree-verify attention for MLA (absorbed form) on MI355X (gfx950).
+ *
+ * The operation (from "The Architecture of Diagnosis: How Three Threads of Inference Engineering
+ * Converged in a Single Session", section "Phase 1: Custom CUDA Kernels", item 2): in the verify step
+ * of DDTree speculative decoding, every node of the draft tree is evaluated in one pass.  Each node
+ * attends over the KV cache under a visibility mask that follows the tree: the whole prefix, its
+ * ancestors and itself.  The cache is MLA's compressed latent (kv_lora_rank latent + qk_rope rotary
+ * elements per token per layer; "From Diagnosis to Deployment: Three Threads of Inference Engineering
+ * for Kimi K2.6", section "The Second Thread: Pivoting to 200k Context"), stored with one token per
+ * page so that accepted tokens can be committed non-contiguously ("The Architecture of Diagnosis...",
+ * section "The Discrepancy That Revealed the Truth").  The latent projection is absorbed into the
+ * attention: the key map W_UK is folded into the query and the value map W_UV is applied once to the
+ * attention output, so no per-head key or value is ever materialised.
+ *
+ * For node t, head h (all arithmetic on bf16 inputs, fp32 accumulation):
+ *   q_lat      = W_UK[h]^T q_nope[t,h]                                  (R)
+ *   s_n        = sm_scale * (q_lat . c_kv[pt[n]] + q_rope[t,h] . k_pe[pt[n]])
+ *   visible(n) = n < L  or  (n - L) is on the root-to-t path of the tree
+ *   p          = softmax of s over the visible n;  o_lat = sum_n p_n c_kv[pt[n]]
+ *   out[t,h]   = W_UV[h] o_lat                                           (Dv)
+ *   lse[t,h]   = ln sum_{visible n} exp(s_n)
+ *
+ * Conventions shared by every entry point:
+ *   - Memory is owned by the caller.  Device pointers are plain HIP device addresses; bf16 arrays are
+ *     passed as uint16_t bit patterns.  The library never allocates, frees or keeps state between calls.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Every call only enqueues work on it and
+ *     returns; device faults surface at the caller's next synchronisation.
+ *   - Argument errors are detected on the host before anything is enqueued and returned as a negative
+ *     kdv_status; nothing is launched in that case.
+ *   - Row-major layouts; "[A][B]" means B is the contiguous dimension.
+ */
+#ifndef KDV_H
+#define KDV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Model dimensions of one MLA attention layer.  Supported shapes:
+ *   Kimi/DeepSeek shape: qk_nope 128, qk_rope 64, kv_lora_rank 512, v_head 128;
+ *   tiny test shape:     qk_nope 32,  qk_rope 16, kv_lora_rank 64,  v_head 32;
+ * with 1 <= num_heads <= 128.  sm_scale multiplies q.k (1/sqrt(qk_nope+qk_rope) for Kimi). */
+typedef struct kdv_mla_dims {
+  int32_t num_heads;
+  int32_t qk_nope_dim;
+  int32_t qk_rope_dim;
+  int32_t kv_lora_rank;
+  int32_t v_head_dim;
+  float sm_scale;
+} kdv_mla_dims;
+
+typedef enum kdv_status {
+  KDV_OK = 0,
+  KDV_ERR_NULL = -1,      /* a required pointer is NULL                                         */
+  KDV_ERR_SHAPE = -2,     /* T outside [1, 64], L < 0, L+T overflow, or unsupported dims          */
+  KDV_ERR_TREE = -3,      /* parent array is not a rooted tree in topological order (device side) */
+  KDV_ERR_ALIGN = -4,     /* a bf16/fp32 array or the workspace is not 16-byte aligned            */
+  KDV_ERR_WORKSPACE = -5, /* workspace smaller than kdv_verify_workspace_bytes()                  */
+  KDV_ERR_HIP = -6        /* a HIP launch or query failed                                         */
+} kdv_status;
+
+#define KDV_MAX_TREE_NODES 64
+
+/* Ancestor bitmask of the draft tree ("visibility mask that reflects the tree structure",
+ * "The Architecture of Diagnosis...", section "Phase 1: Custom CUDA Kernels", item 2).
+ *
+ *   parent : device int32 [T].  parent[0] = -1 (node 0 is the root); parent[i] in [0, i) for i > 0,
+ *            i.e. the nodes are in topological order, as a best-first tree builder emits them.
+ *   T      : number of tree nodes, 1 <= T <= 64.
+ *   mask   : device uint32 [T][W], W = (T + 31) / 32, written.  Bit (j % 32) of word j / 32 of row i is
+ *            set iff node j is on the root-to-i path (i itself included); all other bits, including
+ *            the padding above T, are zero.  Row i equals row parent[i] with bit i added.
+ *   status : device int32, nullable.  The parent array lives on the device, so its validity is
+ *            reported there: KDV_OK, or KDV_ERR_TREE if parent[0] != -1 or some parent[i] is outside
+ *            [0, i).  An invalid row gets only its own bit; rows below it follow the rule above.
+ * Host-side return: KDV_OK, KDV_ERR_NULL (parent or mask NULL), KDV_ERR_SHAPE (T out of range),
+ * KDV_ERR_ALIGN (parent, mask or status not 4-byte aligned), KDV_ERR_HIP. */
+int kdv_build_tree_mask(const int32_t* parent, int32_t T, uint32_t* mask, int32_t* status, void* stream);
+
+/* Bytes of device workspace kdv_verify_mla_attn needs for these dims, tree size T and prefix length L
+ * on the current device (the split-KV plan depends on the device's compute-unit count).  Returns 0 if
+ * the arguments are unsupported.  The environment variable KDV_SPLITS, if set, overrides the number of
+ * KV splits; it must be the same when sizing and when calling. */
+size_t kdv_verify_workspace_bytes(const kdv_mla_dims* d, int32_t T, int32_t L);
+
+/* Tree-verify MLA attention for one layer (formula at the top of this file).
+ *
+ *   d          : dims (host pointer).
+ *   q_nope     : device bf16 [T][H][Dn].
+ *   q_rope     : device bf16 [T][H][Dr], already rotated (post-RoPE).
+ *   w_uk       : device bf16 [H][Dn][R]; per head the key map k_nope = W_UK[h] c.
+ *   w_uv       : device bf16 [H][Dv][R]; per head the value map v = W_UV[h] c.
+ *   c_kv       : device bf16 pool [P][R] of latent rows.
+ *   k_pe       : device bf16 pool [P][Dr] of rotary key rows (post-RoPE).
+ *   pool_slots : P.  Every page_table entry must be in [0, P); this is the caller's contract and is not
+ *                checked on the hot path.
+ *   page_table : device int32 [L+T]; logical position n -> pool slot.  Positions 0..L-1 are the prefix;
+ *                position L+i holds tree node i's own latent row (already appended by the caller).
+ *   L, T       : prefix length (>= 0) and tree size (1..64).
+ *   mask       : device uint32 [T][(T+31)/32] from kdv_build_tree_mask.
+ *   out        : device bf16 [T][H][Dv], written.
+ *   lse        : device fp32 [T][H], nullable; natural-log sum of exp of the scaled visible scores,
+ *                for merging with attention computed elsewhere.
+ *   workspace  : device scratch of workspace_bytes >= kdv_verify_workspace_bytes(d, T, L); 16-byte
+ *                aligned; its contents are undefined after the call.  Calls that share a workspace
+ *                must be ordered on one stream.
+ * Returns KDV_OK or a negative kdv_status (nothing enqueued on error). */
+int kdv_verify_mla_attn(const kdv_mla_dims* d, const uint16_t* q_nope, const uint16_t* q_rope,
+                        const uint16_t* w_uk, const uint16_t* w_uv, const uint16_t* c_kv, const uint16_t* k_pe,
+                        int64_t pool_slots, const int32_t* page_table, int32_t L, int32_t T, const uint32_t* mask,
+                        uint16_t* out, float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Same computation as kdv_verify_mla_attn, for measurement: `events` points to five hipEvent_t created by
+ * the caller; events[0..4] are recorded on `stream` before q absorption, before the split-KV pass, before
+ * the split combine, before the W_UV up-projection and after it, so that each kernel's device time can be
+ * read with hipEventElapsedTime.  Errors as kdv_verify_mla_attn, plus KDV_ERR_NULL if events is NULL. */
+int kdv_verify_mla_attn_profiled(const kdv_mla_dims* d, const uint16_t* q_nope, const uint16_t* q_rope,
+                                 const uint16_t* w_uk, const uint16_t* w_uv, const uint16_t* c_kv,
+                                 const uint16_t* k_pe, int64_t pool_slots, const int32_t* page_table, int32_t L,
+                                 int32_t T, const uint32_t* mask, uint16_t* out, float* lse, void* workspace,
+                                 size_t workspace_bytes, void* stream, void* const* events);
+
+/* Number of KV splits kdv_verify_mla_attn will use for these arguments on the current device
+ * (diagnostic; 0 if unsupported). */
+int32_t kdv_verify_num_splits(const kdv_mla_dims* d, int32_t T, int32_t L);
+
+/* Static English description of a kdv_status value. */
+const char* kdv_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDV_H */

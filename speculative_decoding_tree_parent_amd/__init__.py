@@ -1,0 +1,178 @@
+"""Python binding of libkdv: DDTree tree-verify attention for MLA on MI355X (gfx950).
+
+The functions named ``kdv_*`` are the C ABI of ``include/kdv.h`` one for one (plain integers for device
+pointers and streams).  ``build_tree_mask``, ``verify_workspace_bytes`` and ``verify_mla_attn`` only
+marshal torch tensors into those calls: every step of the computation runs in the HIP kernels of
+``libkdv.so``.  There is no fallback: if the library is missing, importing this package raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+# torch ships its own HIP runtime (same soname as /opt/rocm's).  Loading it first makes libkdv.so bind to that
+# same runtime instead of pulling a second one into the process.
+import torch  # noqa: F401
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libkdv.so")
+
+KDV_OK = 0
+KDV_ERR_NULL = -1
+KDV_ERR_SHAPE = -2
+KDV_ERR_TREE = -3
+KDV_ERR_ALIGN = -4
+KDV_ERR_WORKSPACE = -5
+KDV_ERR_HIP = -6
+KDV_MAX_TREE_NODES = 64
+
+EXPORTED = ("kdv_build_tree_mask", "kdv_verify_workspace_bytes", "kdv_verify_mla_attn",
+            "kdv_verify_mla_attn_profiled", "kdv_verify_num_splits", "kdv_status_string")
+
+
+class KdvMlaDims(ctypes.Structure):
+    _fields_ = [("num_heads", ctypes.c_int32), ("qk_nope_dim", ctypes.c_int32), ("qk_rope_dim", ctypes.c_int32),
+                ("kv_lora_rank", ctypes.c_int32), ("v_head_dim", ctypes.c_int32), ("sm_scale", ctypes.c_float)]
+
+
+class KdvError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {kdv_status_string(status)} ({status})")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libkdv.so not built at {LIB_PATH}; run `python speculative_decoding_tree_parent_amd/build.py`"
+                          " (or __graft_entry__.build())")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    dims_p = ctypes.POINTER(KdvMlaDims)
+    lib.kdv_build_tree_mask.argtypes = [vp, i32, vp, vp, vp]
+    lib.kdv_build_tree_mask.restype = ctypes.c_int
+    lib.kdv_verify_workspace_bytes.argtypes = [dims_p, i32, i32]
+    lib.kdv_verify_workspace_bytes.restype = sz
+    lib.kdv_verify_num_splits.argtypes = [dims_p, i32, i32]
+    lib.kdv_verify_num_splits.restype = i32
+    lib.kdv_verify_mla_attn.argtypes = [dims_p, vp, vp, vp, vp, vp, vp, i64, vp, i32, i32, vp, vp, vp, vp, sz, vp]
+    lib.kdv_verify_mla_attn.restype = ctypes.c_int
+    lib.kdv_verify_mla_attn_profiled.argtypes = [dims_p, vp, vp, vp, vp, vp, vp, i64, vp, i32, i32, vp, vp, vp, vp,
+                                                 sz, vp, vp]
+    lib.kdv_verify_mla_attn_profiled.restype = ctypes.c_int
+    lib.kdv_status_string.argtypes = [ctypes.c_int]
+    lib.kdv_status_string.restype = ctypes.c_char_p
+    return lib
+
+
+_lib = _load()
+
+
+# ------------------------------------------------------------------------------------------- C ABI, 1:1
+def kdv_build_tree_mask(parent: int, T: int, mask: int, status: int | None, stream: int | None) -> int:
+    return _lib.kdv_build_tree_mask(parent, T, mask, status, stream)
+
+
+def kdv_verify_workspace_bytes(dims: KdvMlaDims, T: int, L: int) -> int:
+    return _lib.kdv_verify_workspace_bytes(ctypes.byref(dims), T, L)
+
+
+def kdv_verify_num_splits(dims: KdvMlaDims, T: int, L: int) -> int:
+    return _lib.kdv_verify_num_splits(ctypes.byref(dims), T, L)
+
+
+def kdv_verify_mla_attn(dims: KdvMlaDims, q_nope: int, q_rope: int, w_uk: int, w_uv: int, c_kv: int, k_pe: int,
+                        pool_slots: int, page_table: int, L: int, T: int, mask: int, out: int, lse: int | None,
+                        workspace: int, workspace_bytes: int, stream: int | None) -> int:
+    return _lib.kdv_verify_mla_attn(ctypes.byref(dims), q_nope, q_rope, w_uk, w_uv, c_kv, k_pe, pool_slots,
+                                    page_table, L, T, mask, out, lse, workspace, workspace_bytes, stream)
+
+
+def kdv_verify_mla_attn_profiled(dims: KdvMlaDims, q_nope: int, q_rope: int, w_uk: int, w_uv: int, c_kv: int,
+                                 k_pe: int, pool_slots: int, page_table: int, L: int, T: int, mask: int, out: int,
+                                 lse: int | None, workspace: int, workspace_bytes: int, stream: int | None,
+                                 events: int) -> int:
+    """`events`: address of five hipEvent_t handles (see include/kdv.h)."""
+    return _lib.kdv_verify_mla_attn_profiled(ctypes.byref(dims), q_nope, q_rope, w_uk, w_uv, c_kv, k_pe, pool_slots,
+                                             page_table, L, T, mask, out, lse, workspace, workspace_bytes, stream,
+                                             events)
+
+
+def kdv_status_string(status: int) -> str:
+    return _lib.kdv_status_string(status).decode()
+
+
+# ------------------------------------------------------------------------------------------- torch marshalling
+def make_dims(num_heads: int, qk_nope_dim: int, qk_rope_dim: int, kv_lora_rank: int, v_head_dim: int,
+              sm_scale: float) -> KdvMlaDims:
+    return KdvMlaDims(num_heads, qk_nope_dim, qk_rope_dim, kv_lora_rank, v_head_dim, sm_scale)
+
+
+def _stream_handle(stream) -> int | None:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def _ptr(t, dtype, what: str) -> int:
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{what} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{what} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    return t.data_ptr()
+
+
+def build_tree_mask(parent, mask=None, status=None, stream=None):
+    """parent: int32 [T] device tensor -> (mask uint32-as-int32 [T][W], status int32 [1])."""
+    import torch
+    T = parent.shape[0]
+    W = (T + 31) // 32
+    if mask is None:
+        mask = torch.empty((T, W), dtype=torch.int32, device=parent.device)
+    if status is None:
+        status = torch.empty((1,), dtype=torch.int32, device=parent.device)
+    rc = kdv_build_tree_mask(_ptr(parent, torch.int32, "parent"), T, _ptr(mask, torch.int32, "mask"),
+                             _ptr(status, torch.int32, "status"), _stream_handle(stream))
+    if rc != KDV_OK:
+        raise KdvError(rc, "kdv_build_tree_mask")
+    return mask, status
+
+
+def verify_workspace_bytes(dims: KdvMlaDims, T: int, L: int) -> int:
+    n = kdv_verify_workspace_bytes(dims, T, L)
+    if n == 0:
+        raise KdvError(KDV_ERR_SHAPE, "kdv_verify_workspace_bytes")
+    return n
+
+
+def verify_mla_attn(dims: KdvMlaDims, q_nope, q_rope, w_uk, w_uv, c_kv, k_pe, page_table, L: int, mask, out=None,
+                    lse=None, workspace=None, stream=None):
+    """All tensors on the device; bf16 tensors may be torch.bfloat16 or int16 bit patterns.
+
+    Returns (out [T][H][Dv] bf16, lse [T][H] fp32 or None)."""
+    import torch
+    T = q_nope.shape[0]
+    H = dims.num_heads
+
+    def bf(t, what):
+        if t.dtype == torch.bfloat16:
+            return _ptr(t, torch.bfloat16, what)
+        return _ptr(t, torch.int16, what)
+
+    if out is None:
+        out = torch.empty((T, H, dims.v_head_dim), dtype=torch.bfloat16, device=q_nope.device)
+    if workspace is None:
+        workspace = torch.empty((verify_workspace_bytes(dims, T, L),), dtype=torch.uint8, device=q_nope.device)
+    lse_ptr = None if lse is None else _ptr(lse, torch.float32, "lse")
+    rc = kdv_verify_mla_attn(dims, bf(q_nope, "q_nope"), bf(q_rope, "q_rope"), bf(w_uk, "w_uk"), bf(w_uv, "w_uv"),
+                             bf(c_kv, "c_kv"), bf(k_pe, "k_pe"), c_kv.shape[0], _ptr(page_table, torch.int32, "page_table"),
+                             L, T, _ptr(mask, torch.int32, "mask"), bf(out, "out"), lse_ptr,
+                             _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream_handle(stream))
+    if rc != KDV_OK:
+        raise KdvError(rc, "kdv_verify_mla_attn")
+    return out, lse

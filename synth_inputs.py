@@ -227,3 +227,16 @@ def full61_layer(layer: int, parent: np.ndarray, page_table: np.ndarray, L: int 
                       dist=dist)
     inp.page_table = np.asarray(page_table, dtype=np.int32).copy()
     return inp
+
+
+def to_device(inp: VerifyInputs, device="cuda") -> dict:
+    """Copy one layer's inputs to device tensors (bf16 bit patterns as int16; indices as int32)."""
+    import torch
+
+    def b16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device)
+
+    return dict(parent=torch.from_numpy(inp.parent.astype(np.int32)).to(device),
+                q_nope=b16(inp.q_nope), q_rope=b16(inp.q_rope), w_uk=b16(inp.w_uk), w_uv=b16(inp.w_uv),
+                c_kv=b16(inp.c_kv), k_pe=b16(inp.k_pe),
+                page_table=torch.from_numpy(inp.page_table.astype(np.int32)).to(device))

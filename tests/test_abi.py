@@ -1,0 +1,129 @@
+"""C ABI checks that need no GPU: the library loads, exports every function include/kdv.h declares,
+and rejects bad arguments on the host with the documented status before anything is launched.
+
+Argument errors are tested with fake (never dereferenced) addresses; KDV_SPLITS is set so that
+workspace sizing does not query a device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import speculative_decoding_tree_parent_amd as kdv
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "kdv.h")
+
+KIMI = dict(num_heads=64, qk_nope_dim=128, qk_rope_dim=64, kv_lora_rank=512, v_head_dim=128, sm_scale=192 ** -0.5)
+TINY = dict(num_heads=4, qk_nope_dim=32, qk_rope_dim=16, kv_lora_rank=64, v_head_dim=32, sm_scale=48 ** -0.5)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kdv_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_expected_entry_points():
+    assert declared_functions() == sorted(kdv.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(kdv.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for code in range(-6, 1):
+        s = kdv.kdv_status_string(code)
+        assert s and "unknown" not in s
+    assert "unknown" in kdv.kdv_status_string(-99)
+
+
+@pytest.fixture
+def fixed_splits(monkeypatch):
+    monkeypatch.setenv("KDV_SPLITS", "4")
+
+
+A = 0x10000  # fake, 64 KiB aligned, never dereferenced
+
+
+def _call(dims, T=15, L=100, ws_bytes=1 << 40, **override):
+    args = dict(q_nope=A, q_rope=A, w_uk=A, w_uv=A, c_kv=A, k_pe=A, pool_slots=1 << 20, page_table=A, L=L, T=T,
+                mask=A, out=A, lse=None, workspace=A, workspace_bytes=ws_bytes, stream=None)
+    args.update(override)
+    return kdv.kdv_verify_mla_attn(dims, **args)
+
+
+@pytest.mark.parametrize("field", ["q_nope", "q_rope", "w_uk", "w_uv", "c_kv", "k_pe", "page_table", "mask", "out",
+                                   "workspace"])
+def test_null_pointer_rejected(field, fixed_splits):
+    assert _call(kdv.make_dims(**KIMI), **{field: None}) == kdv.KDV_ERR_NULL
+
+
+@pytest.mark.parametrize("T,L", [(0, 10), (65, 10), (-1, 10), (15, -1)])
+def test_bad_tree_or_prefix_rejected(T, L, fixed_splits):
+    assert _call(kdv.make_dims(**KIMI), T=T, L=L) == kdv.KDV_ERR_SHAPE
+
+
+@pytest.mark.parametrize("change", [dict(qk_nope_dim=64), dict(kv_lora_rank=256), dict(qk_rope_dim=32),
+                                    dict(v_head_dim=64), dict(num_heads=0), dict(num_heads=129)])
+def test_unsupported_dims_rejected(change, fixed_splits):
+    d = dict(KIMI)
+    d.update(change)
+    assert _call(kdv.make_dims(**d)) == kdv.KDV_ERR_SHAPE
+    assert kdv.kdv_verify_workspace_bytes(kdv.make_dims(**d), 15, 100) == 0
+
+
+def test_bad_pool_rejected(fixed_splits):
+    assert _call(kdv.make_dims(**KIMI), pool_slots=0) == kdv.KDV_ERR_SHAPE
+
+
+@pytest.mark.parametrize("field,off", [("q_nope", 8), ("c_kv", 2), ("k_pe", 4), ("w_uk", 8), ("w_uv", 8),
+                                       ("out", 8), ("workspace", 8), ("page_table", 2), ("mask", 1), ("lse", 2)])
+def test_misaligned_rejected(field, off, fixed_splits):
+    assert _call(kdv.make_dims(**KIMI), **{field: A + off}) == kdv.KDV_ERR_ALIGN
+
+
+@pytest.mark.parametrize("dims", [KIMI, TINY])
+def test_workspace_too_small_rejected(dims, fixed_splits):
+    d = kdv.make_dims(**dims)
+    need = kdv.kdv_verify_workspace_bytes(d, 15, 5553)
+    assert need > 0
+    assert _call(d, T=15, L=5553, ws_bytes=need - 1) == kdv.KDV_ERR_WORKSPACE
+    assert _call(d, T=15, L=5553, ws_bytes=0) == kdv.KDV_ERR_WORKSPACE
+
+
+def test_workspace_formula(fixed_splits):
+    # q_cat + o_lat (bf16) + split partials (fp32 O + (max, sum)), each region 256-byte aligned
+    d = kdv.make_dims(**KIMI)
+    T, L = 15, 5553
+    S = kdv.kdv_verify_num_splits(d, T, L)
+    assert S == 4
+    M, Mp = T * 64, ((T * 64 + 63) // 64) * 64
+    up = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    expect = up(M * 576 * 2) + up(M * 512 * 2) + up(S * Mp * 512 * 4) + up(S * Mp * 8)
+    assert kdv.kdv_verify_workspace_bytes(d, T, L) == expect
+
+
+def test_split_count_never_exceeds_tiles(monkeypatch):
+    monkeypatch.setenv("KDV_SPLITS", "1000")
+    d = kdv.make_dims(**KIMI)
+    assert kdv.kdv_verify_num_splits(d, 15, 0) == 1          # N = 15 -> one 64-row tile
+    assert kdv.kdv_verify_num_splits(d, 15, 5553) == 87      # 5568 rows -> 87 tiles
+
+
+def test_tree_mask_argument_errors():
+    assert kdv.kdv_build_tree_mask(None, 7, A, None, None) == kdv.KDV_ERR_NULL
+    assert kdv.kdv_build_tree_mask(A, 7, None, None, None) == kdv.KDV_ERR_NULL
+    assert kdv.kdv_build_tree_mask(A, 0, A, None, None) == kdv.KDV_ERR_SHAPE
+    assert kdv.kdv_build_tree_mask(A, 65, A, None, None) == kdv.KDV_ERR_SHAPE
+    assert kdv.kdv_build_tree_mask(A + 2, 7, A, None, None) == kdv.KDV_ERR_ALIGN
+    assert kdv.kdv_build_tree_mask(A, 7, A, A + 1, None) == kdv.KDV_ERR_ALIGN
+
+
+def test_package_has_no_cpu_fallback():
+    # the product package must not reach the oracle
+    import inspect
+    src = inspect.getsource(kdv)
+    assert "oracle" not in src.replace("never by the product", "")
