@@ -9,8 +9,8 @@
 // Four kernels, enqueued in order on the caller's stream:
 //   q_absorb : q_cat[m] = [W_UK[h]^T q_nope[t,h] ; q_rope[t,h]]          (m = t*H + h; bf16 MFMA)
 //   splitkv  : one workgroup per (64 query rows, KV split).  KV tiles of 64 paged rows are gathered into
-//              LDS; scores S^T = K Q^T and O^T += V^T P^T run on 32x32x16 bf16 MFMA with an online
-//              softmax; the partial (O, max, sum) of the split goes to the workspace.
+//              LDS by DMA one tile ahead; scores S^T = K Q^T and O^T += V^T P^T run on 32x32x16 bf16 MFMA
+//              with an online softmax; the partial (O, max, sum) of the split goes to the workspace.
 //   combine  : log-sum-exp merge of the splits -> o_lat (bf16) and lse.
 //   up_proj  : out[t,h] = W_UV[h] o_lat[t,h]                              (bf16 MFMA)
 #include <math.h>
@@ -94,158 +94,335 @@ __global__ __launch_bounds__(NTHREADS) void q_absorb_kernel(const uint16_t* __re
 }
 
 // ------------------------------------------------------------------------------------------------ splitkv
-// Workgroup = 4 waves over 64 query rows.  Wave (wi, wj): rows wi*32..+31 of the tile.
-//   scores : the wave computes S^T for KV rows wj*32..+31 of each 64-row tile (full 576-deep contraction);
-//   softmax: the two waves of a row pair agree on the running max through LDS, then swap their halves of
-//            P (bf16) through LDS;
-//   values : the wave accumulates O^T for latent columns wj*R/2..+R/2 over all 64 KV rows of the tile.
-// Lane l owns query row m = tile_row + wi*32 + (l%32): the softmax state of a row lives in one lane pair
-// (l, l^32) and every per-row factor is a per-lane scalar.
+// LDS layout of one 64-row KV tile: the latent rows [64][R] then the rotary rows [64][DR], bf16, row-major.
+// Within a row the 16-byte chunks are XOR-swizzled (chunk c of row r is stored at c ^ swz(r)) so that
+//   - the score MFMA's 16 lanes, which read the same chunk of 16 consecutive rows, hit 16 distinct bank
+//     groups, and
+//   - the value MFMA's transposed reads, 4 consecutive rows x 2 adjacent chunks per 16 lanes, hit 8.
+// The swizzle replaces row padding, so two tiles fit in LDS (2 x 72 KB for the Kimi shape).
+template <int C>  // C = 16-byte chunks per row
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (C >= 16) return ((row & 7) << 1) | ((row >> 3) & 1);
+  else return (row >> (C == 8 ? 1 : C == 4 ? 2 : 3)) & (C - 1);
+}
+
+template <int R, int DR>
+struct TileLayout {
+  static constexpr int CK = R / 8;                     // chunks per latent row
+  static constexpr int CP = DR / 8;                    // chunks per rotary row
+  static constexpr int CKV_BYTES = KV_TILE * R * 2;
+  static constexpr int BYTES = CKV_BYTES + KV_TILE * DR * 2;
+  static constexpr int NDMA = CK + CP;                 // 64-lane x 16-byte DMA instructions per tile
+  // byte offset of (row, logical chunk) in the tile
+  __device__ static __forceinline__ int ckv(int row, int ch) { return row * (R * 2) + ((ch ^ swz<CK>(row)) << 4); }
+  __device__ static __forceinline__ int kpe(int row, int ch) {
+    return CKV_BYTES + row * (DR * 2) + ((ch ^ swz<CP>(row)) << 4);
+  }
+};
+
+// Gather one tile of paged rows straight into LDS with global_load_lds_dwordx4: lane l of an instruction
+// writes LDS bytes [16l, 16l+16) of that instruction's 1 KB block (M0 holds the block address).  The loads
+// are issued from inline assembly so that the compiler neither tracks them as LDS stores (it would wait for
+// the prefetch before every read of the other buffer) nor keeps per-instruction 64-bit addresses live;
+// completion is awaited explicitly (wait_vmem_all + barrier) before a tile is read.
+// `slot_v` holds, in lane j, the pool slot of tile row j; the work is split over the 4 waves.
+__device__ __forceinline__ void dma16_uniform_base(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
+               "s"(lds_addr)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma16_lane_addr(const void* vaddr, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(vaddr), "s"(lds_addr)
+               : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return (uint32_t)(size_t)(const __attribute__((address_space(3))) char*)(p);
+}
+
+template <int R, int DR>
+__device__ __forceinline__ void dma_tile(const char* buf, const uint16_t* __restrict__ c_kv,
+                                         const uint16_t* __restrict__ k_pe, int slot_v, int wave, int lane) {
+  using TL = TileLayout<R, DR>;
+  const uint32_t lbase = lds_address(buf);
+  if constexpr (TL::CK == 64) {
+    // one instruction per latent row; wave w takes rows w, w+4, ...; the row's swizzle repeats with period 4
+    uint32_t voff[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) voff[k] = (uint32_t)((lane ^ swz<64>(wave + 4 * k)) << 4);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int i = wave + 4 * k;
+      const int slot = __builtin_amdgcn_readlane(slot_v, i);
+      dma16_uniform_base(reinterpret_cast<const char*>(c_kv) + (size_t)slot * (R * 2), voff[k & 3],
+                         lbase + i * 1024);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < (TL::CK + 3) / 4; ++k) {
+      const int i = wave + 4 * k;
+      if (TL::CK % 4 == 0 || i < TL::CK) {
+        const int flat = i * 64 + lane, row = flat / TL::CK, pos = flat % TL::CK;
+        const int slot = __shfl(slot_v, row);
+        dma16_lane_addr(reinterpret_cast<const char*>(c_kv) + (size_t)slot * (R * 2) + ((pos ^ swz<TL::CK>(row)) << 4),
+                        lbase + i * 1024);
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < (TL::CP + 3) / 4; ++k) {
+    const int j = wave + 4 * k;
+    if (TL::CP % 4 == 0 || j < TL::CP) {
+      const int flat = j * 64 + lane, row = flat / TL::CP, pos = flat % TL::CP;
+      const int slot = __shfl(slot_v, row);
+      dma16_lane_addr(reinterpret_cast<const char*>(k_pe) + (size_t)slot * (DR * 2) + ((pos ^ swz<TL::CP>(row)) << 4),
+                      lbase + TL::CKV_BYTES + j * 1024);
+    }
+  }
+}
+
+__device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Softmax state of one query row, held identically by the two lanes (l, l^32) that own it.
+struct RowState {
+  float m_ref;  // reference max (log2 units; an integer or -inf): P = 2^(s - m_ref) <= 2^8
+  float l;      // this lane's share of sum_n P (the lane pair adds up at the end)
+};
+
+template <int R, int DR>
+struct SplitArgs {
+  const uint16_t* __restrict__ c_kv;
+  const uint16_t* __restrict__ k_pe;
+  const int32_t* __restrict__ page_table;
+  int L, N;
+  float scale_log2;
+};
+
+// One tile: scores for this wave's 32 KV rows, lazy-reference softmax agreed with the partner wave through a
+// single LDS exchange (P halves + proposed references), then O^T += V^T P^T for the wave's R/2 columns.
+template <int R, int DR>
+__device__ __forceinline__ void tile_compute(const char* tile, const bf16x8 (&q)[(R + DR) / 16], f32x16 (&o)[R / 64],
+                                             RowState& st, int n0, int L, int N, uint32_t mw0, uint32_t mw1,
+                                             float scale_log2, uint4 (*pb_own)[2], uint4 (*pb_oth)[2],
+                                             float* ps_own, const float* ps_oth, float* mx_own, const float* mx_oth,
+                                             int wj, int lane) {
+  using TL = TileLayout<R, DR>;
+  constexpr int KB = (R + DR) / 16, DB = R / 64;
+  const int g = lane >> 5, c = lane & 31;
+  // ---- scores S^T[n][m] for tile rows n = wj*32 + (r/4)*8 + g*4 + r%4
+  // The swizzle only touches the low log2(F) bits of a chunk index, so a row's fragment offsets repeat with
+  // period F/2 k-blocks plus a compile-time stride: a few per-lane bases and immediate offsets.
+  constexpr int FK = TL::CK < 16 ? TL::CK : 16, PK = FK / 2;
+  constexpr int FP = TL::CP < 16 ? TL::CP : 16, PP = FP / 2;
+  f32x16 acc = zero16();
+  const int nrow = wj * 32 + c;
+  const char* ckp[PK];
+  const char* kpp[PP];
+#pragma unroll
+  for (int i = 0; i < PK; ++i) ckp[i] = tile + nrow * (R * 2) + (((2 * i + g) ^ swz<TL::CK>(nrow)) << 4);
+#pragma unroll
+  for (int i = 0; i < PP; ++i) kpp[i] = tile + TL::CKV_BYTES + nrow * (DR * 2) + (((2 * i + g) ^ swz<TL::CP>(nrow)) << 4);
+  auto kfrag = [&](int kb) -> bf16x8 {
+    const int kr = kb - R / 16;
+    const char* p = (kb < R / 16) ? ckp[kb % PK] + (kb / PK) * FK * 16 : kpp[kr % PP] + (kr / PP) * FP * 16;
+    return *reinterpret_cast<const bf16x8*>(p);
+  };
+  // software pipeline: fragment kb+QD is requested before the MFMA of kb
+  constexpr int QD = 4;
+  bf16x8 kf[QD];
+#pragma unroll
+  for (int i = 0; i < QD; ++i) kf[i] = kfrag(i);
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    const bf16x8 a = kf[kb % QD];
+    if (kb + QD < KB) kf[kb % QD] = kfrag(kb + QD);
+    acc = mfma32(a, q[kb], acc);
+  }
+  float s[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s[r] = acc[r] * scale_log2;
+  if (n0 + KV_TILE > L) {  // tile reaches the tree rows (or past N): apply the ancestor mask
+    const uint64_t mw = (uint64_t)mw0 | ((uint64_t)mw1 << 32);
+    const int T = N - L;
+    const int jb = n0 + wj * 32 + g * 4 - L;  // tree index of register 0's row
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int jn = jb + (r >> 2) * 8 + (r & 3);
+      const bool vis = (jn < 0) || (jn < T && ((mw >> (jn & 63)) & 1u));
+      s[r] = vis ? s[r] : -INFINITY;
+    }
+  }
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[r]);
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+  // ---- proposed reference: keep the current one unless this half-tile exceeds it by more than 2^8
+  const float prop = (tmax > st.m_ref + 8.f) ? ceilf(tmax) : st.m_ref;
+  const float puse = (prop == -INFINITY) ? 0.f : prop;
+  bf16x8 pk[2];
+  float ps = 0.f;  // this lane's share of the half-tile row sum, unrounded
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float p0 = fast_exp2(s[e] - puse), p1 = fast_exp2(s[8 + e] - puse);
+    ps += p0 + p1;
+    pk[0][e] = (__bf16)p0;
+    pk[1][e] = (__bf16)p1;
+  }
+  pb_own[lane][0] = __builtin_bit_cast(uint4, pk[0]);
+  pb_own[lane][1] = __builtin_bit_cast(uint4, pk[1]);
+  ps_own[lane] = ps;
+  if (g == 0) mx_own[c] = prop;
+  __syncthreads();
+  bf16x8 po[2];
+  po[0] = __builtin_bit_cast(bf16x8, pb_oth[lane][0]);
+  po[1] = __builtin_bit_cast(bf16x8, pb_oth[lane][1]);
+  const float ps_o = ps_oth[lane];
+  const float poth = mx_oth[c];
+  // ---- agree on M = max of both proposals; rescale by exact powers of two
+  const float M = fmaxf(prop, poth);
+  const bool live = M != -INFINITY;
+  const float f_own = live ? fast_exp2(prop - M) : 1.f;
+  const float f_oth = live ? fast_exp2(poth - M) : 1.f;
+  if (__any(f_own != 1.f || f_oth != 1.f)) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        pk[h][e] = (__bf16)((float)pk[h][e] * f_own);
+        po[h][e] = (__bf16)((float)po[h][e] * f_oth);
+      }
+  }
+  if (__any(M > st.m_ref)) {
+    const float alpha = (M > st.m_ref) ? fast_exp2(st.m_ref - M) : 1.f;  // m_ref = -inf -> 0
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+    st.l *= alpha;
+  }
+  st.m_ref = fmaxf(st.m_ref, M);
+  // row sum: both halves' unrounded sums, rescaled exactly and added in a fixed order (KV half 0 first) so that
+  // both waves of the pair hold the same bits
+  const float s_own = ps * f_own, s_oth = ps_o * f_oth;
+  st.l += (wj == 0) ? (s_own + s_oth) : (s_oth + s_own);
+  // ---- O^T[d][m] += sum_n V^T[d][n] P^T[n][m]; within a 16-row block the contraction index k = g*8+e is
+  // KV row (e/4)*8 + g*4 + e%4, matching the score layout.
+  // Lane's rows are h2*32 + kb2*16 + rl (+8): the swizzle depends only on rl and the +8, and the column
+  // chunk's swizzled bits only on db % 4, so 8 per-tile pointers plus immediates address all 64 fragments
+  // (F = 16 case).
+  const int rl = g * 4 + ((lane & 15) >> 2);
+  const int cl = ((lane & 31) >> 4) * 2 + ((lane & 3) >> 1);  // chunk within a 32-column block
+  const int sub = (lane & 1) * 8;                              // byte offset inside the chunk
+  const char* vt = tile + wj * R;                              // this wave's R/2 columns start R bytes in
+  const char* pvp[2][4];
+  if constexpr (TL::CK >= 16) {
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int d4 = 0; d4 < 4; ++d4)
+        pvp[s2][d4] = vt + (rl + 8 * s2) * (R * 2) + (((d4 * 4 + cl) ^ swz<TL::CK>(rl + 8 * s2)) << 4) + sub;
+  }
+  auto vfrag = [&](int idx) -> bf16x8 {  // idx = (h2*2 + kb2)*DB + db
+    const int hk = idx / DB, db = idx % DB, rb = (hk >> 1) * 32 + (hk & 1) * 16;
+    const char *p0, *p1;
+    if constexpr (TL::CK >= 16) {
+      const int imm = rb * (R * 2) + (db >> 2) * 256;
+      p0 = pvp[0][db & 3] + imm;
+      p1 = pvp[1][db & 3] + imm;
+    } else {
+      const int ch = (wj * (R / 2) + db * 32) / 8 + cl;
+      p0 = tile + TL::ckv(rb + rl, ch) + sub;
+      p1 = tile + TL::ckv(rb + rl + 8, ch) + sub;
+    }
+    return concat_tr(lds_read_tr16(p0), lds_read_tr16(p1));
+  };
+  constexpr int NV = 4 * DB, VD = 3;
+  bf16x8 vf[VD];
+#pragma unroll
+  for (int i = 0; i < VD; ++i) vf[i] = vfrag(i);
+#pragma unroll
+  for (int idx = 0; idx < NV; ++idx) {
+    const int hk = idx / DB, db = idx % DB, h2 = hk >> 1, kb2 = hk & 1;
+    const bf16x8 a = vf[idx % VD];
+    if (idx + VD < NV) vf[idx % VD] = vfrag(idx + VD);
+    const bf16x8 pb = (h2 == wj) ? pk[kb2] : po[kb2];
+    o[db] = mfma32(a, pb, o[db]);
+  }
+}
+
+// Workgroup = 4 waves over 64 query rows (m = t*H + h).  Wave (wi, wj): rows wi*32..+31; scores for KV rows
+// wj*32..+31 of each tile; values for latent columns wj*R/2..+R/2.  Lane l owns row m = tile_row + wi*32 + l%32.
+// Two LDS tiles: while one is computed, the next is gathered by DMA (issued right after the tile barrier).
 template <int R, int DR>
 __global__ __launch_bounds__(NTHREADS, 1) void splitkv_kernel(
     const uint16_t* __restrict__ q_cat, const uint16_t* __restrict__ c_kv, const uint16_t* __restrict__ k_pe,
     const int32_t* __restrict__ page_table, const uint32_t* __restrict__ mask, int L, int T, int H, int M, int N,
     int m_tiles, int tiles_per_split, float scale_log2, float* __restrict__ part_o, float2* __restrict__ part_ml,
     int Mp) {
-  using S = Shape<R, DR>;
-  __shared__ __attribute__((aligned(16))) uint16_t kv[KV_TILE * S::PITCH];
+  using TL = TileLayout<R, DR>;
+  constexpr int DQ = R + DR, KB = DQ / 16, DB = R / 64;
+  __shared__ __attribute__((aligned(1024))) char kvbuf[2 * TL::BYTES];
   __shared__ uint4 pbuf[2][2][64][2];  // [row pair][kv half][lane][16-row k-block]: P^T fragments (bf16)
-  __shared__ float xch[2][2][32];      // per-row max / sum exchange within a row pair
-  __shared__ int slots[KV_TILE];
+  __shared__ float mxch[2][2][32];     // proposed reference per row, per wave
+  __shared__ float psum[2][2][64];     // per-lane half-tile row sums, per wave
 
   const int mt = blockIdx.x % m_tiles;
   const int split = blockIdx.x / m_tiles;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wi = wave >> 1, wj = wave & 1;
   const int g = lane >> 5, c = lane & 31;
   const int m = mt * M_TILE + wi * 32 + c;
 
-  bf16x8 q[S::KB];
-  const bool row_ok = m < M;
-#pragma unroll
-  for (int kb = 0; kb < S::KB; ++kb)
-    q[kb] = row_ok ? load_bf16x8(q_cat + (size_t)m * S::DQ + kb * 16 + g * 8) : zero_bf16x8();
-  uint32_t mw0 = 0xffffffffu, mw1 = 0xffffffffu;
-  if (row_ok) {
-    const int t = m / H, W = (T + 31) >> 5;
-    mw0 = mask[t * W];
-    mw1 = (W == 2) ? mask[t * W + 1] : 0u;
-  }
-
-  f32x16 o[S::DB];
-#pragma unroll
-  for (int db = 0; db < S::DB; ++db) o[db] = zero16();
-  float m_run = -INFINITY, l_part = 0.f;
-
   const int ntiles = (N + KV_TILE - 1) / KV_TILE;
   const int tile_begin = split * tiles_per_split;
   const int tile_end = min(tile_begin + tiles_per_split, ntiles);
+
+  // prologue: gather the first tile while the query fragments load
+  int slot_v = page_table[min(tile_begin * KV_TILE + lane, N - 1)];  // rows past N reuse a real row (masked)
+  dma_tile<R, DR>(kvbuf, c_kv, k_pe, slot_v, wave, lane);
+  if (tile_begin + 1 < tile_end) slot_v = page_table[min((tile_begin + 1) * KV_TILE + lane, N - 1)];
+
+  // Padding rows (m >= M) repeat the last real row; their partials are never read.
+  const int me = min(m, M - 1);
+  bf16x8 q[KB];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) q[kb] = load_bf16x8(q_cat + (size_t)me * DQ + kb * 16 + g * 8);
+  const int t_row = me / H, W = (T + 31) >> 5;
+  const uint32_t mw0 = mask[t_row * W];
+  const uint32_t mw1 = (W == 2) ? mask[t_row * W + 1] : 0u;
+  f32x16 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = zero16();
+  RowState st{-INFINITY, 0.f};
+  uint4(*pb_own)[2] = pbuf[wi][wj];
+  uint4(*pb_oth)[2] = pbuf[wi][wj ^ 1];
+  float* mx_own = mxch[wi][wj];
+  const float* mx_oth = mxch[wi][wj ^ 1];
+  float* ps_own = psum[wi][wj];
+  const float* ps_oth = psum[wi][wj ^ 1];
+
   for (int tile = tile_begin; tile < tile_end; ++tile) {
-    const int n0 = tile * KV_TILE;
-    __syncthreads();  // every wave is done with the previous tile
-    if (tid < KV_TILE) slots[tid] = page_table[min(n0 + tid, N - 1)];  // rows past N reuse a real row (masked)
-    __syncthreads();
-#pragma unroll 6
-    for (int ci = tid; ci < KV_TILE * S::CH; ci += NTHREADS) {
-      const int row = ci / S::CH, ch = ci % S::CH;
-      const size_t slot = (size_t)slots[row];
-      const uint16_t* src = (ch < R / 8) ? (c_kv + slot * R + ch * 8) : (k_pe + slot * DR + (ch - R / 8) * 8);
-      *reinterpret_cast<uint4*>(&kv[row * S::PITCH + ch * 8]) = *reinterpret_cast<const uint4*>(src);
+    const int cur = (tile - tile_begin) & 1;
+    wait_vmem_all();  // this wave's share of the current tile has landed
+    __syncthreads();  // ... and every wave's; the other buffer and the exchange buffers are free
+    if (tile + 1 < tile_end) {
+      dma_tile<R, DR>(kvbuf + (cur ^ 1) * TL::BYTES, c_kv, k_pe, slot_v, wave, lane);
+      if (tile + 2 < tile_end) slot_v = page_table[min((tile + 2) * KV_TILE + lane, N - 1)];
     }
-    __syncthreads();
-
-    // scores for KV rows wj*32 + (r/4)*8 + g*4 + r%4 of the tile, query row m
-    f32x16 acc = zero16();
-    const uint16_t* krow = &kv[(wj * 32 + c) * S::PITCH + g * 8];
-#pragma unroll
-    for (int kb = 0; kb < S::KB; ++kb)
-      acc = mfma32(*reinterpret_cast<const bf16x8*>(krow + kb * 16), q[kb], acc);
-
-    float p[16];
-    float tmax = -INFINITY;
-    const bool tail = n0 + KV_TILE > L;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float sv = acc[r] * scale_log2;
-      if (tail) {
-        const int n = n0 + wj * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
-        if (n >= L) {
-          const int jn = n - L;
-          const uint32_t word = jn < 32 ? mw0 : mw1;
-          const bool vis = (n < N) && ((word >> (jn & 31)) & 1u);
-          if (!vis) sv = -INFINITY;
-        }
-      }
-      p[r] = sv;
-      tmax = fmaxf(tmax, sv);
-    }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    if (g == 0) xch[wi][wj][c] = tmax;
-    __syncthreads();
-    tmax = fmaxf(tmax, xch[wi][wj ^ 1][c]);
-    const float m_new = fmaxf(m_run, tmax);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;  // all-masked so far: keep exp2 finite
-    const float alpha = fast_exp2(m_run - m_use);
-    float rsum = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      p[r] = fast_exp2(p[r] - m_use);
-      rsum += p[r];
-    }
-    l_part = l_part * alpha + rsum;
-    m_run = m_new;
-    if (__any(alpha != 1.f)) {
-#pragma unroll
-      for (int db = 0; db < S::DB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-    }
-    bf16x8 pk[2];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      pk[0][e] = (__bf16)p[e];
-      pk[1][e] = (__bf16)p[8 + e];
-    }
-    pbuf[wi][wj][lane][0] = __builtin_bit_cast(uint4, pk[0]);
-    pbuf[wi][wj][lane][1] = __builtin_bit_cast(uint4, pk[1]);
-    __syncthreads();
-    bf16x8 po[2];
-    po[0] = __builtin_bit_cast(bf16x8, pbuf[wi][wj ^ 1][lane][0]);
-    po[1] = __builtin_bit_cast(bf16x8, pbuf[wi][wj ^ 1][lane][1]);
-
-    // O^T[d][m] += sum_n V^T[d][n] P^T[n][m]; contraction order within a 16-row block follows the score
-    // layout: k = g*8 + e  <->  KV row (e/4)*8 + g*4 + e%4.
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) {
-        const bf16x8 pb = (h2 == wj) ? pk[kb2] : po[kb2];
-        const int row = h2 * 32 + kb2 * 16 + g * 4 + ((lane & 15) >> 2);
-#pragma unroll
-        for (int db = 0; db < S::DB; ++db) {
-          const int col = wj * (R / 2) + db * 32 + ((lane & 31) >> 4) * 16 + 4 * (lane & 3);
-          const bf16x8 a = concat_tr(lds_read_tr16(&kv[row * S::PITCH + col]),
-                                     lds_read_tr16(&kv[(row + 8) * S::PITCH + col]));
-          o[db] = mfma32(a, pb, o[db]);
-        }
-      }
-    }
+    tile_compute<R, DR>(kvbuf + cur * TL::BYTES, q, o, st, tile * KV_TILE, L, N, mw0, mw1, scale_log2, pb_own,
+                        pb_oth, ps_own, ps_oth, mx_own, mx_oth, wj, lane);
   }
 
-  const float l_half = l_part + __shfl_xor(l_part, 32);
-  __syncthreads();
-  if (g == 0) xch[wi][wj][c] = l_half;
-  __syncthreads();
-  const float l_tot = l_half + xch[wi][wj ^ 1][c];
+  const float l_row = st.l + __shfl_xor(st.l, 32);
   const int mrow = mt * M_TILE + wi * 32 + c;
   float* dst = part_o + ((size_t)split * Mp + mrow) * R + wj * (R / 2) + g * 4;
 #pragma unroll
-  for (int db = 0; db < S::DB; ++db)
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4)
       *reinterpret_cast<float4*>(dst + db * 32 + q4 * 8) =
           make_float4(o[db][q4 * 4 + 0], o[db][q4 * 4 + 1], o[db][q4 * 4 + 2], o[db][q4 * 4 + 3]);
-  if (wj == 0 && g == 0) part_ml[(size_t)split * Mp + mrow] = make_float2(m_run, l_tot);
+  if (wj == 0 && g == 0) part_ml[(size_t)split * Mp + mrow] = make_float2(st.m_ref, l_row);
 }
 
 // ------------------------------------------------------------------------------------------------ combine
