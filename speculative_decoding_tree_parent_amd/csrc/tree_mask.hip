@@ -11,8 +11,10 @@ namespace kdv {
 __global__ __launch_bounds__(64) void tree_mask_kernel(const int32_t* __restrict__ parent, int T,
                                                        uint32_t* __restrict__ mask, int32_t* __restrict__ status) {
   __shared__ int any_bad;
+  __shared__ int par[KDV_MAX_TREE_NODES];  // the walk reads parents from LDS: one global load per node
   const int i = threadIdx.x;
   if (i == 0) any_bad = 0;
+  if (i < T) par[i] = parent[i];
   __syncthreads();
   if (i < T) {
     uint32_t w0 = 0u, w1 = 0u;
@@ -20,7 +22,7 @@ __global__ __launch_bounds__(64) void tree_mask_kernel(const int32_t* __restrict
     // Walk i -> parent -> ... -> root.  A valid chain strictly decreases, so T steps always suffice.
     for (int step = 0; step < KDV_MAX_TREE_NODES; ++step) {
       if (j < 32) w0 |= 1u << j; else w1 |= 1u << (j - 32);
-      const int p = parent[j];
+      const int p = par[j];
       const bool ok = (j == 0) ? (p == -1) : (p >= 0 && p < j);
       if (!ok) {
         if (j == i) atomicOr(&any_bad, 1);   // report each invalid row once, from its own lane

@@ -23,6 +23,7 @@ namespace kdv {
 constexpr int KV_TILE = 64;   // KV rows per LDS tile
 constexpr int M_TILE = 64;    // query rows (node, head) per split-KV workgroup
 constexpr int NTHREADS = 256;
+constexpr int NUM_XCD = 8;    // MI355X: 8 accelerator complex dies, each with its own L2
 
 template <int R, int DR>
 struct Shape {
@@ -64,6 +65,11 @@ __global__ __launch_bounds__(NTHREADS) void q_absorb_kernel(const uint16_t* __re
           *reinterpret_cast<const uint4*>(q_rope + ((size_t)t * H + h) * DR + col);
     }
   }
+  // the first 32 nodes' query fragments are requested before the barrier, overlapping the W_UK staging
+  bf16x8 qb[DN / 16];
+#pragma unroll
+  for (int kb = 0; kb < DN / 16; ++kb)
+    qb[kb] = (c < T) ? load_bf16x8(q_nope + ((size_t)c * H + h) * DN + kb * 16 + g * 8) : zero_bf16x8();
   __syncthreads();
   const int rs = wave * 32;
   if (r0 + rs >= R) return;  // wave-uniform; no barrier follows
@@ -75,7 +81,8 @@ __global__ __launch_bounds__(NTHREADS) void q_absorb_kernel(const uint16_t* __re
       const int krow = kb * 16 + g * 8 + ((lane & 15) >> 2);
       const int col = rs + ((lane & 31) >> 4) * 16 + 4 * (lane & 3);
       const bf16x8 a = concat_tr(lds_read_tr16(&w_s[krow * WP + col]), lds_read_tr16(&w_s[(krow + 4) * WP + col]));
-      const bf16x8 b = (t < T) ? load_bf16x8(q_nope + ((size_t)t * H + h) * DN + kb * 16 + g * 8) : zero_bf16x8();
+      const bf16x8 b = (tb == 0) ? qb[kb]
+                     : (t < T) ? load_bf16x8(q_nope + ((size_t)t * H + h) * DN + kb * 16 + g * 8) : zero_bf16x8();
       acc = mfma32(a, b, acc);
     }
     if (t < T) {
@@ -98,11 +105,14 @@ __global__ __launch_bounds__(NTHREADS) void q_absorb_kernel(const uint16_t* __re
 // Within a row the 16-byte chunks are XOR-swizzled (chunk c of row r is stored at c ^ swz(r)) so that
 //   - the score MFMA's 16 lanes, which read the same chunk of 16 consecutive rows, hit 16 distinct bank
 //     groups, and
-//   - the value MFMA's transposed reads, 4 consecutive rows x 2 adjacent chunks per 16 lanes, hit 8.
+//   - the value MFMA's transposed reads, 4 consecutive rows x 4 adjacent chunks per 32 lanes, hit 16.
 // The swizzle replaces row padding, so two tiles fit in LDS (2 x 72 KB for the Kimi shape).
+// For rows of >= 16 chunks, swz(r) = 4*(r % 4) + (r / 4) % 4: any 16 aligned rows get 16 distinct values (score
+// reads), and the 32 lanes of a transposed read -- 4 aligned rows x 4 adjacent chunks -- land on 16 distinct
+// 16-byte bank groups.  Narrower rows (test shape) use a simpler row-dependent rotation.
 template <int C>  // C = 16-byte chunks per row
 __device__ __forceinline__ int swz(int row) {
-  if constexpr (C >= 16) return ((row & 7) << 1) | ((row >> 3) & 1);
+  if constexpr (C >= 16) return ((row & 3) << 2) | ((row >> 2) & 3);
   else return (row >> (C == 8 ? 1 : C == 4 ? 2 : 3)) & (C - 1);
 }
 
@@ -126,6 +136,10 @@ struct TileLayout {
 // the prefetch before every read of the other buffer) nor keeps per-instruction 64-bit addresses live;
 // completion is awaited explicitly (wait_vmem_all + barrier) before a tile is read.
 // `slot_v` holds, in lane j, the pool slot of tile row j; the work is split over the 4 waves.
+// M0 is listed as clobbered; the compiler treats it as reserved and does not preserve it around the asm, which
+// is harmless here because nothing else in these kernels reads M0 (no LDS-DMA builtins, GWS or message ops).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16_uniform_base(const void* sbase, uint32_t voff, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
                "s"(lds_addr)
@@ -135,6 +149,7 @@ __device__ __forceinline__ void dma16_lane_addr(const void* vaddr, uint32_t lds_
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(vaddr), "s"(lds_addr)
                : "memory", "m0");
 }
+#pragma clang diagnostic pop
 __device__ __forceinline__ uint32_t lds_address(const void* p) {
   return (uint32_t)(size_t)(const __attribute__((address_space(3))) char*)(p);
 }
@@ -202,7 +217,7 @@ struct SplitArgs {
 template <int R, int DR>
 __device__ __forceinline__ void tile_compute(const char* tile, const bf16x8 (&q)[(R + DR) / 16], f32x16 (&o)[R / 64],
                                              RowState& st, int n0, int L, int N, uint32_t mw0, uint32_t mw1,
-                                             float scale_log2, uint4 (*pb_own)[2], uint4 (*pb_oth)[2],
+                                             float scale_log2, uint4 (*pb_own)[64], uint4 (*pb_oth)[64],
                                              float* ps_own, const float* ps_oth, float* mx_own, const float* mx_oth,
                                              int wj, int lane) {
   using TL = TileLayout<R, DR>;
@@ -226,8 +241,10 @@ __device__ __forceinline__ void tile_compute(const char* tile, const bf16x8 (&q)
     const char* p = (kb < R / 16) ? ckp[kb % PK] + (kb / PK) * FK * 16 : kpp[kr % PP] + (kr / PP) * FP * 16;
     return *reinterpret_cast<const bf16x8*>(p);
   };
-  // software pipeline: fragment kb+QD is requested before the MFMA of kb
-  constexpr int QD = 4;
+  // Software pipeline: fragment kb+QD is requested before the MFMA of kb.  With one wave per SIMD nothing else
+  // hides LDS latency, so the order is pinned with scheduling fences (the compiler would otherwise shorten
+  // the pipeline to save registers).
+  constexpr int QD = KB < 6 ? KB : 6;
   bf16x8 kf[QD];
 #pragma unroll
   for (int i = 0; i < QD; ++i) kf[i] = kfrag(i);
@@ -235,7 +252,9 @@ __device__ __forceinline__ void tile_compute(const char* tile, const bf16x8 (&q)
   for (int kb = 0; kb < KB; ++kb) {
     const bf16x8 a = kf[kb % QD];
     if (kb + QD < KB) kf[kb % QD] = kfrag(kb + QD);
+    __builtin_amdgcn_sched_barrier(0);
     acc = mfma32(a, q[kb], acc);
+    __builtin_amdgcn_sched_barrier(0);
   }
   float s[16];
 #pragma unroll
@@ -267,14 +286,14 @@ __device__ __forceinline__ void tile_compute(const char* tile, const bf16x8 (&q)
     pk[0][e] = (__bf16)p0;
     pk[1][e] = (__bf16)p1;
   }
-  pb_own[lane][0] = __builtin_bit_cast(uint4, pk[0]);
-  pb_own[lane][1] = __builtin_bit_cast(uint4, pk[1]);
+  pb_own[0][lane] = __builtin_bit_cast(uint4, pk[0]);
+  pb_own[1][lane] = __builtin_bit_cast(uint4, pk[1]);
   ps_own[lane] = ps;
   if (g == 0) mx_own[c] = prop;
   __syncthreads();
   bf16x8 po[2];
-  po[0] = __builtin_bit_cast(bf16x8, pb_oth[lane][0]);
-  po[1] = __builtin_bit_cast(bf16x8, pb_oth[lane][1]);
+  po[0] = __builtin_bit_cast(bf16x8, pb_oth[0][lane]);
+  po[1] = __builtin_bit_cast(bf16x8, pb_oth[1][lane]);
   const float ps_o = ps_oth[lane];
   const float poth = mx_oth[c];
   // ---- agree on M = max of both proposals; rescale by exact powers of two
@@ -335,7 +354,7 @@ __device__ __forceinline__ void tile_compute(const char* tile, const bf16x8 (&q)
     }
     return concat_tr(lds_read_tr16(p0), lds_read_tr16(p1));
   };
-  constexpr int NV = 4 * DB, VD = 3;
+  constexpr int NV = 4 * DB, VD = NV < 4 ? NV : 4;
   bf16x8 vf[VD];
 #pragma unroll
   for (int i = 0; i < VD; ++i) vf[i] = vfrag(i);
@@ -345,7 +364,9 @@ __device__ __forceinline__ void tile_compute(const char* tile, const bf16x8 (&q)
     const bf16x8 a = vf[idx % VD];
     if (idx + VD < NV) vf[idx % VD] = vfrag(idx + VD);
     const bf16x8 pb = (h2 == wj) ? pk[kb2] : po[kb2];
+    __builtin_amdgcn_sched_barrier(0);
     o[db] = mfma32(a, pb, o[db]);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -356,17 +377,21 @@ template <int R, int DR>
 __global__ __launch_bounds__(NTHREADS, 1) void splitkv_kernel(
     const uint16_t* __restrict__ q_cat, const uint16_t* __restrict__ c_kv, const uint16_t* __restrict__ k_pe,
     const int32_t* __restrict__ page_table, const uint32_t* __restrict__ mask, int L, int T, int H, int M, int N,
-    int m_tiles, int tiles_per_split, float scale_log2, float* __restrict__ part_o, float2* __restrict__ part_ml,
-    int Mp) {
+    int m_tiles, int tiles_per_split, int num_splits, float scale_log2, float* __restrict__ part_o,
+    float2* __restrict__ part_ml, int Mp) {
   using TL = TileLayout<R, DR>;
   constexpr int DQ = R + DR, KB = DQ / 16, DB = R / 64;
   __shared__ __attribute__((aligned(1024))) char kvbuf[2 * TL::BYTES];
-  __shared__ uint4 pbuf[2][2][64][2];  // [row pair][kv half][lane][16-row k-block]: P^T fragments (bf16)
+  __shared__ uint4 pbuf[2][2][2][64];  // [row pair][kv half][16-row k-block][lane]: P^T fragments (bf16)
   __shared__ float mxch[2][2][32];     // proposed reference per row, per wave
   __shared__ float psum[2][2][64];     // per-lane half-tile row sums, per wave
 
-  const int mt = blockIdx.x % m_tiles;
-  const int split = blockIdx.x / m_tiles;
+  // Workgroups are dealt to the XCDs round-robin (block b -> XCD b % NUM_XCD).  Every query tile of one KV
+  // split is kept on one XCD so that split's rows are fetched into that XCD's L2 once and then shared.
+  const int xcd = blockIdx.x % NUM_XCD, j = blockIdx.x / NUM_XCD;
+  const int split = xcd + NUM_XCD * (j / m_tiles);
+  const int mt = j % m_tiles;
+  if (split >= num_splits) return;  // padding block (uniform; before any barrier)
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wi = wave >> 1, wj = wave & 1;
@@ -387,6 +412,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void splitkv_kernel(
   bf16x8 q[KB];
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) q[kb] = load_bf16x8(q_cat + (size_t)me * DQ + kb * 16 + g * 8);
+  // Register classes: the query fragments (MFMA B operands) live in AGPRs and the O accumulators in VGPRs
+  // (MFMA's VGPR form, selected at build time), so the softmax rescale of O needs no AGPR<->VGPR copies.
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) asm volatile("" : "+a"(q[kb]));
   const int t_row = me / H, W = (T + 31) >> 5;
   const uint32_t mw0 = mask[t_row * W];
   const uint32_t mw1 = (W == 2) ? mask[t_row * W + 1] : 0u;
@@ -394,8 +423,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void splitkv_kernel(
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = zero16();
   RowState st{-INFINITY, 0.f};
-  uint4(*pb_own)[2] = pbuf[wi][wj];
-  uint4(*pb_oth)[2] = pbuf[wi][wj ^ 1];
+  uint4(*pb_own)[64] = pbuf[wi][wj];
+  uint4(*pb_oth)[64] = pbuf[wi][wj ^ 1];
   float* mx_own = mxch[wi][wj];
   const float* mx_oth = mxch[wi][wj ^ 1];
   float* ps_own = psum[wi][wj];
@@ -409,44 +438,53 @@ __global__ __launch_bounds__(NTHREADS, 1) void splitkv_kernel(
       dma_tile<R, DR>(kvbuf + (cur ^ 1) * TL::BYTES, c_kv, k_pe, slot_v, wave, lane);
       if (tile + 2 < tile_end) slot_v = page_table[min((tile + 2) * KV_TILE + lane, N - 1)];
     }
+#pragma unroll
+    for (int db = 0; db < DB; ++db) asm volatile("" : "+v"(o[db]));
     tile_compute<R, DR>(kvbuf + cur * TL::BYTES, q, o, st, tile * KV_TILE, L, N, mw0, mw1, scale_log2, pb_own,
                         pb_oth, ps_own, ps_oth, mx_own, mx_oth, wj, lane);
   }
 
   const float l_row = st.l + __shfl_xor(st.l, 32);
-  const int mrow = mt * M_TILE + wi * 32 + c;
-  float* dst = part_o + ((size_t)split * Mp + mrow) * R + wj * (R / 2) + g * 4;
+  // Partial O in register-fragment order: [split][m tile][wave][column block][q4][lane] float4, so every store
+  // instruction writes 1 KB contiguously.  (max, sum) per row: [split][row].
+  float4* dst = reinterpret_cast<float4*>(part_o) + ((size_t)(split * m_tiles + mt) * 4 + wave) * DB * 4 * 64 + lane;
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4)
-      *reinterpret_cast<float4*>(dst + db * 32 + q4 * 8) =
-          make_float4(o[db][q4 * 4 + 0], o[db][q4 * 4 + 1], o[db][q4 * 4 + 2], o[db][q4 * 4 + 3]);
-  if (wj == 0 && g == 0) part_ml[(size_t)split * Mp + mrow] = make_float2(st.m_ref, l_row);
+      dst[(db * 4 + q4) * 64] = make_float4(o[db][q4 * 4 + 0], o[db][q4 * 4 + 1], o[db][q4 * 4 + 2], o[db][q4 * 4 + 3]);
+  if (wj == 0 && g == 0) part_ml[(size_t)split * Mp + mt * M_TILE + wi * 32 + c] = make_float2(st.m_ref, l_row);
 }
 
 // ------------------------------------------------------------------------------------------------ combine
 // o_lat[m] = sum_s 2^(m_s - M) O_s[m] / sum_s 2^(m_s - M) l_s,  lse[m] = ln 2 * (M + log2 sum_s 2^(m_s-M) l_s).
 // A split in which row m saw nothing has m_s = -inf and l_s = 0 and gets weight 0.
+// One workgroup per (query tile, split-KV wave, 32-column block): thread (q4, lane) holds exactly the float4 that
+// lane wrote for fragment q4, so each split contributes one contiguous 4 KB read per workgroup.
 template <int R>
 __global__ __launch_bounds__(NTHREADS) void combine_kernel(const float* __restrict__ part_o,
-                                                           const float2* __restrict__ part_ml, int S, int Mp,
-                                                           int M, uint16_t* __restrict__ o_lat,
+                                                           const float2* __restrict__ part_ml, int S, int m_tiles,
+                                                           int Mp, int M, uint16_t* __restrict__ o_lat,
                                                            float* __restrict__ lse) {
-  constexpr int TPR = R / 4;
-  constexpr int RPB = NTHREADS / TPR;
-  const int m = blockIdx.x * RPB + threadIdx.x / TPR;
-  const int d = (threadIdx.x % TPR) * 4;
+  constexpr int DB = R / 64;
+  const int blk = blockIdx.x;
+  const int db = blk % DB, wave = (blk / DB) % 4, mt = blk / (DB * 4);
+  const int q4 = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wi = wave >> 1, wj = wave & 1, g = lane >> 5, c = lane & 31;
+  const int m = mt * M_TILE + wi * 32 + c;
   if (m >= M) return;
+  const int d = wj * (R / 2) + db * 32 + q4 * 8 + g * 4;
   float mx = -INFINITY;
   for (int s = 0; s < S; ++s) mx = fmaxf(mx, part_ml[(size_t)s * Mp + m].x);
+  const size_t stride = (size_t)m_tiles * 4 * DB * 4 * 64;  // float4s per split
+  const float4* src = reinterpret_cast<const float4*>(part_o) + ((size_t)mt * 4 + wave) * DB * 4 * 64 + (db * 4 + q4) * 64 + lane;
   float den = 0.f;
   float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int s = 0; s < S; ++s) {
     const float2 ml = part_ml[(size_t)s * Mp + m];
     const float w = (ml.x == -INFINITY) ? 0.f : fast_exp2(ml.x - mx);
     den += w * ml.y;
-    const float4 v = *reinterpret_cast<const float4*>(part_o + ((size_t)s * Mp + m) * R + d);
+    const float4 v = src[s * stride];
     num.x += w * v.x;
     num.y += w * v.y;
     num.z += w * v.z;
@@ -546,9 +584,11 @@ static int make_plan(const kdv_mla_dims* d, int T, int L, Plan* p) {
   int want = 0;
   if (const char* env = getenv("KDV_SPLITS")) want = atoi(env);
   if (want <= 0) {
+    // One workgroup per CU, all query tiles of a split on one XCD: NUM_XCD * floor(CUs per XCD / query tiles).
     const int cus = device_cu_count();
     if (cus <= 0) return KDV_ERR_HIP;
-    want = cus / p->m_tiles;
+    const int per_xcd = cus / NUM_XCD;
+    want = (p->m_tiles <= per_xcd) ? NUM_XCD * (per_xcd / p->m_tiles) : cus / p->m_tiles;
     if (want < 1) want = 1;
   }
   if (want > p->ntiles) want = p->ntiles;
@@ -582,13 +622,13 @@ static void launch_all(const Plan& pl, float sm_scale, const uint16_t* q_nope, c
                      q_rope, w_uk, q_cat, T, pl.H);
   const float scale_log2 = sm_scale * 1.44269504088896340736f;
   if (ev) (void)hipEventRecord(ev[1], st);
-  hipLaunchKernelGGL((splitkv_kernel<R, DR>), dim3(pl.m_tiles * pl.splits), dim3(NTHREADS), 0, st, q_cat, c_kv,
-                     k_pe, page_table, mask, L, T, pl.H, pl.M, pl.N, pl.m_tiles, pl.tiles_per_split, scale_log2,
-                     part_o, part_ml, pl.Mp);
-  constexpr int RPB = NTHREADS / (R / 4);
+  const int grid = NUM_XCD * pl.m_tiles * ((pl.splits + NUM_XCD - 1) / NUM_XCD);
+  hipLaunchKernelGGL((splitkv_kernel<R, DR>), dim3(grid), dim3(NTHREADS), 0, st, q_cat, c_kv, k_pe, page_table,
+                     mask, L, T, pl.H, pl.M, pl.N, pl.m_tiles, pl.tiles_per_split, pl.splits, scale_log2, part_o,
+                     part_ml, pl.Mp);
   if (ev) (void)hipEventRecord(ev[2], st);
-  hipLaunchKernelGGL((combine_kernel<R>), dim3((pl.M + RPB - 1) / RPB), dim3(NTHREADS), 0, st, part_o, part_ml,
-                     pl.splits, pl.Mp, pl.M, o_lat, lse);
+  hipLaunchKernelGGL((combine_kernel<R>), dim3(pl.m_tiles * 4 * (R / 64)), dim3(NTHREADS), 0, st, part_o, part_ml,
+                     pl.splits, pl.m_tiles, pl.Mp, pl.M, o_lat, lse);
   if (ev) (void)hipEventRecord(ev[3], st);
   hipLaunchKernelGGL((up_proj_kernel<R, DV>), dim3(pl.H, DV / 32), dim3(NTHREADS), 0, st, o_lat, w_uv, out, T,
                      pl.H);
