@@ -286,6 +286,40 @@ __device__ __forceinline__ void tile_compute(const char* tile, const bf16x8 (&q)
     pk[0][e] = (__bf16)p0;
     pk[1][e] = (__bf16)p1;
   }
+  // Lane's rows are h2*32 + kb2*16 + rl (+8): the swizzle depends only on rl and the +8, and the column
+  // chunk's swizzled bits only on db % 4, so 8 per-tile pointers plus immediates address all 64 fragments
+  // (F = 16 case).
+  const int rl = g * 4 + ((lane & 15) >> 2);
+  const int cl = ((lane & 31) >> 4) * 2 + ((lane & 3) >> 1);  // chunk within a 32-column block
+  const int sub = (lane & 1) * 8;                              // byte offset inside the chunk
+  const char* vt = tile + wj * R;                              // this wave's R/2 columns start R bytes in
+  const char* pvp[2][4];
+  if constexpr (TL::CK >= 16) {
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int d4 = 0; d4 < 4; ++d4)
+        pvp[s2][d4] = vt + (rl + 8 * s2) * (R * 2) + (((d4 * 4 + cl) ^ swz<TL::CK>(rl + 8 * s2)) << 4) + sub;
+  }
+  auto vfrag = [&](int idx) -> bf16x8 {  // idx = (h2*2 + kb2)*DB + db
+    const int hk = idx / DB, db = idx % DB, rb = (hk >> 1) * 32 + (hk & 1) * 16;
+    const char *p0, *p1;
+    if constexpr (TL::CK >= 16) {
+      const int imm = rb * (R * 2) + (db >> 2) * 256;
+      p0 = pvp[0][db & 3] + imm;
+      p1 = pvp[1][db & 3] + imm;
+    } else {
+      const int ch = (wj * (R / 2) + db * 32) / 8 + cl;
+      p0 = tile + TL::ckv(rb + rl, ch) + sub;
+      p1 = tile + TL::ckv(rb + rl + 8, ch) + sub;
+    }
+    return concat_tr(lds_read_tr16(p0), lds_read_tr16(p1));
+  };
+  // the first value fragments do not depend on P: request them before the exchange barrier
+  constexpr int NV = 4 * DB, VD = NV < 4 ? NV : 4;
+  bf16x8 vf[VD];
+#pragma unroll
+  for (int i = 0; i < VD; ++i) vf[i] = vfrag(i);
   pb_own[0][lane] = __builtin_bit_cast(uint4, pk[0]);
   pb_own[1][lane] = __builtin_bit_cast(uint4, pk[1]);
   ps_own[lane] = ps;
@@ -325,39 +359,6 @@ __device__ __forceinline__ void tile_compute(const char* tile, const bf16x8 (&q)
   st.l += (wj == 0) ? (s_own + s_oth) : (s_oth + s_own);
   // ---- O^T[d][m] += sum_n V^T[d][n] P^T[n][m]; within a 16-row block the contraction index k = g*8+e is
   // KV row (e/4)*8 + g*4 + e%4, matching the score layout.
-  // Lane's rows are h2*32 + kb2*16 + rl (+8): the swizzle depends only on rl and the +8, and the column
-  // chunk's swizzled bits only on db % 4, so 8 per-tile pointers plus immediates address all 64 fragments
-  // (F = 16 case).
-  const int rl = g * 4 + ((lane & 15) >> 2);
-  const int cl = ((lane & 31) >> 4) * 2 + ((lane & 3) >> 1);  // chunk within a 32-column block
-  const int sub = (lane & 1) * 8;                              // byte offset inside the chunk
-  const char* vt = tile + wj * R;                              // this wave's R/2 columns start R bytes in
-  const char* pvp[2][4];
-  if constexpr (TL::CK >= 16) {
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-      for (int d4 = 0; d4 < 4; ++d4)
-        pvp[s2][d4] = vt + (rl + 8 * s2) * (R * 2) + (((d4 * 4 + cl) ^ swz<TL::CK>(rl + 8 * s2)) << 4) + sub;
-  }
-  auto vfrag = [&](int idx) -> bf16x8 {  // idx = (h2*2 + kb2)*DB + db
-    const int hk = idx / DB, db = idx % DB, rb = (hk >> 1) * 32 + (hk & 1) * 16;
-    const char *p0, *p1;
-    if constexpr (TL::CK >= 16) {
-      const int imm = rb * (R * 2) + (db >> 2) * 256;
-      p0 = pvp[0][db & 3] + imm;
-      p1 = pvp[1][db & 3] + imm;
-    } else {
-      const int ch = (wj * (R / 2) + db * 32) / 8 + cl;
-      p0 = tile + TL::ckv(rb + rl, ch) + sub;
-      p1 = tile + TL::ckv(rb + rl + 8, ch) + sub;
-    }
-    return concat_tr(lds_read_tr16(p0), lds_read_tr16(p1));
-  };
-  constexpr int NV = 4 * DB, VD = NV < 4 ? NV : 4;
-  bf16x8 vf[VD];
-#pragma unroll
-  for (int i = 0; i < VD; ++i) vf[i] = vfrag(i);
 #pragma unroll
   for (int idx = 0; idx < NV; ++idx) {
     const int hk = idx / DB, db = idx % DB, h2 = hk >> 1, kb2 = hk & 1;
@@ -474,21 +475,34 @@ __global__ __launch_bounds__(NTHREADS) void combine_kernel(const float* __restri
   const int m = mt * M_TILE + wi * 32 + c;
   if (m >= M) return;
   const int d = wj * (R / 2) + db * 32 + q4 * 8 + g * 4;
-  float mx = -INFINITY;
-  for (int s = 0; s < S; ++s) mx = fmaxf(mx, part_ml[(size_t)s * Mp + m].x);
   const size_t stride = (size_t)m_tiles * 4 * DB * 4 * 64;  // float4s per split
   const float4* src = reinterpret_cast<const float4*>(part_o) + ((size_t)mt * 4 + wave) * DB * 4 * 64 + (db * 4 + q4) * 64 + lane;
-  float den = 0.f;
+  // single pass, online merge; a chunk's loads are all issued before any is used
+  constexpr int CH = 8;
+  float mx = -INFINITY, den = 0.f;
   float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s = 0; s < S; ++s) {
-    const float2 ml = part_ml[(size_t)s * Mp + m];
-    const float w = (ml.x == -INFINITY) ? 0.f : fast_exp2(ml.x - mx);
-    den += w * ml.y;
-    const float4 v = src[s * stride];
-    num.x += w * v.x;
-    num.y += w * v.y;
-    num.z += w * v.z;
-    num.w += w * v.w;
+  for (int s0 = 0; s0 < S; s0 += CH) {
+    float2 ml[CH];
+    float4 v[CH];
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+      const int sk = min(s0 + k, S - 1);
+      ml[k] = part_ml[(size_t)sk * Mp + m];
+      v[k] = src[sk * stride];
+    }
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+      if (s0 + k >= S || ml[k].x == -INFINITY) continue;  // nothing visible in that split
+      const float mn = fmaxf(mx, ml[k].x);
+      const float a = fast_exp2(mx - mn);  // mx = -inf -> 0
+      const float w = fast_exp2(ml[k].x - mn);
+      den = den * a + w * ml[k].y;
+      num.x = num.x * a + w * v[k].x;
+      num.y = num.y * a + w * v[k].y;
+      num.z = num.z * a + w * v[k].z;
+      num.w = num.w * a + w * v[k].w;
+      mx = mn;
+    }
   }
   const float inv = 1.f / den;
   bf16x4 ov;
