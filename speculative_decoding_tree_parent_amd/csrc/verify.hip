@@ -154,72 +154,71 @@ __device__ __forceinline__ uint32_t lds_address(const void* p) {
   return (uint32_t)(size_t)(const __attribute__((address_space(3))) char*)(p);
 }
 
+// The DMA instructions of one tile, as issued by one wave: latent rows first (wave w takes rows w, w+4, ...),
+// then rotary rows.  `issue(k)` sends this wave's k-th instruction, so the loads of the next tile can be spread
+// between the MFMAs of the current one.  `slot_v` holds, in lane j, the pool slot of tile row j.
 template <int R, int DR>
-__device__ __forceinline__ void dma_tile(const char* buf, const uint16_t* __restrict__ c_kv,
-                                         const uint16_t* __restrict__ k_pe, int slot_v, int wave, int lane) {
+struct TileDma {
   using TL = TileLayout<R, DR>;
-  const uint32_t lbase = lds_address(buf);
-  if constexpr (TL::CK == 64) {
-    // one instruction per latent row; wave w takes rows w, w+4, ...; the row's swizzle repeats with period 4
-    uint32_t voff[4];
+  static constexpr int NKC = (TL::CK + 3) / 4, NKP = (TL::CP + 3) / 4, NK = NKC + NKP;
+  const char* c_kv;
+  const char* k_pe;
+  uint32_t lbase;
+  int slot_v, wave, lane;
+  uint32_t voff[4];  // per-lane offsets of a latent row (64-chunk rows: the swizzle repeats every 4 rows)
+
+  __device__ __forceinline__ TileDma(const uint16_t* ckv, const uint16_t* kpe, int wave_, int lane_)
+      : c_kv(reinterpret_cast<const char*>(ckv)), k_pe(reinterpret_cast<const char*>(kpe)), lbase(0), slot_v(0),
+        wave(wave_), lane(lane_) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) voff[k] = (uint32_t)((lane ^ swz<64>(wave + 4 * k)) << 4);
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
+    for (int k = 0; k < 4; ++k) voff[k] = (uint32_t)((lane ^ swz<TL::CK>(wave + 4 * k)) << 4);
+  }
+  __device__ __forceinline__ void target(const char* buf, int slots) {
+    lbase = lds_address(buf);
+    slot_v = slots;
+  }
+  __device__ __forceinline__ void issue(int k) const {
+    if (k < NKC) {
       const int i = wave + 4 * k;
-      const int slot = __builtin_amdgcn_readlane(slot_v, i);
-      dma16_uniform_base(reinterpret_cast<const char*>(c_kv) + (size_t)slot * (R * 2), voff[k & 3],
-                         lbase + i * 1024);
-    }
-  } else {
-#pragma unroll
-    for (int k = 0; k < (TL::CK + 3) / 4; ++k) {
-      const int i = wave + 4 * k;
-      if (TL::CK % 4 == 0 || i < TL::CK) {
+      if constexpr (TL::CK == 64) {
+        const int slot = __builtin_amdgcn_readlane(slot_v, i);
+        dma16_uniform_base(c_kv + (size_t)slot * (R * 2), voff[k & 3], lbase + i * 1024);
+      } else if (TL::CK % 4 == 0 || i < TL::CK) {
         const int flat = i * 64 + lane, row = flat / TL::CK, pos = flat % TL::CK;
         const int slot = __shfl(slot_v, row);
-        dma16_lane_addr(reinterpret_cast<const char*>(c_kv) + (size_t)slot * (R * 2) + ((pos ^ swz<TL::CK>(row)) << 4),
-                        lbase + i * 1024);
+        dma16_lane_addr(c_kv + (size_t)slot * (R * 2) + ((pos ^ swz<TL::CK>(row)) << 4), lbase + i * 1024);
+      }
+    } else {
+      const int j = wave + 4 * (k - NKC);
+      if (TL::CP % 4 == 0 || j < TL::CP) {
+        const int flat = j * 64 + lane, row = flat / TL::CP, pos = flat % TL::CP;
+        const int slot = __shfl(slot_v, row);
+        dma16_lane_addr(k_pe + (size_t)slot * (DR * 2) + ((pos ^ swz<TL::CP>(row)) << 4),
+                        lbase + TL::CKV_BYTES + j * 1024);
       }
     }
   }
-#pragma unroll
-  for (int k = 0; k < (TL::CP + 3) / 4; ++k) {
-    const int j = wave + 4 * k;
-    if (TL::CP % 4 == 0 || j < TL::CP) {
-      const int flat = j * 64 + lane, row = flat / TL::CP, pos = flat % TL::CP;
-      const int slot = __shfl(slot_v, row);
-      dma16_lane_addr(reinterpret_cast<const char*>(k_pe) + (size_t)slot * (DR * 2) + ((pos ^ swz<TL::CP>(row)) << 4),
-                      lbase + TL::CKV_BYTES + j * 1024);
-    }
-  }
-}
+};
 
 __device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Softmax state of one query row, held identically by the two lanes (l, l^32) that own it.
+// Softmax state of one query row, held identically by the two lanes (l, l^32) that own it and by both waves of
+// the row pair.
 struct RowState {
   float m_ref;  // reference max (log2 units; an integer or -inf): P = 2^(s - m_ref) <= 2^8
   float l;      // this lane's share of sum_n P (the lane pair adds up at the end)
 };
 
-template <int R, int DR>
-struct SplitArgs {
-  const uint16_t* __restrict__ c_kv;
-  const uint16_t* __restrict__ k_pe;
-  const int32_t* __restrict__ page_table;
-  int L, N;
-  float scale_log2;
-};
-
-// One tile: scores for this wave's 32 KV rows, lazy-reference softmax agreed with the partner wave through a
-// single LDS exchange (P halves + proposed references), then O^T += V^T P^T for the wave's R/2 columns.
+// One tile.  Wave (wi, wj) computes the scores of its 32 KV rows (half wj of the tile), proposes a softmax
+// reference, and accumulates O^T += V^T P^T for its R/2 columns over its own half first; only then does it swap
+// P halves, proposals and row sums with its partner through LDS and add the partner's half.  The next tile's
+// DMA instructions (if `dma_on`) are spread over the score MFMAs.
 template <int R, int DR>
 __device__ __forceinline__ void tile_compute(const char* tile, const bf16x8 (&q)[(R + DR) / 16], f32x16 (&o)[R / 64],
                                              RowState& st, int n0, int L, int N, uint32_t mw0, uint32_t mw1,
                                              float scale_log2, uint4 (*pb_own)[64], uint4 (*pb_oth)[64],
                                              float* ps_own, const float* ps_oth, float* mx_own, const float* mx_oth,
-                                             int wj, int lane) {
+                                             int wj, int lane, const TileDma<R, DR>& dma, bool dma_on) {
   using TL = TileLayout<R, DR>;
   constexpr int KB = (R + DR) / 16, DB = R / 64;
   const int g = lane >> 5, c = lane & 31;
@@ -228,7 +227,7 @@ __device__ __forceinline__ void tile_compute(const char* tile, const bf16x8 (&q)
   // period F/2 k-blocks plus a compile-time stride: a few per-lane bases and immediate offsets.
   constexpr int FK = TL::CK < 16 ? TL::CK : 16, PK = FK / 2;
   constexpr int FP = TL::CP < 16 ? TL::CP : 16, PP = FP / 2;
-  f32x16 acc = zero16();
+  f32x16 acc0 = zero16(), acc1 = zero16();  // two chains: a single dependent MFMA chain issues ~25% slower
   const int nrow = wj * 32 + c;
   const char* ckp[PK];
   const char* kpp[PP];
@@ -243,8 +242,10 @@ __device__ __forceinline__ void tile_compute(const char* tile, const bf16x8 (&q)
   };
   // Software pipeline: fragment kb+QD is requested before the MFMA of kb.  With one wave per SIMD nothing else
   // hides LDS latency, so the order is pinned with scheduling fences (the compiler would otherwise shorten
-  // the pipeline to save registers).
+  // the pipeline to save registers).  A DMA instruction goes out every DSTEP MFMAs: its issue stalls while the
+  // address unit drains the previous ones, and the MFMAs in flight cover that stall.
   constexpr int QD = KB < 6 ? KB : 6;
+  constexpr int DSTEP = KB / TileDma<R, DR>::NK > 0 ? KB / TileDma<R, DR>::NK : 1;
   bf16x8 kf[QD];
 #pragma unroll
   for (int i = 0; i < QD; ++i) kf[i] = kfrag(i);
@@ -252,13 +253,19 @@ __device__ __forceinline__ void tile_compute(const char* tile, const bf16x8 (&q)
   for (int kb = 0; kb < KB; ++kb) {
     const bf16x8 a = kf[kb % QD];
     if (kb + QD < KB) kf[kb % QD] = kfrag(kb + QD);
+    if (kb % DSTEP == 0 && kb / DSTEP < TileDma<R, DR>::NK && dma_on) dma.issue(kb / DSTEP);
     __builtin_amdgcn_sched_barrier(0);
-    acc = mfma32(a, q[kb], acc);
+    if (kb & 1) acc1 = mfma32(a, q[kb], acc1);
+    else acc0 = mfma32(a, q[kb], acc0);
     __builtin_amdgcn_sched_barrier(0);
+  }
+  if (KB < TileDma<R, DR>::NK && dma_on) {  // (narrow test shape: more DMA instructions than k-blocks)
+#pragma unroll
+    for (int k = KB; k < TileDma<R, DR>::NK; ++k) dma.issue(k);
   }
   float s[16];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) s[r] = acc[r] * scale_log2;
+  for (int r = 0; r < 16; ++r) s[r] = (acc0[r] + acc1[r]) * scale_log2;
   if (n0 + KV_TILE > L) {  // tile reaches the tree rows (or past N): apply the ancestor mask
     const uint64_t mw = (uint64_t)mw0 | ((uint64_t)mw1 << 32);
     const int T = N - L;
@@ -274,8 +281,16 @@ __device__ __forceinline__ void tile_compute(const char* tile, const bf16x8 (&q)
 #pragma unroll
   for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[r]);
   tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-  // ---- proposed reference: keep the current one unless this half-tile exceeds it by more than 2^8
+  // ---- proposed reference: keep the current one unless this half-tile exceeds it by more than 2^8.  If it
+  // moves, O is brought to it now (exact power of two), before this half is accumulated.
   const float prop = (tmax > st.m_ref + 8.f) ? ceilf(tmax) : st.m_ref;
+  if (__any(prop > st.m_ref)) {
+    const float a = (prop > st.m_ref) ? fast_exp2(st.m_ref - prop) : 1.f;  // m_ref = -inf -> 0
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] *= a;
+  }
   const float puse = (prop == -INFINITY) ? 0.f : prop;
   bf16x8 pk[2];
   float ps = 0.f;  // this lane's share of the half-tile row sum, unrounded
@@ -286,6 +301,14 @@ __device__ __forceinline__ void tile_compute(const char* tile, const bf16x8 (&q)
     pk[0][e] = (__bf16)p0;
     pk[1][e] = (__bf16)p1;
   }
+  pb_own[0][lane] = __builtin_bit_cast(uint4, pk[0]);
+  pb_own[1][lane] = __builtin_bit_cast(uint4, pk[1]);
+  ps_own[lane] = ps;
+  if (g == 0) mx_own[c] = prop;
+
+  // ---- O^T[d][m] += sum_n V^T[d][n] P^T[n][m]; within a 16-row block the contraction index k = g*8+e is
+  // KV row (e/4)*8 + g*4 + e%4, matching the score layout.  Fragment idx covers KV half (own first), 16-row
+  // block kb2 and column block db.
   // Lane's rows are h2*32 + kb2*16 + rl (+8): the swizzle depends only on rl and the +8, and the column
   // chunk's swizzled bits only on db % 4, so 8 per-tile pointers plus immediates address all 64 fragments
   // (F = 16 case).
@@ -301,8 +324,10 @@ __device__ __forceinline__ void tile_compute(const char* tile, const bf16x8 (&q)
       for (int d4 = 0; d4 < 4; ++d4)
         pvp[s2][d4] = vt + (rl + 8 * s2) * (R * 2) + (((d4 * 4 + cl) ^ swz<TL::CK>(rl + 8 * s2)) << 4) + sub;
   }
-  auto vfrag = [&](int idx) -> bf16x8 {  // idx = (h2*2 + kb2)*DB + db
-    const int hk = idx / DB, db = idx % DB, rb = (hk >> 1) * 32 + (hk & 1) * 16;
+  constexpr int NV = 4 * DB, NH = NV / 2, VD = NV < 6 ? NV : 6;
+  auto vfrag = [&](int idx) -> bf16x8 {
+    const int h2 = (idx < NH) ? wj : (wj ^ 1), kb2 = (idx % NH) / DB, db = idx % DB;
+    const int rb = h2 * 32 + kb2 * 16;
     const char *p0, *p1;
     if constexpr (TL::CK >= 16) {
       const int imm = rb * (R * 2) + (db >> 2) * 256;
@@ -315,70 +340,63 @@ __device__ __forceinline__ void tile_compute(const char* tile, const bf16x8 (&q)
     }
     return concat_tr(lds_read_tr16(p0), lds_read_tr16(p1));
   };
-  // the first value fragments do not depend on P: request them before the exchange barrier
-  constexpr int NV = 4 * DB, VD = NV < 4 ? NV : 4;
   bf16x8 vf[VD];
 #pragma unroll
   for (int i = 0; i < VD; ++i) vf[i] = vfrag(i);
-  pb_own[0][lane] = __builtin_bit_cast(uint4, pk[0]);
-  pb_own[1][lane] = __builtin_bit_cast(uint4, pk[1]);
-  ps_own[lane] = ps;
-  if (g == 0) mx_own[c] = prop;
-  __syncthreads();
   bf16x8 po[2];
-  po[0] = __builtin_bit_cast(bf16x8, pb_oth[0][lane]);
-  po[1] = __builtin_bit_cast(bf16x8, pb_oth[1][lane]);
-  const float ps_o = ps_oth[lane];
-  const float poth = mx_oth[c];
-  // ---- agree on M = max of both proposals; rescale by exact powers of two
-  const float M = fmaxf(prop, poth);
-  const bool live = M != -INFINITY;
-  const float f_own = live ? fast_exp2(prop - M) : 1.f;
-  const float f_oth = live ? fast_exp2(poth - M) : 1.f;
-  if (__any(f_own != 1.f || f_oth != 1.f)) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        pk[h][e] = (__bf16)((float)pk[h][e] * f_own);
-        po[h][e] = (__bf16)((float)po[h][e] * f_oth);
-      }
-  }
-  if (__any(M > st.m_ref)) {
-    const float alpha = (M > st.m_ref) ? fast_exp2(st.m_ref - M) : 1.f;  // m_ref = -inf -> 0
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-    st.l *= alpha;
-  }
-  st.m_ref = fmaxf(st.m_ref, M);
-  // row sum: both halves' unrounded sums, rescaled exactly and added in a fixed order (KV half 0 first) so that
-  // both waves of the pair hold the same bits
-  const float s_own = ps * f_own, s_oth = ps_o * f_oth;
-  st.l += (wj == 0) ? (s_own + s_oth) : (s_oth + s_own);
-  // ---- O^T[d][m] += sum_n V^T[d][n] P^T[n][m]; within a 16-row block the contraction index k = g*8+e is
-  // KV row (e/4)*8 + g*4 + e%4, matching the score layout.
+  float poth = 0.f, ps_o = 0.f, M = prop;
 #pragma unroll
   for (int idx = 0; idx < NV; ++idx) {
-    const int hk = idx / DB, db = idx % DB, h2 = hk >> 1, kb2 = hk & 1;
+    if (idx == NH) {
+      // ---- partner's half: exchange, agree on M = max of both proposals, rescale by exact powers of two
+      __syncthreads();
+      po[0] = __builtin_bit_cast(bf16x8, pb_oth[0][lane]);
+      po[1] = __builtin_bit_cast(bf16x8, pb_oth[1][lane]);
+      ps_o = ps_oth[lane];
+      poth = mx_oth[c];
+      M = fmaxf(prop, poth);
+      if (__any(M > prop)) {
+        const float b = (M > prop) ? fast_exp2(prop - M) : 1.f;  // prop = -inf -> 0 (O holds nothing yet)
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[db][r] *= b;
+      }
+      const float f_oth = (M != -INFINITY) ? fast_exp2(poth - M) : 1.f;
+      if (__any(f_oth != 1.f)) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) po[h][e] = (__bf16)((float)po[h][e] * f_oth);
+      }
+    }
+    const int kb2 = (idx % NH) / DB, db = idx % DB;
     const bf16x8 a = vf[idx % VD];
     if (idx + VD < NV) vf[idx % VD] = vfrag(idx + VD);
-    const bf16x8 pb = (h2 == wj) ? pk[kb2] : po[kb2];
+    const bf16x8 pb = (idx < NH) ? pk[kb2] : po[kb2];
     __builtin_amdgcn_sched_barrier(0);
     o[db] = mfma32(a, pb, o[db]);
     __builtin_amdgcn_sched_barrier(0);
+  }
+  // ---- row sum relative to M, from both halves' unrounded sums, in a fixed order (KV half 0 first) so that both
+  // waves of the pair hold the same bits
+  if (M != -INFINITY) {
+    const float p0 = (wj == 0) ? prop : poth, p1 = (wj == 0) ? poth : prop;
+    const float q0 = (wj == 0) ? ps : ps_o, q1 = (wj == 0) ? ps_o : ps;
+    const float keep = fast_exp2(st.m_ref - M);  // m_ref = -inf -> 0
+    st.l = st.l * keep + (q0 * fast_exp2(p0 - M) + q1 * fast_exp2(p1 - M));
+    st.m_ref = M;
   }
 }
 
 // Workgroup = 4 waves over 64 query rows (m = t*H + h).  Wave (wi, wj): rows wi*32..+31; scores for KV rows
 // wj*32..+31 of each tile; values for latent columns wj*R/2..+R/2.  Lane l owns row m = tile_row + wi*32 + l%32.
-// Two LDS tiles: while one is computed, the next is gathered by DMA (issued right after the tile barrier).
+// Two LDS tiles: while one is computed, the next is gathered by DMA (spread over the score MFMAs).
 template <int R, int DR>
 __global__ __launch_bounds__(NTHREADS, 1) void splitkv_kernel(
     const uint16_t* __restrict__ q_cat, const uint16_t* __restrict__ c_kv, const uint16_t* __restrict__ k_pe,
     const int32_t* __restrict__ page_table, const uint32_t* __restrict__ mask, int L, int T, int H, int M, int N,
-    int m_tiles, int tiles_per_split, int num_splits, float scale_log2, float* __restrict__ part_o,
+    int m_tiles, int tiles_per_split, int num_splits, float scale_log2, uint16_t* __restrict__ part_o,
     float2* __restrict__ part_ml, int Mp) {
   using TL = TileLayout<R, DR>;
   constexpr int DQ = R + DR, KB = DQ / 16, DB = R / 64;
@@ -404,8 +422,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void splitkv_kernel(
   const int tile_end = min(tile_begin + tiles_per_split, ntiles);
 
   // prologue: gather the first tile while the query fragments load
-  int slot_v = page_table[min(tile_begin * KV_TILE + lane, N - 1)];  // rows past N reuse a real row (masked)
-  dma_tile<R, DR>(kvbuf, c_kv, k_pe, slot_v, wave, lane);
+  TileDma<R, DR> dma(c_kv, k_pe, wave, lane);
+  dma.target(kvbuf, page_table[min(tile_begin * KV_TILE + lane, N - 1)]);  // rows past N reuse a real row (masked)
+#pragma unroll
+  for (int k = 0; k < TileDma<R, DR>::NK; ++k) dma.issue(k);
+  int slot_v = 0;
   if (tile_begin + 1 < tile_end) slot_v = page_table[min((tile_begin + 1) * KV_TILE + lane, N - 1)];
 
   // Padding rows (m >= M) repeat the last real row; their partials are never read.
@@ -435,35 +456,41 @@ __global__ __launch_bounds__(NTHREADS, 1) void splitkv_kernel(
     const int cur = (tile - tile_begin) & 1;
     wait_vmem_all();  // this wave's share of the current tile has landed
     __syncthreads();  // ... and every wave's; the other buffer and the exchange buffers are free
-    if (tile + 1 < tile_end) {
-      dma_tile<R, DR>(kvbuf + (cur ^ 1) * TL::BYTES, c_kv, k_pe, slot_v, wave, lane);
-      if (tile + 2 < tile_end) slot_v = page_table[min((tile + 2) * KV_TILE + lane, N - 1)];
-    }
+    const bool more = tile + 1 < tile_end;
+    dma.target(kvbuf + (cur ^ 1) * TL::BYTES, slot_v);
+    if (tile + 2 < tile_end) slot_v = page_table[min((tile + 2) * KV_TILE + lane, N - 1)];
 #pragma unroll
     for (int db = 0; db < DB; ++db) asm volatile("" : "+v"(o[db]));
     tile_compute<R, DR>(kvbuf + cur * TL::BYTES, q, o, st, tile * KV_TILE, L, N, mw0, mw1, scale_log2, pb_own,
-                        pb_oth, ps_own, ps_oth, mx_own, mx_oth, wj, lane);
+                        pb_oth, ps_own, ps_oth, mx_own, mx_oth, wj, lane, dma, more);
   }
 
   const float l_row = st.l + __shfl_xor(st.l, 32);
-  // Partial O in register-fragment order: [split][m tile][wave][column block][q4][lane] float4, so every store
-  // instruction writes 1 KB contiguously.  (max, sum) per row: [split][row].
-  float4* dst = reinterpret_cast<float4*>(part_o) + ((size_t)(split * m_tiles + mt) * 4 + wave) * DB * 4 * 64 + lane;
+  // Partial in register-fragment order, normalised by its own row sum and rounded to bf16:
+  // [split][m tile][wave][column block][q4][lane] x 4 bf16 (one 512 B contiguous store per instruction).
+  // (max, sum) per row stay fp32: [split][row].
+  const float inv = (l_row > 0.f) ? 1.f / l_row : 0.f;  // a row that saw nothing here has O = 0
+  bf16x4* dst = reinterpret_cast<bf16x4*>(part_o) + ((size_t)(split * m_tiles + mt) * 4 + wave) * DB * 4 * 64 + lane;
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4)
-      dst[(db * 4 + q4) * 64] = make_float4(o[db][q4 * 4 + 0], o[db][q4 * 4 + 1], o[db][q4 * 4 + 2], o[db][q4 * 4 + 3]);
+    for (int q4 = 0; q4 < 4; ++q4) {
+      bf16x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = (__bf16)(o[db][q4 * 4 + e] * inv);
+      dst[(db * 4 + q4) * 64] = v;
+    }
   if (wj == 0 && g == 0) part_ml[(size_t)split * Mp + mt * M_TILE + wi * 32 + c] = make_float2(st.m_ref, l_row);
 }
 
 // ------------------------------------------------------------------------------------------------ combine
-// o_lat[m] = sum_s 2^(m_s - M) O_s[m] / sum_s 2^(m_s - M) l_s,  lse[m] = ln 2 * (M + log2 sum_s 2^(m_s-M) l_s).
+// o_lat[m] = sum_s 2^(m_s - M) O_s[m] / sum_s 2^(m_s - M) l_s,  lse[m] = ln 2 * (M + log2 sum_s 2^(m_s-M) l_s),
+// with O_s stored as O_s / l_s in bf16.
 // A split in which row m saw nothing has m_s = -inf and l_s = 0 and gets weight 0.
-// One workgroup per (query tile, split-KV wave, 32-column block): thread (q4, lane) holds exactly the float4 that
-// lane wrote for fragment q4, so each split contributes one contiguous 4 KB read per workgroup.
+// One workgroup per (query tile, split-KV wave, 32-column block): thread (q4, lane) reads exactly the 4 values that
+// lane wrote for fragment q4, so each split contributes one contiguous 2 KB read per workgroup.
 template <int R>
-__global__ __launch_bounds__(NTHREADS) void combine_kernel(const float* __restrict__ part_o,
+__global__ __launch_bounds__(NTHREADS) void combine_kernel(const uint16_t* __restrict__ part_o,
                                                            const float2* __restrict__ part_ml, int S, int m_tiles,
                                                            int Mp, int M, uint16_t* __restrict__ o_lat,
                                                            float* __restrict__ lse) {
@@ -475,15 +502,15 @@ __global__ __launch_bounds__(NTHREADS) void combine_kernel(const float* __restri
   const int m = mt * M_TILE + wi * 32 + c;
   if (m >= M) return;
   const int d = wj * (R / 2) + db * 32 + q4 * 8 + g * 4;
-  const size_t stride = (size_t)m_tiles * 4 * DB * 4 * 64;  // float4s per split
-  const float4* src = reinterpret_cast<const float4*>(part_o) + ((size_t)mt * 4 + wave) * DB * 4 * 64 + (db * 4 + q4) * 64 + lane;
+  const size_t stride = (size_t)m_tiles * 4 * DB * 4 * 64;  // 4-element groups per split
+  const bf16x4* src = reinterpret_cast<const bf16x4*>(part_o) + ((size_t)mt * 4 + wave) * DB * 4 * 64 + (db * 4 + q4) * 64 + lane;
   // single pass, online merge; a chunk's loads are all issued before any is used
   constexpr int CH = 8;
   float mx = -INFINITY, den = 0.f;
   float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int s0 = 0; s0 < S; s0 += CH) {
     float2 ml[CH];
-    float4 v[CH];
+    bf16x4 v[CH];
 #pragma unroll
     for (int k = 0; k < CH; ++k) {
       const int sk = min(s0 + k, S - 1);
@@ -493,14 +520,15 @@ __global__ __launch_bounds__(NTHREADS) void combine_kernel(const float* __restri
 #pragma unroll
     for (int k = 0; k < CH; ++k) {
       if (s0 + k >= S || ml[k].x == -INFINITY) continue;  // nothing visible in that split
+      // the stored partial is O_s / l_s, so its weight is 2^(m_s - M) * l_s
       const float mn = fmaxf(mx, ml[k].x);
       const float a = fast_exp2(mx - mn);  // mx = -inf -> 0
-      const float w = fast_exp2(ml[k].x - mn);
-      den = den * a + w * ml[k].y;
-      num.x = num.x * a + w * v[k].x;
-      num.y = num.y * a + w * v[k].y;
-      num.z = num.z * a + w * v[k].z;
-      num.w = num.w * a + w * v[k].w;
+      const float w = fast_exp2(ml[k].x - mn) * ml[k].y;
+      den = den * a + w;
+      num.x = num.x * a + w * (float)v[k][0];
+      num.y = num.y * a + w * (float)v[k][1];
+      num.z = num.z * a + w * (float)v[k][2];
+      num.w = num.w * a + w * (float)v[k][3];
       mx = mn;
     }
   }
@@ -615,7 +643,7 @@ static int make_plan(const kdv_mla_dims* d, int T, int L, Plan* p) {
   p->off_olat = off;
   off += align256((size_t)p->M * R * 2);
   p->off_po = off;
-  off += align256((size_t)p->splits * p->Mp * R * 4);
+  off += align256((size_t)p->splits * p->Mp * R * 2);
   p->off_pml = off;
   off += align256((size_t)p->splits * p->Mp * 8);
   p->total = off;
@@ -629,7 +657,7 @@ static void launch_all(const Plan& pl, float sm_scale, const uint16_t* q_nope, c
                        char* ws, hipStream_t st, hipEvent_t const* ev) {
   uint16_t* q_cat = reinterpret_cast<uint16_t*>(ws + pl.off_qcat);
   uint16_t* o_lat = reinterpret_cast<uint16_t*>(ws + pl.off_olat);
-  float* part_o = reinterpret_cast<float*>(ws + pl.off_po);
+  uint16_t* part_o = reinterpret_cast<uint16_t*>(ws + pl.off_po);
   float2* part_ml = reinterpret_cast<float2*>(ws + pl.off_pml);
   if (ev) (void)hipEventRecord(ev[0], st);
   hipLaunchKernelGGL((q_absorb_kernel<DN, R, DR>), dim3(pl.H, (R + 127) / 128), dim3(NTHREADS), 0, st, q_nope,
