@@ -11,8 +11,12 @@ Timing: W eager warm-up steps, then the K timed steps are captured in one HIP gr
 not counted) and replayed once between two device synchronisations, timed with HIP events on the stream the
 kernels run on.  "Cold" rotates the steps over distinct copies of the layer's buffers totalling more than
 512 MiB (twice the 256 MiB Infinity Cache) as a real multi-layer model would; "hot" reuses one copy.
-The split-KV kernel's own time comes from HIP events recorded between the four kernels (eager launches of
-the same steps, queued behind a spin kernel so that no host gap falls between the events).  Work counts are algorithmic: masked tree entries and padding are not counted.
+Each kernel's own time comes from HIP events that the launch itself stamps with the kernel's start and end
+(hipExtLaunchKernelGGL, through kdv_verify_mla_attn_profiled), over eager launches of the same cold steps.
+Work counts are algorithmic: masked tree entries and padding are not counted.
+
+Profile evidence (bash profile_bench.sh) is summarised by `--summarize-profile DIR`; `roofline.traffic`
+is read from the committed counter summary only while its hash of the kernel source matches the source.
 
 Prints ONE JSON line.  Inputs are seeded synthetic data with the shapes of the pages' workloads.
 """
@@ -24,6 +28,9 @@ import json
 import math
 import os
 import sys
+import csv
+import hashlib
+import re
 import time
 
 import numpy as np
@@ -36,6 +43,9 @@ METRIC = "tree-verify MLA attn µs/layer + TFLOP/s (% MFMA peak), 64 heads, 15 n
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, vendor figure
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, vendor figure
 COLD_BYTES = 576 << 20
+KERNEL_SOURCES = ("speculative_decoding_tree_parent_amd/csrc/verify.hip",
+                  "speculative_decoding_tree_parent_amd/csrc/common.h")
+KERNELS = ("tree_mask_kernel", "q_absorb_kernel", "splitkv_kernel", "combine_kernel", "up_proj_kernel")
 
 
 def log(msg):
@@ -145,7 +155,14 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of one HIP graph")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 256 MiB device copy (the reference for FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--summarize-profile", metavar="DIR",
+                    help="print the markdown summaries of a profile_bench.sh run and exit (no GPU needed)")
     args = ap.parse_args()
+    if args.summarize_profile:
+        summarize_profile(args.summarize_profile, args.workload)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -162,6 +179,9 @@ def main():
         raise SystemExit("bench.py needs a GPU (gfx950)")
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        copy_calibration(torch, dev)
+        return
     hip = Hip()
     stream = torch.cuda.Stream(device=dev)      # default priority; graphs cannot capture the null stream
     sh = stream.cuda_stream
@@ -225,37 +245,32 @@ def run(args, torch, si, kdv, dev, hip, stream, sh):
     fixed = dict(pt=table_t.data_ptr(), mask=mask_t.data_ptr(), out=out_t.data_ptr(), lse=lse_t.data_ptr(),
                  ws=ws_t.data_ptr(), parent=parent_t.data_ptr(), status=status_t.data_ptr())
 
-    def step(set_ptrs, ev=None):
+    def step(set_ptrs):
         rc = kdv.kdv_build_tree_mask(fixed["parent"], T, fixed["mask"], fixed["status"], sh)
         if rc:
             raise kdv.KdvError(rc, "kdv_build_tree_mask")
         for lp in set_ptrs:
-            if ev is None:
-                rc = kdv.kdv_verify_mla_attn(dims, *lp, pool_slots, fixed["pt"], L, T, fixed["mask"], fixed["out"],
-                                             fixed["lse"], fixed["ws"], ws_bytes, sh)
-            else:
-                rc = kdv.kdv_verify_mla_attn_profiled(dims, *lp, pool_slots, fixed["pt"], L, T, fixed["mask"],
-                                                      fixed["out"], fixed["lse"], fixed["ws"], ws_bytes, sh,
-                                                      ctypes.addressof(ev))
+            rc = kdv.kdv_verify_mla_attn(dims, *lp, pool_slots, fixed["pt"], L, T, fixed["mask"], fixed["out"],
+                                         fixed["lse"], fixed["ws"], ws_bytes, sh)
             if rc:
                 raise kdv.KdvError(rc, "kdv_verify_mla_attn")
 
-    def run_steps(sets, K, evs=None):
+    def run_steps(sets, K):
         for i in range(K):
-            step(sets[i % len(sets)], None if evs is None else evs[i])
+            step(sets[i % len(sets)])
 
-    def timed(sets, K, evs=None):
+    def timed(sets, K):
         """Device time (ms) of K steps: graph-captured unless --no-graph."""
         e0, e1 = hip.event(), hip.event()
         if args.no_graph:
             torch.cuda.synchronize()
             hip.record(e0, sh)
-            run_steps(sets, K, evs)
+            run_steps(sets, K)
             hip.record(e1, sh)
             return hip.elapsed_ms(e0, e1)
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
-            run_steps(sets, K, evs)
+            run_steps(sets, K)
         g.replay()                       # untimed replay: graph upload, first-touch
         torch.cuda.synchronize()
         hip.record(e0, sh)
@@ -277,12 +292,12 @@ def run(args, torch, si, kdv, dev, hip, stream, sh):
     log(f"[bench] timing {K} steps (hot)")
     ms_hot = timed(hot_ptrs, K)
 
-    # per-kernel split with events between the four kernels of every layer call
+    # per-kernel device time: events stamped by each kernel's own dispatch
     log("[bench] per-kernel timing")
-    EvArr = ctypes.c_void_p * 5
+    EvArr = ctypes.c_void_p * 8
     Kp = min(K, max(1, 400 // layers_per_step))
     n_calls = Kp * layers_per_step
-    ev_list = [EvArr(*[hip.event() for _ in range(5)]) for _ in range(n_calls)]
+    ev_list = [EvArr(*[hip.event() for _ in range(8)]) for _ in range(n_calls)]
     per_step_evs = []
     for i in range(Kp):
         per_step_evs.append(ev_list[i * layers_per_step:(i + 1) * layers_per_step])
@@ -298,10 +313,9 @@ def run(args, torch, si, kdv, dev, hip, stream, sh):
             if rc:
                 raise kdv.KdvError(rc, "kdv_verify_mla_attn_profiled")
 
-    # Eager launches queued behind a spin kernel: the host enqueues every launch while the device is busy, so
-    # the events bracket back-to-back kernels with no host gaps.  (Events recorded inside a captured graph
-    # cannot be timed.)
-    kern_mode = "eager, queued behind a spin kernel"
+    # Eager launches (events stamped inside a captured graph cannot be timed), queued behind a spin kernel so
+    # that the kernels run back to back as in the graph.
+    kern_mode = "eager, kernel-stamped HIP events, queued behind a spin kernel"
     torch.cuda.synchronize()
     torch.cuda._sleep(int(2.4e9 * 0.05))
     for i in range(Kp):
@@ -311,7 +325,7 @@ def run(args, torch, si, kdv, dev, hip, stream, sh):
     tot = {n: 0.0 for n in names}
     for ev in ev_list:
         for k, n in enumerate(names):
-            tot[n] += hip.elapsed_ms(ev[k], ev[k + 1])
+            tot[n] += hip.elapsed_ms(ev[2 * k], ev[2 * k + 1])
     kern_us = {n: 1e3 * tot[n] / n_calls for n in names}
 
     us_layer_cold = 1e3 * ms_cold / (K * layers_per_step)
@@ -344,10 +358,11 @@ def run(args, torch, si, kdv, dev, hip, stream, sh):
                 "frac_bf16_peak": round(tflops_hot / PEAK_BF16_TFLOPS, 4)},
         "kernels_us": {k: round(v, 3) for k, v in kern_us.items()},
         "kernel_timing": kern_mode,
+        "kernel_calls": n_calls,
         "work_per_layer": {"gflop": round(wk["flops"] / 1e9, 4), "mbytes": round(wk["bytes"] / 1e6, 3)},
         "roofline": {"bound": "mfma", "kernel": "splitkv", "achieved": round(sk_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(sk_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None,
+                     "traffic": traffic_from_profile(args.workload),
                      "work_per_launch_gflop": round(wk["flops_splitkv"] / 1e9, 4)},
         "cpu_baseline": None,
     }
@@ -394,6 +409,192 @@ def cpu_baseline(args, inp, wk, layers_per_step):
     return {"value": round(wk1["flops"] / s_per_layer / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle", "sample": f"{sample}; {n} calls in {el:.1f} s",
             "seconds_per_layer": round(s_per_layer, 4), "host_cpus": os.cpu_count()}
+
+
+# ------------------------------------------------------------------------------------------------ profiles
+COPY_BYTES = 256 << 20
+COPY_REPS = 3
+
+
+def copy_calibration(torch, dev):
+    """A plain device-to-device copy of known size: what FETCH_SIZE / WRITE_SIZE read for it gives the
+    factor from counter units to bytes."""
+    a = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(COPY_REPS):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "copies": COPY_REPS}), flush=True)
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_profile_path(workload):
+    return os.path.join(ROOT, "profiles", f"splitkv_{workload}_hbm_traffic.md")
+
+
+def traffic_from_profile(workload):
+    """HBM bytes per split-KV launch from the committed counter summary, or None when there is none or the
+    kernel source has changed since the counters were taken."""
+    path = traffic_profile_path(workload)
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"```json\n(.*?)\n```", open(path).read(), re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("source_sha256") != source_hash():
+        return None
+    return rec["traffic_bytes_per_launch"]
+
+
+def _kernel_key(name):
+    for k in KERNELS:
+        if k in name:
+            return k
+    return None
+
+
+def _read_csv(path):
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _phases(bench, kernel):
+    """Dispatch index ranges of bench.py's phases for one kernel, in launch order."""
+    W, K, lps, n = bench["warmup"], bench["steps"], bench["config"]["layers_per_step"], bench["kernel_calls"]
+    per = 1 if kernel == "tree_mask_kernel" else lps
+    n_eager = n // lps if kernel == "tree_mask_kernel" else n
+    edges = [("warm-up", W * per), ("graph cold, upload replay", K * per), ("graph cold, timed replay", K * per),
+             ("graph hot, upload replay", K * per), ("graph hot, timed replay", K * per),
+             ("eager cold, kernel events", n_eager)]
+    out, a = {}, 0
+    for name, c in edges:
+        out[name] = (a, a + c)
+        a += c
+    return out, a
+
+
+def _counter_per_dispatch(d, counter, kernel_pred):
+    rows = [r for r in _read_csv(os.path.join(d, "run_counter_collection.csv")) if r["Counter_Name"] == counter]
+    by = {}
+    for r in rows:
+        k = kernel_pred(r["Kernel_Name"])
+        if k:
+            by.setdefault(k, []).append((int(r["Dispatch_Id"]), float(r["Counter_Value"])))
+    return {k: [v for _, v in sorted(lst)] for k, lst in by.items()}
+
+
+def summarize_profile(d, workload):
+    """Writes <kernel>_<workload>_kernel_trace.md and splitkv_<workload>_hbm_traffic.md into d/summaries."""
+    cmds = open(os.path.join(d, "commands.txt")).read().strip()
+    out_dir = os.path.join(d, "summaries")
+    os.makedirs(out_dir, exist_ok=True)
+
+    # kernel trace: per-kernel durations by bench phase, next to bench.py's own event timings
+    bench = json.loads(open(os.path.join(d, "trace_bench.json")).read().strip().splitlines()[-1])
+    plain = json.loads(open(os.path.join(d, "plain_bench.json")).read().strip().splitlines()[-1])
+    trace = _read_csv(os.path.join(d, "trace", "run_kernel_trace.csv"))
+    durs = {}
+    for r in trace:
+        k = _kernel_key(r["Kernel_Name"])
+        if k:
+            durs.setdefault(k, []).append((int(r["Dispatch_Id"]), int(r["Start_Timestamp"]),
+                                           int(r["End_Timestamp"])))
+    lines = [f"# Kernel trace: tree-verify MLA attention, workload `{workload}`", "",
+             f"Kernel source sha256 (first 16 hex): `{source_hash()}`", "",
+             "Commands (from the repository root on the GPU machine; `bash profile_bench.sh` runs them):", "",
+             "```", cmds, "```", "",
+             f"bench.py without the tracer: {plain['us_per_layer']} us/layer cold, "
+             f"{plain['hot']['us_per_layer']} us/layer hot, {plain['value']} {plain['unit']}; under the tracer: "
+             f"{bench['us_per_layer']} us/layer cold.", "",
+             "Average kernel duration (us) from rocprofv3 `--kernel-trace`, by phase of the bench run:", ""]
+    kinds = None
+    rows_out = []
+    for k in KERNELS:
+        if k not in durs:
+            continue
+        lst = sorted(durs[k])
+        ph, total = _phases(bench, k)
+        if len(lst) != total:
+            raise SystemExit(f"{k}: {len(lst)} dispatches traced, {total} expected")
+        kinds = list(ph)
+        avg = {}
+        for name, (a, b) in ph.items():
+            seg = lst[a:b]
+            avg[name] = sum(e - s for _, s, e in seg) / len(seg) / 1e3 if seg else float("nan")
+        rows_out.append((k, len(lst), avg))
+    lines.append("| kernel | dispatches | " + " | ".join(kinds) + " | bench.py events, no tracer |")
+    lines.append("|---|---|" + "---|" * (len(kinds) + 1))
+    ev = {f"{k}_kernel": v for k, v in plain["kernels_us"].items()}
+    for k, n, avg in rows_out:
+        lines.append(f"| {k} | {n} | " + " | ".join(f"{avg[p]:.2f}" for p in kinds) +
+                     f" | {ev.get(k, float('nan')):.2f} |")
+    # step span in the timed cold replay (includes gaps between kernels)
+    tm = sorted(durs["tree_mask_kernel"])
+    ph, _ = _phases(bench, "tree_mask_kernel")
+    a, b = ph["graph cold, timed replay"]
+    span = (tm[b - 1][1] - tm[a][1]) / (b - a - 1) / 1e3 if b - a > 1 else float("nan")
+    lines += ["", f"Cold timed replay: one step every {span:.2f} us under the tracer "
+              f"(bench.py without the tracer: {1e3 * plain['ms_per_step']:.2f} us per step).", "",
+              "The last column is bench.py's kernel-stamped HIP events over its eager cold launches, measured "
+              "without the tracer (the tracer lengthens event-bracketed launches); it corresponds to the "
+              "'eager cold' column.", ""]
+    with open(os.path.join(out_dir, f"verify_{workload}_kernel_trace.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+    # HBM traffic of the split-KV kernel: FETCH_SIZE and WRITE_SIZE, scaled by the copy calibration
+    def kp(name):
+        return _kernel_key(name)
+
+    def copy_pred(name):
+        return "copy" if "copyBuffer" in name else None
+    fb = json.loads(open(os.path.join(d, "fetch_bench.json")).read().strip().splitlines()[-1])
+    fetch = _counter_per_dispatch(os.path.join(d, "fetch"), "FETCH_SIZE", kp)
+    write = _counter_per_dispatch(os.path.join(d, "write"), "WRITE_SIZE", kp)
+    cf = _counter_per_dispatch(os.path.join(d, "copy_fetch"), "FETCH_SIZE", copy_pred)["copy"]
+    cw = _counter_per_dispatch(os.path.join(d, "copy_write"), "WRITE_SIZE", copy_pred)["copy"]
+    copy_kib = COPY_BYTES / 1024
+    f_fac = copy_kib / (sum(cf) / len(cf))
+    w_fac = copy_kib / (sum(cw) / len(cw))
+    lines = [f"# HBM traffic per dispatch: tree-verify MLA attention, workload `{workload}`", "",
+             "Commands (from the repository root on the GPU machine; `bash profile_bench.sh` runs them):", "",
+             "```", cmds, "```", "",
+             f"Calibration: a plain {COPY_BYTES >> 20} MiB device copy (`bench.py --copy-calibration`) reads "
+             f"FETCH_SIZE {sum(cf) / len(cf):.0f} KiB and WRITE_SIZE {sum(cw) / len(cw):.0f} KiB per dispatch "
+             f"for {copy_kib:.0f} KiB moved each way: bytes = FETCH_SIZE x {f_fac:.3f} KiB, "
+             f"WRITE_SIZE x {w_fac:.3f} KiB.", "",
+             "Per dispatch, averaged over the eager cold launches of the counted run "
+             f"(`--steps {fb['steps']} --warmup {fb['warmup']}`):", "",
+             "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | fetched MB | written MB |", "|---|---|---|---|---|"]
+    rec = None
+    for k in KERNELS:
+        if k not in fetch or k not in write:
+            continue
+        ph, total = _phases(fb, k)
+        a, b = ph["eager cold, kernel events"]
+        fv, wv = fetch[k][a:b], write[k][a:b]
+        if len(fetch[k]) != total or len(write[k]) != total:
+            raise SystemExit(f"{k}: counter dispatch count mismatch")
+        fk, wk_ = sum(fv) / len(fv), sum(wv) / len(wv)
+        fb_bytes, wb_bytes = fk * f_fac * 1024, wk_ * w_fac * 1024
+        lines.append(f"| {k} | {fk:.1f} | {wk_:.1f} | {fb_bytes / 1e6:.3f} | {wb_bytes / 1e6:.3f} |")
+        if k == "splitkv_kernel":
+            rec = {"kernel": k, "workload": workload, "source_sha256": source_hash(),
+                   "fetch_kib_per_dispatch": round(fk, 2), "write_kib_per_dispatch": round(wk_, 2),
+                   "fetch_factor": round(f_fac, 4), "write_factor": round(w_fac, 4),
+                   "traffic_bytes_per_launch": round(fb_bytes + wb_bytes)}
+    lines += ["", "Record read by bench.py (`roofline.traffic`, used only while the kernel source hash matches):",
+              "", "```json", json.dumps(rec), "```", ""]
+    with open(os.path.join(out_dir, f"splitkv_{workload}_hbm_traffic.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(out_dir)
 
 
 if __name__ == "__main__":

@@ -2,40 +2,41 @@
 //
 // A draft-tree node may attend to the prefix, its ancestors and itself ("The Architecture of
 // Diagnosis...", section "Phase 1: Custom CUDA Kernels", item 2: a visibility mask that reflects the
-// tree structure).  With nodes in topological order (parent[i] < i) the mask of node i is the mask of
-// its parent plus its own bit; each lane here walks its node's parent chain, which is at most T long.
+// tree structure).  Nodes are in topological order (parent[i] < i), so every chain of parents is at
+// most T - 1 <= 63 steps long.  One wave holds one node per lane and builds all rows at once by
+// pointer jumping: after round r a lane holds the bits of the first 2^r nodes of its root path and
+// the node 2^r steps up, so six rounds of cross-lane reads (ds_bpermute) cover any path.
 #include "common.h"
 
 namespace kdv {
 
 __global__ __launch_bounds__(64) void tree_mask_kernel(const int32_t* __restrict__ parent, int T,
                                                        uint32_t* __restrict__ mask, int32_t* __restrict__ status) {
-  __shared__ int any_bad;
-  __shared__ int par[KDV_MAX_TREE_NODES];  // the walk reads parents from LDS: one global load per node
   const int i = threadIdx.x;
-  if (i == 0) any_bad = 0;
-  if (i < T) par[i] = parent[i];
-  __syncthreads();
-  if (i < T) {
-    uint32_t w0 = 0u, w1 = 0u;
-    int j = i;
-    // Walk i -> parent -> ... -> root.  A valid chain strictly decreases, so T steps always suffice.
-    for (int step = 0; step < KDV_MAX_TREE_NODES; ++step) {
-      if (j < 32) w0 |= 1u << j; else w1 |= 1u << (j - 32);
-      const int p = par[j];
-      const bool ok = (j == 0) ? (p == -1) : (p >= 0 && p < j);
-      if (!ok) {
-        if (j == i) atomicOr(&any_bad, 1);   // report each invalid row once, from its own lane
-        break;
-      }
-      if (j == 0) break;
-      j = p;
+  const bool live = i < T;
+  const int p = live ? parent[i] : -1;
+  // A row is valid when the root has no parent and every other node's parent precedes it.  The walk
+  // from an invalid row stops at that row: its mask holds its own bit only.
+  const bool valid = !live || (i == 0 ? p == -1 : (p >= 0 && p < i));
+  int up = (live && valid && i != 0) ? p : -1;  // next node on the path, -1 at its end
+  uint64_t anc = live ? (1ull << i) : 0ull;
+#pragma unroll
+  for (int r = 0; r < 6; ++r) {
+    const int src = up < 0 ? i : up;
+    const uint32_t lo = __shfl((uint32_t)anc, src);
+    const uint32_t hi = __shfl((uint32_t)(anc >> 32), src);
+    const int up2 = __shfl(up, src);
+    if (up >= 0) {
+      anc |= ((uint64_t)hi << 32) | lo;
+      up = up2;
     }
-    const int W = (T + 31) >> 5;
-    mask[i * W] = w0;
-    if (W == 2) mask[i * W + 1] = w1;
   }
-  __syncthreads();
+  if (live) {
+    const int W = (T + 31) >> 5;
+    mask[i * W] = (uint32_t)anc;
+    if (W == 2) mask[i * W + 1] = (uint32_t)(anc >> 32);
+  }
+  const bool any_bad = __any(!valid);
   if (i == 0 && status != nullptr) status[0] = any_bad ? KDV_ERR_TREE : KDV_OK;
 }
 

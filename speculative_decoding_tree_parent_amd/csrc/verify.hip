@@ -13,6 +13,7 @@
 //              with an online softmax; the partial (O, max, sum) of the split goes to the workspace.
 //   combine  : log-sum-exp merge of the splits -> o_lat (bf16) and lse.
 //   up_proj  : out[t,h] = W_UV[h] o_lat[t,h]                              (bf16 MFMA)
+#include <hip/hip_ext.h>
 #include <math.h>
 #include <stdlib.h>
 
@@ -650,6 +651,15 @@ static int make_plan(const kdv_mla_dims* d, int T, int L, Plan* p) {
   return KDV_OK;
 }
 
+// Launch one kernel; with `ev` (start, stop) the events take the kernel's own start and end timestamps.
+template <typename... KArgs, typename... Args>
+static void launch(void (*k)(KArgs...), dim3 grid, hipStream_t st, hipEvent_t const* ev, Args... args) {
+  if (ev)
+    hipExtLaunchKernelGGL(k, grid, dim3(NTHREADS), 0, st, ev[0], ev[1], 0, args...);
+  else
+    hipLaunchKernelGGL(k, grid, dim3(NTHREADS), 0, st, args...);
+}
+
 template <int DN, int R, int DR, int DV>
 static void launch_all(const Plan& pl, float sm_scale, const uint16_t* q_nope, const uint16_t* q_rope,
                        const uint16_t* w_uk, const uint16_t* w_uv, const uint16_t* c_kv, const uint16_t* k_pe,
@@ -659,22 +669,17 @@ static void launch_all(const Plan& pl, float sm_scale, const uint16_t* q_nope, c
   uint16_t* o_lat = reinterpret_cast<uint16_t*>(ws + pl.off_olat);
   uint16_t* part_o = reinterpret_cast<uint16_t*>(ws + pl.off_po);
   float2* part_ml = reinterpret_cast<float2*>(ws + pl.off_pml);
-  if (ev) (void)hipEventRecord(ev[0], st);
-  hipLaunchKernelGGL((q_absorb_kernel<DN, R, DR>), dim3(pl.H, (R + 127) / 128), dim3(NTHREADS), 0, st, q_nope,
-                     q_rope, w_uk, q_cat, T, pl.H);
+  launch(q_absorb_kernel<DN, R, DR>, dim3(pl.H, (R + 127) / 128), st, ev ? ev + 0 : nullptr, q_nope, q_rope, w_uk,
+         q_cat, T, pl.H);
   const float scale_log2 = sm_scale * 1.44269504088896340736f;
-  if (ev) (void)hipEventRecord(ev[1], st);
   const int grid = NUM_XCD * pl.m_tiles * ((pl.splits + NUM_XCD - 1) / NUM_XCD);
-  hipLaunchKernelGGL((splitkv_kernel<R, DR>), dim3(grid), dim3(NTHREADS), 0, st, q_cat, c_kv, k_pe, page_table,
-                     mask, L, T, pl.H, pl.M, pl.N, pl.m_tiles, pl.tiles_per_split, pl.splits, scale_log2, part_o,
-                     part_ml, pl.Mp);
-  if (ev) (void)hipEventRecord(ev[2], st);
-  hipLaunchKernelGGL((combine_kernel<R>), dim3(pl.m_tiles * 4 * (R / 64)), dim3(NTHREADS), 0, st, part_o, part_ml,
-                     pl.splits, pl.m_tiles, pl.Mp, pl.M, o_lat, lse);
-  if (ev) (void)hipEventRecord(ev[3], st);
-  hipLaunchKernelGGL((up_proj_kernel<R, DV>), dim3(pl.H, DV / 32), dim3(NTHREADS), 0, st, o_lat, w_uv, out, T,
-                     pl.H);
-  if (ev) (void)hipEventRecord(ev[4], st);
+  launch(splitkv_kernel<R, DR>, dim3(grid), st, ev ? ev + 2 : nullptr, (const uint16_t*)q_cat, c_kv, k_pe,
+         page_table, mask, L, T, pl.H, pl.M, pl.N, pl.m_tiles, pl.tiles_per_split, pl.splits, scale_log2, part_o,
+         part_ml, pl.Mp);
+  launch(combine_kernel<R>, dim3(pl.m_tiles * 4 * (R / 64)), st, ev ? ev + 4 : nullptr, (const uint16_t*)part_o,
+         (const float2*)part_ml, pl.splits, pl.m_tiles, pl.Mp, pl.M, o_lat, lse);
+  launch(up_proj_kernel<R, DV>, dim3(pl.H, DV / 32), st, ev ? ev + 6 : nullptr, (const uint16_t*)o_lat, w_uv, out,
+         T, pl.H);
 }
 
 static bool misaligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
