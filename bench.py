@@ -5,7 +5,7 @@
 
 A step is one pass of the whole hot path over one batch of synthetic input: the ancestor mask of the draft
 tree (kdv_build_tree_mask) and tree-verify attention for one layer (kdv_verify_mla_attn: q absorption,
-split-KV MFMA pass, split combine, W_UV up-projection); for `full61` a step is one mask and 61 layers.
+split-KV MFMA pass, split combine fused with the W_UV up-projection); for `full61` a step is one mask and 61 layers.
 
 Timing: W eager warm-up steps, then the K timed steps are captured in one HIP graph (so host launch cost is
 not counted) and replayed once between two device synchronisations, timed with HIP events on the stream the
@@ -45,7 +45,7 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, vendor figure
 COLD_BYTES = 576 << 20
 KERNEL_SOURCES = ("speculative_decoding_tree_parent_amd/csrc/verify.hip",
                   "speculative_decoding_tree_parent_amd/csrc/common.h")
-KERNELS = ("tree_mask_kernel", "q_absorb_kernel", "splitkv_kernel", "combine_kernel", "up_proj_kernel")
+KERNELS = ("tree_mask_kernel", "q_absorb_kernel", "splitkv_kernel", "combine_up_kernel")
 
 
 def log(msg):
@@ -294,10 +294,10 @@ def run(args, torch, si, kdv, dev, hip, stream, sh):
 
     # per-kernel device time: events stamped by each kernel's own dispatch
     log("[bench] per-kernel timing")
-    EvArr = ctypes.c_void_p * 8
+    EvArr = ctypes.c_void_p * 6
     Kp = min(K, max(1, 400 // layers_per_step))
     n_calls = Kp * layers_per_step
-    ev_list = [EvArr(*[hip.event() for _ in range(8)]) for _ in range(n_calls)]
+    ev_list = [EvArr(*[hip.event() for _ in range(6)]) for _ in range(n_calls)]
     per_step_evs = []
     for i in range(Kp):
         per_step_evs.append(ev_list[i * layers_per_step:(i + 1) * layers_per_step])
@@ -321,7 +321,7 @@ def run(args, torch, si, kdv, dev, hip, stream, sh):
     for i in range(Kp):
         step_ev(cold_ptrs[i % len(cold_ptrs)], per_step_evs[i])
     torch.cuda.synchronize()
-    names = ["q_absorb", "splitkv", "combine", "up_proj"]
+    names = ["q_absorb", "splitkv", "combine_up"]
     tot = {n: 0.0 for n in names}
     for ev in ev_list:
         for k, n in enumerate(names):

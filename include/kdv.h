@@ -114,10 +114,10 @@ int kdv_verify_mla_attn(const kdv_mla_dims* d, const uint16_t* q_nope, const uin
                         int64_t pool_slots, const int32_t* page_table, int32_t L, int32_t T, const uint32_t* mask,
                         uint16_t* out, float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Same computation as kdv_verify_mla_attn, for measurement: `events` points to eight hipEvent_t created by the
+/* Same computation as kdv_verify_mla_attn, for measurement: `events` points to six hipEvent_t created by the
  * caller.  events[2k] and events[2k+1] receive the start and end timestamps of kernel k as the hardware dispatches
- * it (k = 0 q absorption, 1 split-KV pass, 2 split combine, 3 W_UV up-projection), so hipEventElapsedTime gives
- * each kernel's device time.  Errors as kdv_verify_mla_attn, plus KDV_ERR_NULL if events is NULL. */
+ * it (k = 0 q absorption, 1 split-KV pass, 2 split combine with the W_UV up-projection), so hipEventElapsedTime
+ * gives each kernel's device time.  Errors as kdv_verify_mla_attn, plus KDV_ERR_NULL if events is NULL. */
 int kdv_verify_mla_attn_profiled(const kdv_mla_dims* d, const uint16_t* q_nope, const uint16_t* q_rope,
                                  const uint16_t* w_uk, const uint16_t* w_uv, const uint16_t* c_kv,
                                  const uint16_t* k_pe, int64_t pool_slots, const int32_t* page_table, int32_t L,

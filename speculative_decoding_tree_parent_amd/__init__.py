@@ -91,7 +91,7 @@ def kdv_verify_mla_attn_profiled(dims: KdvMlaDims, q_nope: int, q_rope: int, w_u
                                  k_pe: int, pool_slots: int, page_table: int, L: int, T: int, mask: int, out: int,
                                  lse: int | None, workspace: int, workspace_bytes: int, stream: int | None,
                                  events: int) -> int:
-    """`events`: address of eight hipEvent_t handles: start/stop of each of the four kernels (include/kdv.h)."""
+    """`events`: address of six hipEvent_t handles: start/stop of each of the three kernels (include/kdv.h)."""
     return _lib.kdv_verify_mla_attn_profiled(ctypes.byref(dims), q_nope, q_rope, w_uk, w_uv, c_kv, k_pe, pool_slots,
                                              page_table, L, T, mask, out, lse, workspace, workspace_bytes, stream,
                                              events)

@@ -6,13 +6,13 @@
 // Deployment...", section "The Second Thread: Pivoting to 200k Context", addressed one token per page
 // ("The Architecture of Diagnosis...", section "The Discrepancy That Revealed the Truth").
 //
-// Four kernels, enqueued in order on the caller's stream:
+// Three kernels, enqueued in order on the caller's stream:
 //   q_absorb : q_cat[m] = [W_UK[h]^T q_nope[t,h] ; q_rope[t,h]]          (m = t*H + h; bf16 MFMA)
 //   splitkv  : one workgroup per (64 query rows, KV split).  KV tiles of 64 paged rows are gathered into
 //              LDS by DMA one tile ahead; scores S^T = K Q^T and O^T += V^T P^T run on 32x32x16 bf16 MFMA
 //              with an online softmax; the partial (O, max, sum) of the split goes to the workspace.
-//   combine  : log-sum-exp merge of the splits -> o_lat (bf16) and lse.
-//   up_proj  : out[t,h] = W_UV[h] o_lat[t,h]                              (bf16 MFMA)
+//   combine_up : log-sum-exp merge of the splits -> lse and the latent output o[t,h] (bf16, in LDS), then
+//              out[t,h] = W_UV[h] o[t,h]                                   (bf16 MFMA)
 #include <hip/hip_ext.h>
 #include <math.h>
 #include <stdlib.h>
@@ -52,12 +52,24 @@ __global__ __launch_bounds__(NTHREADS) void q_absorb_kernel(const uint16_t* __re
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, c = lane & 31;
 
+  // W_UK[h][:, r0:r0+RB] -> LDS: every load of a thread is issued before the first LDS write, so the
+  // workgroup waits for one memory round trip, not one per load
+  constexpr int WLOADS = DN * (RB / 8) / NTHREADS;
+  static_assert(DN * (RB / 8) % NTHREADS == 0, "W_UK slice must split evenly over the threads");
   const uint16_t* wh = w_uk + (size_t)h * DN * R;
-  for (int ci = tid; ci < DN * (RB / 8); ci += NTHREADS) {
+  uint4 wv[WLOADS];
+#pragma unroll
+  for (int u = 0; u < WLOADS; ++u) {
+    const int ci = tid + u * NTHREADS;
     const int k = ci / (RB / 8), col = (ci % (RB / 8)) * 8;
-    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (r0 + col < R) v = *reinterpret_cast<const uint4*>(wh + (size_t)k * R + r0 + col);
-    *reinterpret_cast<uint4*>(&w_s[k * WP + col]) = v;
+    wv[u] = (r0 + col < R) ? *reinterpret_cast<const uint4*>(wh + (size_t)k * R + r0 + col) : make_uint4(0u, 0u, 0u, 0u);
+  }
+  // query fragments of the first 32 nodes; rows past T load node T-1 (their results are never stored)
+  bf16x8 qb[DN / 16];
+  {
+    const int tq = min(c, T - 1);
+#pragma unroll
+    for (int kb = 0; kb < DN / 16; ++kb) qb[kb] = load_bf16x8(q_nope + ((size_t)tq * H + h) * DN + kb * 16 + g * 8);
   }
   if (blockIdx.y == 0) {
     for (int ci = tid; ci < T * (DR / 8); ci += NTHREADS) {
@@ -66,11 +78,12 @@ __global__ __launch_bounds__(NTHREADS) void q_absorb_kernel(const uint16_t* __re
           *reinterpret_cast<const uint4*>(q_rope + ((size_t)t * H + h) * DR + col);
     }
   }
-  // the first 32 nodes' query fragments are requested before the barrier, overlapping the W_UK staging
-  bf16x8 qb[DN / 16];
 #pragma unroll
-  for (int kb = 0; kb < DN / 16; ++kb)
-    qb[kb] = (c < T) ? load_bf16x8(q_nope + ((size_t)c * H + h) * DN + kb * 16 + g * 8) : zero_bf16x8();
+  for (int u = 0; u < WLOADS; ++u) {
+    const int ci = tid + u * NTHREADS;
+    const int k = ci / (RB / 8), col = (ci % (RB / 8)) * 8;
+    *reinterpret_cast<uint4*>(&w_s[k * WP + col]) = wv[u];
+  }
   __syncthreads();
   const int rs = wave * 32;
   if (r0 + rs >= R) return;  // wave-uniform; no barrier follows
@@ -82,8 +95,7 @@ __global__ __launch_bounds__(NTHREADS) void q_absorb_kernel(const uint16_t* __re
       const int krow = kb * 16 + g * 8 + ((lane & 15) >> 2);
       const int col = rs + ((lane & 31) >> 4) * 16 + 4 * (lane & 3);
       const bf16x8 a = concat_tr(lds_read_tr16(&w_s[krow * WP + col]), lds_read_tr16(&w_s[(krow + 4) * WP + col]));
-      const bf16x8 b = (tb == 0) ? qb[kb]
-                     : (t < T) ? load_bf16x8(q_nope + ((size_t)t * H + h) * DN + kb * 16 + g * 8) : zero_bf16x8();
+      const bf16x8 b = (tb == 0) ? qb[kb] : load_bf16x8(q_nope + ((size_t)min(t, T - 1) * H + h) * DN + kb * 16 + g * 8);
       acc = mfma32(a, b, acc);
     }
     if (t < T) {
@@ -115,6 +127,13 @@ template <int C>  // C = 16-byte chunks per row
 __device__ __forceinline__ int swz(int row) {
   if constexpr (C >= 16) return ((row & 3) << 2) | ((row >> 2) & 3);
   else return (row >> (C == 8 ? 1 : C == 4 ? 2 : 3)) & (C - 1);
+}
+
+// Query-tile staging swizzle (rows of QC 16-byte chunks): XOR within aligned groups of 8 chunks.
+template <int QC>
+__device__ __forceinline__ int qswz(int row, int ch) {
+  if constexpr (QC % 8 == 0) return (ch & ~7) | ((ch ^ (row >> 1)) & 7);
+  else return ch;
 }
 
 template <int R, int DR>
@@ -422,26 +441,55 @@ __global__ __launch_bounds__(NTHREADS, 1) void splitkv_kernel(
   const int tile_begin = split * tiles_per_split;
   const int tile_end = min(tile_begin + tiles_per_split, ntiles);
 
-  // prologue: gather the first tile while the query fragments load
+  // Prologue.  The query tile (64 rows of q_cat) is gathered once per workgroup by DMA into the second KV
+  // buffer, which is idle until the loop's first iteration, while the first tile's page-table slice and the
+  // mask words load; the first tile's gather follows the page-table slice.  Each wave then reads its query
+  // fragments from LDS.  (Each DMA asm clobbers memory, so no load is moved past it.)
+  // Padding rows (m >= M) repeat the last real row; their partials are never read.
+  const int me = min(m, M - 1);
+  const int slot0 = page_table[min(tile_begin * KV_TILE + lane, N - 1)];  // rows past N reuse a real row (masked)
+  const int t_row = me / H, W = (T + 31) >> 5;
+  const uint32_t mw0 = mask[t_row * W];
+  const uint32_t mw1 = (W == 2) ? mask[t_row * W + 1] : 0u;
+  char* qbuf = kvbuf + TL::BYTES;
+  {
+    // LDS holds the tile's rows back to back, DQ/8 chunks each; within aligned groups of 8 chunks, chunk ch of
+    // row r sits at position ch ^ ((r >> 1) & 7), so the 16 rows a quarter-wave reads at one chunk fall in 16
+    // distinct 16-byte bank groups (an involution: the same formula maps a position back to its chunk).
+    // Lane l of DMA instruction i fills position i*64 + l.
+    constexpr int QC = DQ / 8, QN = (M_TILE * QC + 255) / 256;
+    static_assert(M_TILE * QC * 16 <= TL::BYTES, "query tile must fit in one KV buffer");
+    const uint32_t qlds = lds_address(qbuf);
+#pragma unroll
+    for (int k = 0; k < QN; ++k) {
+      const int ins = wave + 4 * k, pos = ins * 64 + lane;
+      if (ins * 64 < M_TILE * QC) {
+        const int r = pos / QC, ch = qswz<QC>(r, pos % QC);
+        const int gr = min(mt * M_TILE + r, M - 1);
+        dma16_lane_addr(q_cat + (size_t)gr * DQ + ch * 8, qlds + ins * 1024);
+      }
+    }
+  }
   TileDma<R, DR> dma(c_kv, k_pe, wave, lane);
-  dma.target(kvbuf, page_table[min(tile_begin * KV_TILE + lane, N - 1)]);  // rows past N reuse a real row (masked)
+  dma.target(kvbuf, slot0);
 #pragma unroll
   for (int k = 0; k < TileDma<R, DR>::NK; ++k) dma.issue(k);
   int slot_v = 0;
   if (tile_begin + 1 < tile_end) slot_v = page_table[min((tile_begin + 1) * KV_TILE + lane, N - 1)];
-
-  // Padding rows (m >= M) repeat the last real row; their partials are never read.
-  const int me = min(m, M - 1);
+  wait_vmem_all();
+  __syncthreads();
   bf16x8 q[KB];
+  {
+    constexpr int QC = DQ / 8;
+    const int r = wi * 32 + c;
+    const char* qrow = qbuf + r * QC * 16;
 #pragma unroll
-  for (int kb = 0; kb < KB; ++kb) q[kb] = load_bf16x8(q_cat + (size_t)me * DQ + kb * 16 + g * 8);
+    for (int kb = 0; kb < KB; ++kb) q[kb] = *reinterpret_cast<const bf16x8*>(qrow + qswz<QC>(r, 2 * kb + g) * 16);
+  }
   // Register classes: the query fragments (MFMA B operands) live in AGPRs and the O accumulators in VGPRs
   // (MFMA's VGPR form, selected at build time), so the softmax rescale of O needs no AGPR<->VGPR copies.
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) asm volatile("" : "+a"(q[kb]));
-  const int t_row = me / H, W = (T + 31) >> 5;
-  const uint32_t mw0 = mask[t_row * W];
-  const uint32_t mw1 = (W == 2) ? mask[t_row * W + 1] : 0u;
   f32x16 o[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = zero16();
@@ -467,129 +515,151 @@ __global__ __launch_bounds__(NTHREADS, 1) void splitkv_kernel(
   }
 
   const float l_row = st.l + __shfl_xor(st.l, 32);
-  // Partial in register-fragment order, normalised by its own row sum and rounded to bf16:
-  // [split][m tile][wave][column block][q4][lane] x 4 bf16 (one 512 B contiguous store per instruction).
-  // (max, sum) per row stay fp32: [split][row].
+  // Partial of this split: O / l rounded to bf16, row-major [split][row][R] so that a row is one contiguous
+  // 1 KB line for the combine, plus fp32 (max, sum) per row, [split][row].  The register fragments go to
+  // LDS first (the KV buffers are free once every wave has left the loop), then out as whole rows.
   const float inv = (l_row > 0.f) ? 1.f / l_row : 0.f;  // a row that saw nothing here has O = 0
-  bf16x4* dst = reinterpret_cast<bf16x4*>(part_o) + ((size_t)(split * m_tiles + mt) * 4 + wave) * DB * 4 * 64 + lane;
+  constexpr int OP = R + 8;  // staging pitch (elements): rows 16 B apart in the bank space
+  static_assert(M_TILE * OP * 2 <= 2 * TL::BYTES, "O staging must fit in the KV buffers");
+  uint16_t* o_s = reinterpret_cast<uint16_t*>(kvbuf);
+  __syncthreads();
+  {
+    // lane (c, g) of wave (wi, wj) holds row wi*32 + c, columns wj*R/2 + db*32 + q4*8 + g*4 + 0..3
+    uint16_t* row_s = o_s + (wi * 32 + c) * OP + wj * (R / 2) + g * 4;
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      bf16x4 v;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = (__bf16)(o[db][q4 * 4 + e] * inv);
-      dst[(db * 4 + q4) * 64] = v;
-    }
-  if (wj == 0 && g == 0) part_ml[(size_t)split * Mp + mt * M_TILE + wi * 32 + c] = make_float2(st.m_ref, l_row);
-}
-
-// ------------------------------------------------------------------------------------------------ combine
-// o_lat[m] = sum_s 2^(m_s - M) O_s[m] / sum_s 2^(m_s - M) l_s,  lse[m] = ln 2 * (M + log2 sum_s 2^(m_s-M) l_s),
-// with O_s stored as O_s / l_s in bf16.
-// A split in which row m saw nothing has m_s = -inf and l_s = 0 and gets weight 0.
-// One workgroup per (query tile, split-KV wave, 32-column block): thread (q4, lane) reads exactly the 4 values that
-// lane wrote for fragment q4, so each split contributes one contiguous 2 KB read per workgroup.
-template <int R>
-__global__ __launch_bounds__(NTHREADS) void combine_kernel(const uint16_t* __restrict__ part_o,
-                                                           const float2* __restrict__ part_ml, int S, int m_tiles,
-                                                           int Mp, int M, uint16_t* __restrict__ o_lat,
-                                                           float* __restrict__ lse) {
-  constexpr int DB = R / 64;
-  const int blk = blockIdx.x;
-  const int db = blk % DB, wave = (blk / DB) % 4, mt = blk / (DB * 4);
-  const int q4 = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wi = wave >> 1, wj = wave & 1, g = lane >> 5, c = lane & 31;
-  const int m = mt * M_TILE + wi * 32 + c;
-  if (m >= M) return;
-  const int d = wj * (R / 2) + db * 32 + q4 * 8 + g * 4;
-  const size_t stride = (size_t)m_tiles * 4 * DB * 4 * 64;  // 4-element groups per split
-  const bf16x4* src = reinterpret_cast<const bf16x4*>(part_o) + ((size_t)mt * 4 + wave) * DB * 4 * 64 + (db * 4 + q4) * 64 + lane;
-  // single pass, online merge; a chunk's loads are all issued before any is used
-  constexpr int CH = 8;
-  float mx = -INFINITY, den = 0.f;
-  float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s0 = 0; s0 < S; s0 += CH) {
-    float2 ml[CH];
-    bf16x4 v[CH];
-#pragma unroll
-    for (int k = 0; k < CH; ++k) {
-      const int sk = min(s0 + k, S - 1);
-      ml[k] = part_ml[(size_t)sk * Mp + m];
-      v[k] = src[sk * stride];
-    }
-#pragma unroll
-    for (int k = 0; k < CH; ++k) {
-      if (s0 + k >= S || ml[k].x == -INFINITY) continue;  // nothing visible in that split
-      // the stored partial is O_s / l_s, so its weight is 2^(m_s - M) * l_s
-      const float mn = fmaxf(mx, ml[k].x);
-      const float a = fast_exp2(mx - mn);  // mx = -inf -> 0
-      const float w = fast_exp2(ml[k].x - mn) * ml[k].y;
-      den = den * a + w;
-      num.x = num.x * a + w * (float)v[k][0];
-      num.y = num.y * a + w * (float)v[k][1];
-      num.z = num.z * a + w * (float)v[k][2];
-      num.w = num.w * a + w * (float)v[k][3];
-      mx = mn;
-    }
-  }
-  const float inv = 1.f / den;
-  bf16x4 ov;
-  ov[0] = (__bf16)(num.x * inv);
-  ov[1] = (__bf16)(num.y * inv);
-  ov[2] = (__bf16)(num.z * inv);
-  ov[3] = (__bf16)(num.w * inv);
-  *reinterpret_cast<bf16x4*>(o_lat + (size_t)m * R + d) = ov;
-  if (lse != nullptr && d == 0) lse[m] = (mx + log2f(den)) * 0.69314718055994530942f;
-}
-
-// ------------------------------------------------------------------------------------------------ up_proj
-// grid (H, DV/32); the four waves split the R-deep contraction and reduce through LDS.
-// MFMA D[v][t] = sum_r W_UV[h][v][r] o_lat[t,h][r]: both operands are r-contiguous in memory.
-template <int R, int DV>
-__global__ __launch_bounds__(NTHREADS) void up_proj_kernel(const uint16_t* __restrict__ o_lat,
-                                                           const uint16_t* __restrict__ w_uv,
-                                                           uint16_t* __restrict__ out, int T, int H) {
-  constexpr int KBW = R / 16 / 4;  // k-blocks per wave
-  __shared__ float red[4][16][64];
-  const int h = blockIdx.x, v0 = blockIdx.y * 32;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 5, c = lane & 31;
-  const uint16_t* wrow = w_uv + ((size_t)h * DV + v0 + c) * R + wave * KBW * 16 + g * 8;
-  bf16x8 a[KBW];
-#pragma unroll
-  for (int kk = 0; kk < KBW; ++kk) a[kk] = load_bf16x8(wrow + kk * 16);
-  for (int tb = 0; tb < T; tb += 32) {
-    const int t = tb + c;
-    f32x16 acc = zero16();
-    const uint16_t* orow = o_lat + ((size_t)t * H + h) * R + wave * KBW * 16 + g * 8;
-#pragma unroll
-    for (int kk = 0; kk < KBW; ++kk)
-      acc = mfma32(a[kk], (t < T) ? load_bf16x8(orow + kk * 16) : zero_bf16x8(), acc);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) red[wave][r][lane] = acc[r];
-    __syncthreads();
-    if (wave == 0 && t < T) {
-      uint16_t* dst = out + ((size_t)t * H + h) * DV + v0 + g * 4;
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         bf16x4 v;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = q4 * 4 + e;
-          v[e] = (__bf16)(red[0][r][lane] + red[1][r][lane] + red[2][r][lane] + red[3][r][lane]);
-        }
-        *reinterpret_cast<bf16x4*>(dst + q4 * 8) = v;
+        for (int e = 0; e < 4; ++e) v[e] = (__bf16)(o[db][q4 * 4 + e] * inv);
+        *reinterpret_cast<bf16x4*>(row_s + db * 32 + q4 * 8) = v;
       }
+  }
+  if (wj == 0 && g == 0) part_ml[(size_t)split * Mp + mt * M_TILE + wi * 32 + c] = make_float2(st.m_ref, l_row);
+  __syncthreads();
+  uint16_t* dst = part_o + ((size_t)split * Mp + mt * M_TILE) * R;
+  constexpr int CPR = R / 8;  // 16-byte chunks per row
+#pragma unroll 4
+  for (int idx = tid; idx < M_TILE * CPR; idx += NTHREADS) {
+    const int row = idx / CPR, ch = idx % CPR;
+    *reinterpret_cast<uint4*>(dst + (size_t)row * R + ch * 8) = *reinterpret_cast<const uint4*>(o_s + row * OP + ch * 8);
+  }
+}
+
+// ------------------------------------------------------------------------------------------------ combine + W_UV
+// Merging the splits: o[m] = sum_s 2^(m_s - M) O_s[m] / sum_s 2^(m_s - M) l_s and
+// lse[m] = ln 2 * (M + log2 sum_s 2^(m_s - M) l_s), M = max_s m_s, with O_s stored as O_s / l_s in bf16
+// (so its weight is 2^(m_s - M) l_s); a split in which row m saw nothing has m_s = -inf, l_s = 0, weight 0.
+// The merged latent row, rounded to bf16, goes through the value up-projection right away:
+// out[t,h][v] = sum_r W_UV[h][v][r] o[t,h][r].
+//
+// One workgroup per (head, block of RT nodes).  Workgroups are dealt to the XCDs round-robin, and the node
+// blocks of one head are kept on one XCD, so W_UV[h] is fetched into that XCD's L2 once.  The first 16
+// splits' partials and each wave's 32 rows of W_UV are requested together; the workgroup merges its RT
+// latent rows (one thread per 16-byte chunk of a row) while W_UV is still arriving.  MFMA D[v][t] = sum_r W_UV[h][v][r] o[t][r] then reads W from registers and o
+// from LDS, both r-contiguous; columns t >= RT of the product repeat the last row and are never stored.
+template <int R, int DV>
+__global__ __launch_bounds__(NTHREADS) void combine_up_kernel(const uint16_t* __restrict__ part_o,
+                                                              const float2* __restrict__ part_ml, int S, int Mp,
+                                                              int T, int H, const uint16_t* __restrict__ w_uv,
+                                                              uint16_t* __restrict__ out, float* __restrict__ lse) {
+  constexpr int RT = 4;            // tree nodes per workgroup
+  constexpr int CPR = R / 8;       // 16-byte chunks per latent row
+  constexpr int KS = R / 16;       // MFMA k-steps
+  constexpr int OP = R + 8;        // LDS pitch of a merged row (elements)
+  constexpr int CH = 16;           // splits whose loads are in flight together
+  static_assert(RT * CPR <= NTHREADS, "one thread per chunk of each row");
+  static_assert(DV % 32 == 0 && DV / 32 <= NTHREADS / 64, "one wave per 32 output columns");
+  __shared__ __attribute__((aligned(16))) uint16_t o_s[RT * OP];
+  const int xcd = blockIdx.x % NUM_XCD, j = blockIdx.x / NUM_XCD;
+  const int TB = (T + RT - 1) / RT;
+  const int h = xcd + NUM_XCD * (j / TB), t0 = (j % TB) * RT;
+  if (h >= H) return;  // padding block (uniform; before any barrier)
+  const int nrow = min(RT, T - t0);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, c = lane & 31;
+  const bool up_wave = wave * 32 < DV;
+
+  const int i = tid / CPR, k = tid % CPR;
+  const bool merge_thread = i < RT;
+  const int t = t0 + min(i, nrow - 1);  // rows past the last node repeat it (never stored)
+  const int m = t * H + h;
+  const bf16x8* src = reinterpret_cast<const bf16x8*>(part_o + (size_t)m * R) + k;
+  const size_t stride = (size_t)Mp * CPR;  // bf16x8 per split
+  float2 ml[CH];
+  bf16x8 v[CH];
+  auto load_chunk = [&](int s0) {
+#pragma unroll
+    for (int q = 0; q < CH; ++q) {
+      const int sq = min(s0 + q, S - 1);
+      ml[q] = part_ml[(size_t)sq * Mp + m];
+      v[q] = src[sq * stride];
     }
-    __syncthreads();
+  };
+  float mx = -INFINITY, den = 0.f;
+  float num[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  auto merge_chunk = [&](int s0) {
+#pragma unroll
+    for (int q = 0; q < CH; ++q) {
+      if (s0 + q >= S || ml[q].x == -INFINITY) continue;  // nothing visible in that split
+      const float mn = fmaxf(mx, ml[q].x);
+      const float a = fast_exp2(mx - mn);  // mx = -inf -> 0
+      const float wgt = fast_exp2(ml[q].x - mn) * ml[q].y;
+      den = den * a + wgt;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) num[e] = num[e] * a + wgt * (float)v[q][e];
+      mx = mn;
+    }
+  };
+  // the first chunk of partials, then this wave's rows of W_UV: one memory round trip for both
+  if (merge_thread) load_chunk(0);
+  bf16x8 w[KS];
+  if (up_wave) {
+    const uint16_t* wrow = w_uv + ((size_t)h * DV + wave * 32 + c) * R + g * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) w[ks] = load_bf16x8(wrow + ks * 16);
+  }
+  if (merge_thread) {
+    merge_chunk(0);
+    for (int s0 = CH; s0 < S; s0 += CH) {
+      load_chunk(s0);
+      merge_chunk(s0);
+    }
+    const float inv = 1.f / den;
+    bf16x8 ov;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ov[e] = (__bf16)(num[e] * inv);
+    *reinterpret_cast<bf16x8*>(&o_s[i * OP + k * 8]) = ov;
+    if (lse != nullptr && k == 0 && i < nrow) lse[m] = (mx + log2f(den)) * 0.69314718055994530942f;
+  }
+  __syncthreads();
+  if (!up_wave) return;  // wave-uniform; no barrier follows
+
+  // two independent accumulation chains (even / odd k-steps)
+  f32x16 acc0 = zero16(), acc1 = zero16();
+  const uint16_t* orow = o_s + min(c, RT - 1) * OP + g * 8;
+#pragma unroll
+  for (int ks = 0; ks < KS; ks += 2) {
+    acc0 = mfma32(w[ks], *reinterpret_cast<const bf16x8*>(orow + ks * 16), acc0);
+    acc1 = mfma32(w[ks + 1], *reinterpret_cast<const bf16x8*>(orow + (ks + 1) * 16), acc1);
+  }
+  if (c < nrow) {
+    uint16_t* dst = out + ((size_t)(t0 + c) * H + h) * DV + wave * 32 + g * 4;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      bf16x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc0[q4 * 4 + e] + acc1[q4 * 4 + e]);
+      *reinterpret_cast<bf16x4*>(dst + q4 * 8) = v;
+    }
   }
 }
 
 // ------------------------------------------------------------------------------------------------ host side
 struct Plan {
   int H, M, Mp, m_tiles, N, ntiles, tiles_per_split, splits;
-  size_t off_qcat, off_olat, off_po, off_pml, total;
+  size_t off_qcat, off_po, off_pml, total;
 };
 
 enum ShapeId { SHAPE_NONE = 0, SHAPE_KIMI = 1, SHAPE_TINY = 2 };
@@ -641,8 +711,6 @@ static int make_plan(const kdv_mla_dims* d, int T, int L, Plan* p) {
   size_t off = 0;
   p->off_qcat = off;
   off += align256((size_t)p->M * DQ * 2);
-  p->off_olat = off;
-  off += align256((size_t)p->M * R * 2);
   p->off_po = off;
   off += align256((size_t)p->splits * p->Mp * R * 2);
   p->off_pml = off;
@@ -666,7 +734,6 @@ static void launch_all(const Plan& pl, float sm_scale, const uint16_t* q_nope, c
                        const int32_t* page_table, int L, int T, const uint32_t* mask, uint16_t* out, float* lse,
                        char* ws, hipStream_t st, hipEvent_t const* ev) {
   uint16_t* q_cat = reinterpret_cast<uint16_t*>(ws + pl.off_qcat);
-  uint16_t* o_lat = reinterpret_cast<uint16_t*>(ws + pl.off_olat);
   uint16_t* part_o = reinterpret_cast<uint16_t*>(ws + pl.off_po);
   float2* part_ml = reinterpret_cast<float2*>(ws + pl.off_pml);
   launch(q_absorb_kernel<DN, R, DR>, dim3(pl.H, (R + 127) / 128), st, ev ? ev + 0 : nullptr, q_nope, q_rope, w_uk,
@@ -676,10 +743,9 @@ static void launch_all(const Plan& pl, float sm_scale, const uint16_t* q_nope, c
   launch(splitkv_kernel<R, DR>, dim3(grid), st, ev ? ev + 2 : nullptr, (const uint16_t*)q_cat, c_kv, k_pe,
          page_table, mask, L, T, pl.H, pl.M, pl.N, pl.m_tiles, pl.tiles_per_split, pl.splits, scale_log2, part_o,
          part_ml, pl.Mp);
-  launch(combine_kernel<R>, dim3(pl.m_tiles * 4 * (R / 64)), st, ev ? ev + 4 : nullptr, (const uint16_t*)part_o,
-         (const float2*)part_ml, pl.splits, pl.m_tiles, pl.Mp, pl.M, o_lat, lse);
-  launch(up_proj_kernel<R, DV>, dim3(pl.H, DV / 32), st, ev ? ev + 6 : nullptr, (const uint16_t*)o_lat, w_uv, out,
-         T, pl.H);
+  const int cgrid = NUM_XCD * ((pl.H + NUM_XCD - 1) / NUM_XCD) * ((T + 3) / 4);
+  launch(combine_up_kernel<R, DV>, dim3(cgrid), st, ev ? ev + 4 : nullptr, (const uint16_t*)part_o,
+         (const float2*)part_ml, pl.splits, pl.Mp, T, pl.H, w_uv, out, lse);
 }
 
 static bool misaligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }

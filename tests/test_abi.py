@@ -95,14 +95,14 @@ def test_workspace_too_small_rejected(dims, fixed_splits):
 
 
 def test_workspace_formula(fixed_splits):
-    # q_cat + o_lat (bf16) + split partials (bf16 O / l + fp32 (max, sum)), each region 256-byte aligned
+    # q_cat (bf16) + split partials (bf16 O / l + fp32 (max, sum)), each region 256-byte aligned
     d = kdv.make_dims(**KIMI)
     T, L = 15, 5553
     S = kdv.kdv_verify_num_splits(d, T, L)
     assert S == 4
     M, Mp = T * 64, ((T * 64 + 63) // 64) * 64
     up = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    expect = up(M * 576 * 2) + up(M * 512 * 2) + up(S * Mp * 512 * 2) + up(S * Mp * 8)
+    expect = up(M * 576 * 2) + up(S * Mp * 512 * 2) + up(S * Mp * 8)
     assert kdv.kdv_verify_workspace_bytes(d, T, L) == expect
 
 
