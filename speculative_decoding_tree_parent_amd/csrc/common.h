@@ -53,4 +53,16 @@ __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Combine a value across the lane pair (l, l ^ 32) with one VALU swap (v_permlane32_swap) instead of an LDS
+// permute.  Swapping a register with itself leaves lane l holding v[l & 31] in the first result and
+// v[(l & 31) + 32] in the second; both lanes of a pair combine the two in the same order, so they get the same bits.
+__device__ __forceinline__ float pair_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 }  // namespace kdv

@@ -222,23 +222,36 @@ struct TileDma {
 
 __device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Softmax state of one query row, held identically by the two lanes (l, l^32) that own it and by both waves of
-// the row pair.
+// Softmax state of the two query rows a lane serves in the value product: row c of row block 0 and row c of
+// row block 1 (c = lane % 32, a row block = 32 rows).  Every lane with the same c, in every wave, holds the
+// same values.
 struct RowState {
-  float m_ref;  // reference max (log2 units; an integer or -inf): P = 2^(s - m_ref) <= 2^8
-  float l;      // this lane's share of sum_n P (the lane pair adds up at the end)
+  float m_ref[2];  // reference max per row block (log2 units; an integer or -inf): P = 2^(s - m_ref) <= 2^8
+  float l[2];      // sum_n P relative to m_ref
 };
 
-// One tile.  Wave (wi, wj) computes the scores of its 32 KV rows (half wj of the tile), proposes a softmax
-// reference, and accumulates O^T += V^T P^T for its R/2 columns over its own half first; only then does it swap
-// P halves, proposals and row sums with its partner through LDS and add the partner's half.  The next tile's
-// DMA instructions (if `dma_on`) are spread over the score MFMAs.
+// Value-product split: each wave owns CPW latent columns for all 64 query rows, so every transposed V
+// fragment it reads from LDS feeds two MFMAs (row blocks 0 and 1).  (Transposed LDS reads cost about three
+// times as much per byte as plain 16-byte reads; this halves them.)  The narrow test shape (R = 64) uses two
+// waves of 32 columns.
+template <int R>
+struct PvSplit {
+  static constexpr int CPW = R / 4 >= 32 ? R / 4 : 32;  // latent columns per wave
+  static constexpr int WAVES = R / CPW;                  // waves that own columns
+  static constexpr int DBW = CPW / 32;                   // 32-column blocks per wave
+};
+
+// One tile.  Wave (wi, wj) computes the scores of row block wi against its 32 KV rows (half wj of the tile)
+// and proposes a softmax reference for its rows; P (bf16), proposals and row sums of all four waves are
+// swapped through LDS; every wave then agrees on each row block's maximum, brings its O to it (exact powers
+// of two) and accumulates O^T += V^T P^T for its columns over the whole tile.  The next tile's DMA
+// instructions (if `dma_on`) are spread over the score MFMAs.
 template <int R, int DR>
-__device__ __forceinline__ void tile_compute(const char* tile, const bf16x8 (&q)[(R + DR) / 16], f32x16 (&o)[R / 64],
-                                             RowState& st, int n0, int L, int N, uint32_t mw0, uint32_t mw1,
-                                             float scale_log2, uint4 (*pb_own)[64], uint4 (*pb_oth)[64],
-                                             float* ps_own, const float* ps_oth, float* mx_own, const float* mx_oth,
-                                             int wj, int lane, const TileDma<R, DR>& dma, bool dma_on) {
+__device__ __forceinline__ void tile_compute(const char* tile, const bf16x8 (&q)[(R + DR) / 16],
+                                             f32x16 (&o)[2][PvSplit<R>::DBW], RowState& st, int n0, int L, int N,
+                                             uint32_t mw0, uint32_t mw1, float scale_log2, uint4 (*pbuf)[2][2][64],
+                                             float (*mxch)[2][32], float (*psum)[2][32], int wi, int wj, int wave,
+                                             int lane, const TileDma<R, DR>& dma, bool dma_on) {
   using TL = TileLayout<R, DR>;
   constexpr int KB = (R + DR) / 16, DB = R / 64;
   const int g = lane >> 5, c = lane & 31;
@@ -300,20 +313,14 @@ __device__ __forceinline__ void tile_compute(const char* tile, const bf16x8 (&q)
   float tmax = -INFINITY;
 #pragma unroll
   for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[r]);
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-  // ---- proposed reference: keep the current one unless this half-tile exceeds it by more than 2^8.  If it
-  // moves, O is brought to it now (exact power of two), before this half is accumulated.
-  const float prop = (tmax > st.m_ref + 8.f) ? ceilf(tmax) : st.m_ref;
-  if (__any(prop > st.m_ref)) {
-    const float a = (prop > st.m_ref) ? fast_exp2(st.m_ref - prop) : 1.f;  // m_ref = -inf -> 0
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[db][r] *= a;
-  }
+  tmax = pair_max(tmax);
+  // ---- proposed reference for row (wi, c): keep the current one unless this half-tile exceeds it by more
+  // than 2^8.  P of this half-tile is taken relative to the proposal.
+  const float mref = (wi == 0) ? st.m_ref[0] : st.m_ref[1];  // (no dynamic index: st stays in registers)
+  const float prop = (tmax > mref + 8.f) ? ceilf(tmax) : mref;
   const float puse = (prop == -INFINITY) ? 0.f : prop;
   bf16x8 pk[2];
-  float ps = 0.f;  // this lane's share of the half-tile row sum, unrounded
+  float ps = 0.f;  // unrounded row sum of this half-tile
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const float p0 = fast_exp2(s[e] - puse), p1 = fast_exp2(s[8 + e] - puse);
@@ -321,96 +328,114 @@ __device__ __forceinline__ void tile_compute(const char* tile, const bf16x8 (&q)
     pk[0][e] = (__bf16)p0;
     pk[1][e] = (__bf16)p1;
   }
-  pb_own[0][lane] = __builtin_bit_cast(uint4, pk[0]);
-  pb_own[1][lane] = __builtin_bit_cast(uint4, pk[1]);
-  ps_own[lane] = ps;
-  if (g == 0) mx_own[c] = prop;
+  ps = pair_sum(ps);
+  pbuf[wi][wj][0][lane] = __builtin_bit_cast(uint4, pk[0]);
+  pbuf[wi][wj][1][lane] = __builtin_bit_cast(uint4, pk[1]);
+  if (g == 0) {
+    mxch[wi][wj][c] = prop;
+    psum[wi][wj][c] = ps;
+  }
 
-  // ---- O^T[d][m] += sum_n V^T[d][n] P^T[n][m]; within a 16-row block the contraction index k = g*8+e is
-  // KV row (e/4)*8 + g*4 + e%4, matching the score layout.  Fragment idx covers KV half (own first), 16-row
-  // block kb2 and column block db.
-  // Lane's rows are h2*32 + kb2*16 + rl (+8): the swizzle depends only on rl and the +8, and the column
-  // chunk's swizzled bits only on db % 4, so 8 per-tile pointers plus immediates address all 64 fragments
-  // (F = 16 case).
+  // ---- O^T[d][m] += sum_n V^T[d][n] P^T[n][m]; within a 16-row k-step the contraction index k = g*8+e is
+  // KV row (e/4)*8 + g*4 + e%4, matching the score layout.  Fragment idx = k-step ks (KV rows ks*16..+15) x
+  // column block db of this wave's columns.
+  // Lane's rows are ks*16 + rl (+8): the swizzle depends only on rl and the +8, and the column chunk's
+  // swizzled bits only on db, so 8 per-tile pointers plus immediates address all fragments (F = 16 case).
+  using PV = PvSplit<R>;
+  constexpr int DBW = PV::DBW;
+  const bool pv_wave = wave < PV::WAVES;
   const int rl = g * 4 + ((lane & 15) >> 2);
   const int cl = ((lane & 31) >> 4) * 2 + ((lane & 3) >> 1);  // chunk within a 32-column block
   const int sub = (lane & 1) * 8;                              // byte offset inside the chunk
-  const char* vt = tile + wj * R;                              // this wave's R/2 columns start R bytes in
-  const char* pvp[2][4];
+  const int col0 = (pv_wave ? wave : 0) * PV::CPW;             // first latent column of this wave
+  const char* pvp[2][DBW < 4 ? DBW : 4];
   if constexpr (TL::CK >= 16) {
+    static_assert(PV::CPW % 128 == 0, "column base must be a multiple of 16 chunks");
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-      for (int d4 = 0; d4 < 4; ++d4)
-        pvp[s2][d4] = vt + (rl + 8 * s2) * (R * 2) + (((d4 * 4 + cl) ^ swz<TL::CK>(rl + 8 * s2)) << 4) + sub;
+      for (int d4 = 0; d4 < (DBW < 4 ? DBW : 4); ++d4)
+        pvp[s2][d4] = tile + col0 * 2 + (rl + 8 * s2) * (R * 2) + (((d4 * 4 + cl) ^ swz<TL::CK>(rl + 8 * s2)) << 4) + sub;
   }
-  constexpr int NV = 4 * DB, NH = NV / 2, VD = NV < 6 ? NV : 6;
+  constexpr int NV = 4 * DBW, VD = NV < 6 ? NV : 6;
   auto vfrag = [&](int idx) -> bf16x8 {
-    const int h2 = (idx < NH) ? wj : (wj ^ 1), kb2 = (idx % NH) / DB, db = idx % DB;
-    const int rb = h2 * 32 + kb2 * 16;
+    const int ks = idx / DBW, db = idx % DBW;
+    const int rb = ks * 16;
     const char *p0, *p1;
     if constexpr (TL::CK >= 16) {
       const int imm = rb * (R * 2) + (db >> 2) * 256;
       p0 = pvp[0][db & 3] + imm;
       p1 = pvp[1][db & 3] + imm;
     } else {
-      const int ch = (wj * (R / 2) + db * 32) / 8 + cl;
+      const int ch = (col0 + db * 32) / 8 + cl;
       p0 = tile + TL::ckv(rb + rl, ch) + sub;
       p1 = tile + TL::ckv(rb + rl + 8, ch) + sub;
     }
     return concat_tr(lds_read_tr16(p0), lds_read_tr16(p1));
   };
+  // the first value fragments are requested before the exchange barrier
   bf16x8 vf[VD];
+  if (pv_wave) {
 #pragma unroll
-  for (int i = 0; i < VD; ++i) vf[i] = vfrag(i);
-  bf16x8 po[2];
-  float poth = 0.f, ps_o = 0.f, M = prop;
+    for (int i = 0; i < VD; ++i) vf[i] = vfrag(i);
+  }
+  __syncthreads();
+
+  // ---- every row block: agree on M = max of both halves' proposals, bring O and the P blocks to it, and update
+  // the row sum (fixed order, so all waves hold the same bits)
+  // all exchange reads are issued together (the own P block is read back too: same bits, no branch)
+  bf16x8 pf[2][4];  // [row block][k-step]: k-steps 0, 1 from KV half 0, 2, 3 from half 1
+  float pr[2][2], sm[2][2];
 #pragma unroll
-  for (int idx = 0; idx < NV; ++idx) {
-    if (idx == NH) {
-      // ---- partner's half: exchange, agree on M = max of both proposals, rescale by exact powers of two
-      __syncthreads();
-      po[0] = __builtin_bit_cast(bf16x8, pb_oth[0][lane]);
-      po[1] = __builtin_bit_cast(bf16x8, pb_oth[1][lane]);
-      ps_o = ps_oth[lane];
-      poth = mx_oth[c];
-      M = fmaxf(prop, poth);
-      if (__any(M > prop)) {
-        const float b = (M > prop) ? fast_exp2(prop - M) : 1.f;  // prop = -inf -> 0 (O holds nothing yet)
+  for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+    for (int jh = 0; jh < 2; ++jh) {
+      pr[b][jh] = mxch[b][jh][c];
+      sm[b][jh] = psum[b][jh][c];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) o[db][r] *= b;
-      }
-      const float f_oth = (M != -INFINITY) ? fast_exp2(poth - M) : 1.f;
-      if (__any(f_oth != 1.f)) {
+      for (int h = 0; h < 2; ++h) pf[b][jh * 2 + h] = __builtin_bit_cast(bf16x8, pbuf[b][jh][h][lane]);
+    }
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+  for (int b = 0; b < 2; ++b) {
+    const float p0 = pr[b][0], p1 = pr[b][1];
+    const float s0 = sm[b][0], s1 = sm[b][1];
+    const float M = fmaxf(p0, p1);  // >= m_ref: a proposal never lowers the reference
+    // A row that has seen nothing yet (M = -inf) has O = 0, l = 0 and P = 0: scaling it by 2^(x - 0) = 0 is exact.
+    const float Ms = (M == -INFINITY) ? 0.f : M;
+    const float a = fast_exp2(st.m_ref[b] - Ms);  // m_ref = -inf -> 0
+    if (__any(M > st.m_ref[b])) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) po[h][e] = (__bf16)((float)po[h][e] * f_oth);
+      for (int db = 0; db < DBW; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[b][db][r] *= a;
+    }
+    const float f0 = fast_exp2(p0 - Ms), f1 = fast_exp2(p1 - Ms);
+    if (__any((f0 != 1.f || f1 != 1.f) && M != -INFINITY)) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float f = (k < 2) ? f0 : f1;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pf[b][k][e] = (__bf16)((float)pf[b][k][e] * f);
       }
     }
-    const int kb2 = (idx % NH) / DB, db = idx % DB;
+    st.l[b] = st.l[b] * a + (s0 * f0 + s1 * f1);
+    st.m_ref[b] = M;
+  }
+  if (!pv_wave) return;  // wave-uniform; the caller's next barrier is the only one that follows
+#pragma unroll
+  for (int idx = 0; idx < NV; ++idx) {
+    const int ks = idx / DBW, db = idx % DBW;
     const bf16x8 a = vf[idx % VD];
     if (idx + VD < NV) vf[idx % VD] = vfrag(idx + VD);
-    const bf16x8 pb = (idx < NH) ? pk[kb2] : po[kb2];
     __builtin_amdgcn_sched_barrier(0);
-    o[db] = mfma32(a, pb, o[db]);
+    o[0][db] = mfma32(a, pf[0][ks], o[0][db]);
+    o[1][db] = mfma32(a, pf[1][ks], o[1][db]);
     __builtin_amdgcn_sched_barrier(0);
-  }
-  // ---- row sum relative to M, from both halves' unrounded sums, in a fixed order (KV half 0 first) so that both
-  // waves of the pair hold the same bits
-  if (M != -INFINITY) {
-    const float p0 = (wj == 0) ? prop : poth, p1 = (wj == 0) ? poth : prop;
-    const float q0 = (wj == 0) ? ps : ps_o, q1 = (wj == 0) ? ps_o : ps;
-    const float keep = fast_exp2(st.m_ref - M);  // m_ref = -inf -> 0
-    st.l = st.l * keep + (q0 * fast_exp2(p0 - M) + q1 * fast_exp2(p1 - M));
-    st.m_ref = M;
   }
 }
 
-// Workgroup = 4 waves over 64 query rows (m = t*H + h).  Wave (wi, wj): rows wi*32..+31; scores for KV rows
-// wj*32..+31 of each tile; values for latent columns wj*R/2..+R/2.  Lane l owns row m = tile_row + wi*32 + l%32.
+// Workgroup = 4 waves over 64 query rows (m = t*H + h).  Wave (wi, wj) = (w / 2, w % 2): scores of rows wi*32..+31
+// against KV rows wj*32..+31 of each tile; values for latent columns w*CPW..+CPW of all 64 rows.
 // Two LDS tiles: while one is computed, the next is gathered by DMA (spread over the score MFMAs).
 template <int R, int DR>
 __global__ __launch_bounds__(NTHREADS, 1) void splitkv_kernel(
@@ -421,9 +446,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void splitkv_kernel(
   using TL = TileLayout<R, DR>;
   constexpr int DQ = R + DR, KB = DQ / 16, DB = R / 64;
   __shared__ __attribute__((aligned(1024))) char kvbuf[2 * TL::BYTES];
-  __shared__ uint4 pbuf[2][2][2][64];  // [row pair][kv half][16-row k-block][lane]: P^T fragments (bf16)
-  __shared__ float mxch[2][2][32];     // proposed reference per row, per wave
-  __shared__ float psum[2][2][64];     // per-lane half-tile row sums, per wave
+  __shared__ uint4 pbuf[2][2][2][64];  // [row block][kv half][16-row k-step][lane]: P^T fragments (bf16)
+  __shared__ float mxch[2][2][32];     // [row block][kv half][row]: proposed reference
+  __shared__ float psum[2][2][32];     // [row block][kv half][row]: half-tile row sum
 
   // Workgroups are dealt to the XCDs round-robin (block b -> XCD b % NUM_XCD).  Every query tile of one KV
   // split is kept on one XCD so that split's rows are fetched into that XCD's L2 once and then shared.
@@ -490,16 +515,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void splitkv_kernel(
   // (MFMA's VGPR form, selected at build time), so the softmax rescale of O needs no AGPR<->VGPR copies.
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) asm volatile("" : "+a"(q[kb]));
-  f32x16 o[DB];
+  constexpr int DBW = PvSplit<R>::DBW;
+  f32x16 o[2][DBW];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) o[db] = zero16();
-  RowState st{-INFINITY, 0.f};
-  uint4(*pb_own)[64] = pbuf[wi][wj];
-  uint4(*pb_oth)[64] = pbuf[wi][wj ^ 1];
-  float* mx_own = mxch[wi][wj];
-  const float* mx_oth = mxch[wi][wj ^ 1];
-  float* ps_own = psum[wi][wj];
-  const float* ps_oth = psum[wi][wj ^ 1];
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int db = 0; db < DBW; ++db) o[b][db] = zero16();
+  RowState st{{-INFINITY, -INFINITY}, {0.f, 0.f}};
 
   for (int tile = tile_begin; tile < tile_end; ++tile) {
     const int cur = (tile - tile_begin) & 1;
@@ -509,34 +531,42 @@ __global__ __launch_bounds__(NTHREADS, 1) void splitkv_kernel(
     dma.target(kvbuf + (cur ^ 1) * TL::BYTES, slot_v);
     if (tile + 2 < tile_end) slot_v = page_table[min((tile + 2) * KV_TILE + lane, N - 1)];
 #pragma unroll
-    for (int db = 0; db < DB; ++db) asm volatile("" : "+v"(o[db]));
-    tile_compute<R, DR>(kvbuf + cur * TL::BYTES, q, o, st, tile * KV_TILE, L, N, mw0, mw1, scale_log2, pb_own,
-                        pb_oth, ps_own, ps_oth, mx_own, mx_oth, wj, lane, dma, more);
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int db = 0; db < DBW; ++db) asm volatile("" : "+v"(o[b][db]));
+    tile_compute<R, DR>(kvbuf + cur * TL::BYTES, q, o, st, tile * KV_TILE, L, N, mw0, mw1, scale_log2, pbuf, mxch,
+                        psum, wi, wj, wave, lane, dma, more);
   }
 
-  const float l_row = st.l + __shfl_xor(st.l, 32);
   // Partial of this split: O / l rounded to bf16, row-major [split][row][R] so that a row is one contiguous
   // 1 KB line for the combine, plus fp32 (max, sum) per row, [split][row].  The register fragments go to
   // LDS first (the KV buffers are free once every wave has left the loop), then out as whole rows.
-  const float inv = (l_row > 0.f) ? 1.f / l_row : 0.f;  // a row that saw nothing here has O = 0
   constexpr int OP = R + 8;  // staging pitch (elements): rows 16 B apart in the bank space
   static_assert(M_TILE * OP * 2 <= 2 * TL::BYTES, "O staging must fit in the KV buffers");
   uint16_t* o_s = reinterpret_cast<uint16_t*>(kvbuf);
   __syncthreads();
-  {
-    // lane (c, g) of wave (wi, wj) holds row wi*32 + c, columns wj*R/2 + db*32 + q4*8 + g*4 + 0..3
-    uint16_t* row_s = o_s + (wi * 32 + c) * OP + wj * (R / 2) + g * 4;
+  if (wave < PvSplit<R>::WAVES) {
+    // lane (c, g) holds rows b*32 + c, columns wave*CPW + db*32 + q4*8 + g*4 + 0..3
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int b = 0; b < 2; ++b) {
+      const float inv = (st.l[b] > 0.f) ? 1.f / st.l[b] : 0.f;  // a row that saw nothing here has O = 0
+      uint16_t* row_s = o_s + (b * 32 + c) * OP + wave * PvSplit<R>::CPW + g * 4;
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        bf16x4 v;
+      for (int db = 0; db < DBW; ++db)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = (__bf16)(o[db][q4 * 4 + e] * inv);
-        *reinterpret_cast<bf16x4*>(row_s + db * 32 + q4 * 8) = v;
-      }
+        for (int q4 = 0; q4 < 4; ++q4) {
+          bf16x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = (__bf16)(o[b][db][q4 * 4 + e] * inv);
+          *reinterpret_cast<bf16x4*>(row_s + db * 32 + q4 * 8) = v;
+        }
+    }
   }
-  if (wj == 0 && g == 0) part_ml[(size_t)split * Mp + mt * M_TILE + wi * 32 + c] = make_float2(st.m_ref, l_row);
+  if (wave == 0 && g == 0) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+      part_ml[(size_t)split * Mp + mt * M_TILE + b * 32 + c] = make_float2(st.m_ref[b], st.l[b]);
+  }
   __syncthreads();
   uint16_t* dst = part_o + ((size_t)split * Mp + mt * M_TILE) * R;
   constexpr int CPR = R / 8;  // 16-byte chunks per row
