@@ -585,94 +585,116 @@ __global__ __launch_bounds__(NTHREADS, 1) void splitkv_kernel(
 // out[t,h][v] = sum_r W_UV[h][v][r] o[t,h][r].
 //
 // One workgroup per (head, block of RT nodes).  Workgroups are dealt to the XCDs round-robin, and the node
-// blocks of one head are kept on one XCD, so W_UV[h] is fetched into that XCD's L2 once.  The first 16
-// splits' partials and each wave's 32 rows of W_UV are requested together; the workgroup merges its RT
-// latent rows (one thread per 16-byte chunk of a row) while W_UV is still arriving.  MFMA D[v][t] = sum_r W_UV[h][v][r] o[t][r] then reads W from registers and o
-// from LDS, both r-contiguous; columns t >= RT of the product repeat the last row and are never stored.
+// blocks of one head are kept on one XCD, so W_UV[h] is fetched into that XCD's L2 once.  The waves split
+// the fetching so that none waits for the other's loads (a wave's load counter is in order):
+//   - waves 0 and 1 load the partials of the RT rows into registers and merge them (two 16-byte chunks of a
+//     row per thread);
+//   - waves 2 and 3 gather all of W_UV[h] into LDS by DMA (an LDS-DMA gather moves about 2.5 times the
+//     bytes per CU that loads into registers do).  Chunk ch of W row r sits at position ch ^ (r % WSW) of
+//     the row, so the MFMA's quarter-wave reads (16 rows, one chunk) hit 16 distinct bank groups.
+// After one barrier, wave w computes D[v][t] = sum_r W_UV[h][v][r] o[t][r] for its 32 columns v, both
+// operands read from LDS (r-contiguous); columns t >= RT of the product repeat the last row, never stored.
 template <int R, int DV>
 __global__ __launch_bounds__(NTHREADS) void combine_up_kernel(const uint16_t* __restrict__ part_o,
                                                               const float2* __restrict__ part_ml, int S, int Mp,
                                                               int T, int H, const uint16_t* __restrict__ w_uv,
                                                               uint16_t* __restrict__ out, float* __restrict__ lse) {
-  constexpr int RT = 4;            // tree nodes per workgroup
-  constexpr int CPR = R / 8;       // 16-byte chunks per latent row
-  constexpr int KS = R / 16;       // MFMA k-steps
-  constexpr int OP = R + 8;        // LDS pitch of a merged row (elements)
-  constexpr int CH = 16;           // splits whose loads are in flight together
-  static_assert(RT * CPR <= NTHREADS, "one thread per chunk of each row");
+  constexpr int RT = 4;                      // tree nodes per workgroup
+  constexpr int CPR = R / 8;                 // 16-byte chunks per latent row
+  constexpr int KS = R / 16;                 // MFMA k-steps
+  constexpr int OP = R + 8;                  // LDS pitch of a merged row (elements)
+  constexpr int CH = 16;                     // splits whose loads are in flight together
+  constexpr int MT = RT * CPR < 128 ? RT * CPR : 128;  // merging threads (in waves 0 and 1)
+  constexpr int CPT = RT * CPR / MT;         // chunks per merging thread
+  constexpr int WSW = CPR < 16 ? CPR : 16;   // W_UV staging swizzle width (chunks)
+  constexpr int WBYTES = DV * R * 2;         // all of W_UV[h]
+  constexpr int WINS = WBYTES / 1024 / 2;    // DMA instructions per fetching wave (waves 2 and 3)
+  static_assert(CPT >= 1 && RT * CPR % MT == 0, "chunks must split evenly over the merging threads");
   static_assert(DV % 32 == 0 && DV / 32 <= NTHREADS / 64, "one wave per 32 output columns");
+  static_assert(WBYTES % 2048 == 0, "W_UV must split evenly over two fetching waves");
   __shared__ __attribute__((aligned(16))) uint16_t o_s[RT * OP];
+  __shared__ __attribute__((aligned(1024))) char w_s[WBYTES];
   const int xcd = blockIdx.x % NUM_XCD, j = blockIdx.x / NUM_XCD;
   const int TB = (T + RT - 1) / RT;
   const int h = xcd + NUM_XCD * (j / TB), t0 = (j % TB) * RT;
   if (h >= H) return;  // padding block (uniform; before any barrier)
   const int nrow = min(RT, T - t0);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, c = lane & 31;
-  const bool up_wave = wave * 32 < DV;
 
-  const int i = tid / CPR, k = tid % CPR;
-  const bool merge_thread = i < RT;
-  const int t = t0 + min(i, nrow - 1);  // rows past the last node repeat it (never stored)
-  const int m = t * H + h;
-  const bf16x8* src = reinterpret_cast<const bf16x8*>(part_o + (size_t)m * R) + k;
-  const size_t stride = (size_t)Mp * CPR;  // bf16x8 per split
-  float2 ml[CH];
-  bf16x8 v[CH];
-  auto load_chunk = [&](int s0) {
+  if (wave >= 2) {
+    // ---- W_UV[h] -> LDS: lane l of instruction i fills position (i*64 + l) of the swizzled rows
+    const char* wsrc = reinterpret_cast<const char*>(w_uv + (size_t)h * DV * R);
+    const uint32_t wl = lds_address(w_s);
 #pragma unroll
-    for (int q = 0; q < CH; ++q) {
-      const int sq = min(s0 + q, S - 1);
-      ml[q] = part_ml[(size_t)sq * Mp + m];
-      v[q] = src[sq * stride];
+    for (int k = 0; k < WINS; ++k) {
+      const int ins = (wave - 2) + 2 * k;
+      const int pos = ins * 64 + lane, r = pos / CPR, p = pos % CPR;
+      dma16_lane_addr(wsrc + (size_t)r * (R * 2) + ((p ^ (r & (WSW - 1))) << 4), wl + ins * 1024);
     }
-  };
-  float mx = -INFINITY, den = 0.f;
-  float num[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  auto merge_chunk = [&](int s0) {
+    wait_vmem_all();
+  } else if (tid < MT) {
+    // ---- merge: thread handles chunks k0 .. k0 + CPT - 1 of row i
+    const int i = tid / (CPR / CPT), k0 = (tid % (CPR / CPT)) * CPT;
+    const int t = t0 + min(i, nrow - 1);  // rows past the last node repeat it (never stored)
+    const int m = t * H + h;
+    const bf16x8* src = reinterpret_cast<const bf16x8*>(part_o + (size_t)m * R) + k0;
+    const size_t stride = (size_t)Mp * CPR;  // bf16x8 per split
+    float mx = -INFINITY, den = 0.f;
+    float num[CPT][8];
 #pragma unroll
-    for (int q = 0; q < CH; ++q) {
-      if (s0 + q >= S || ml[q].x == -INFINITY) continue;  // nothing visible in that split
-      const float mn = fmaxf(mx, ml[q].x);
-      const float a = fast_exp2(mx - mn);  // mx = -inf -> 0
-      const float wgt = fast_exp2(ml[q].x - mn) * ml[q].y;
-      den = den * a + wgt;
+    for (int u = 0; u < CPT; ++u)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) num[e] = num[e] * a + wgt * (float)v[q][e];
-      mx = mn;
-    }
-  };
-  // the first chunk of partials, then this wave's rows of W_UV: one memory round trip for both
-  if (merge_thread) load_chunk(0);
-  bf16x8 w[KS];
-  if (up_wave) {
-    const uint16_t* wrow = w_uv + ((size_t)h * DV + wave * 32 + c) * R + g * 8;
+      for (int e = 0; e < 8; ++e) num[u][e] = 0.f;
+    for (int s0 = 0; s0 < S; s0 += CH) {
+      float2 ml[CH];
+      bf16x8 v[CH][CPT];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) w[ks] = load_bf16x8(wrow + ks * 16);
-  }
-  if (merge_thread) {
-    merge_chunk(0);
-    for (int s0 = CH; s0 < S; s0 += CH) {
-      load_chunk(s0);
-      merge_chunk(s0);
+      for (int q = 0; q < CH; ++q) {
+        const int sq = min(s0 + q, S - 1);
+        ml[q] = part_ml[(size_t)sq * Mp + m];
+#pragma unroll
+        for (int u = 0; u < CPT; ++u) v[q][u] = src[sq * stride + u];
+      }
+#pragma unroll
+      for (int q = 0; q < CH; ++q) {
+        if (s0 + q >= S || ml[q].x == -INFINITY) continue;  // nothing visible in that split
+        const float mn = fmaxf(mx, ml[q].x);
+        const float a = fast_exp2(mx - mn);  // mx = -inf -> 0
+        const float wgt = fast_exp2(ml[q].x - mn) * ml[q].y;
+        den = den * a + wgt;
+#pragma unroll
+        for (int u = 0; u < CPT; ++u)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) num[u][e] = num[u][e] * a + wgt * (float)v[q][u][e];
+        mx = mn;
+      }
     }
     const float inv = 1.f / den;
-    bf16x8 ov;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) ov[e] = (__bf16)(num[e] * inv);
-    *reinterpret_cast<bf16x8*>(&o_s[i * OP + k * 8]) = ov;
-    if (lse != nullptr && k == 0 && i < nrow) lse[m] = (mx + log2f(den)) * 0.69314718055994530942f;
+    for (int u = 0; u < CPT; ++u) {
+      bf16x8 ov;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ov[e] = (__bf16)(num[u][e] * inv);
+      *reinterpret_cast<bf16x8*>(&o_s[i * OP + (k0 + u) * 8]) = ov;
+    }
+    if (lse != nullptr && k0 == 0 && i < nrow) lse[m] = (mx + log2f(den)) * 0.69314718055994530942f;
   }
-  __syncthreads();
-  if (!up_wave) return;  // wave-uniform; no barrier follows
+  __syncthreads();  // merged rows and W_UV are in LDS
+  if (wave * 32 >= DV) return;  // wave-uniform; no barrier follows
 
-  // two independent accumulation chains (even / odd k-steps)
+  // all W fragments first (one round of LDS latency), then two independent accumulation chains
+  const char* wrow = w_s + (wave * 32 + c) * (R * 2);
+  const int wsz = (wave * 32 + c) & (WSW - 1);
+  bf16x8 wf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) wf[ks] = *reinterpret_cast<const bf16x8*>(wrow + (((2 * ks + g) ^ wsz) << 4));
   f32x16 acc0 = zero16(), acc1 = zero16();
   const uint16_t* orow = o_s + min(c, RT - 1) * OP + g * 8;
 #pragma unroll
   for (int ks = 0; ks < KS; ks += 2) {
-    acc0 = mfma32(w[ks], *reinterpret_cast<const bf16x8*>(orow + ks * 16), acc0);
-    acc1 = mfma32(w[ks + 1], *reinterpret_cast<const bf16x8*>(orow + (ks + 1) * 16), acc1);
+    acc0 = mfma32(wf[ks], *reinterpret_cast<const bf16x8*>(orow + ks * 16), acc0);
+    acc1 = mfma32(wf[ks + 1], *reinterpret_cast<const bf16x8*>(orow + (ks + 1) * 16), acc1);
   }
   if (c < nrow) {
     uint16_t* dst = out + ((size_t)(t0 + c) * H + h) * DV + wave * 32 + g * 4;
