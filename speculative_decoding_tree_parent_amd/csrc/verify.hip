@@ -35,84 +35,6 @@ struct Shape {
   static constexpr int DB = R / 64;      // 32-wide output column blocks per wave (a wave owns R/2 columns)
 };
 
-// ------------------------------------------------------------------------------------------------ q_absorb
-// grid (H, ceil(R/128)); each wave produces 32 latent columns for all T nodes of head h.
-// MFMA D[r][t] = sum_k W_UK[h][k][r] q_nope[t,h][k]: the A operand W^T is read from LDS with transposed
-// reads (W_UK is stored k-major), the B operand straight from global memory.
-template <int DN, int R, int DR>
-__global__ __launch_bounds__(NTHREADS) void q_absorb_kernel(const uint16_t* __restrict__ q_nope,
-                                                            const uint16_t* __restrict__ q_rope,
-                                                            const uint16_t* __restrict__ w_uk,
-                                                            uint16_t* __restrict__ q_cat, int T, int H) {
-  constexpr int DQ = R + DR;
-  constexpr int RB = 128;         // latent columns per workgroup
-  constexpr int WP = RB + 16;     // LDS pitch (elements)
-  __shared__ __attribute__((aligned(16))) uint16_t w_s[DN * WP];
-  const int h = blockIdx.x, r0 = blockIdx.y * RB;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 5, c = lane & 31;
-
-  // W_UK[h][:, r0:r0+RB] -> LDS: every load of a thread is issued before the first LDS write, so the
-  // workgroup waits for one memory round trip, not one per load
-  constexpr int WLOADS = DN * (RB / 8) / NTHREADS;
-  static_assert(DN * (RB / 8) % NTHREADS == 0, "W_UK slice must split evenly over the threads");
-  const uint16_t* wh = w_uk + (size_t)h * DN * R;
-  uint4 wv[WLOADS];
-#pragma unroll
-  for (int u = 0; u < WLOADS; ++u) {
-    const int ci = tid + u * NTHREADS;
-    const int k = ci / (RB / 8), col = (ci % (RB / 8)) * 8;
-    wv[u] = (r0 + col < R) ? *reinterpret_cast<const uint4*>(wh + (size_t)k * R + r0 + col) : make_uint4(0u, 0u, 0u, 0u);
-  }
-  // query fragments of the first 32 nodes; rows past T load node T-1 (their results are never stored)
-  bf16x8 qb[DN / 16];
-  {
-    const int tq = min(c, T - 1);
-#pragma unroll
-    for (int kb = 0; kb < DN / 16; ++kb) qb[kb] = load_bf16x8(q_nope + ((size_t)tq * H + h) * DN + kb * 16 + g * 8);
-  }
-  if (blockIdx.y == 0) {
-    for (int ci = tid; ci < T * (DR / 8); ci += NTHREADS) {
-      const int t = ci / (DR / 8), col = (ci % (DR / 8)) * 8;
-      *reinterpret_cast<uint4*>(q_cat + (size_t)(t * H + h) * DQ + R + col) =
-          *reinterpret_cast<const uint4*>(q_rope + ((size_t)t * H + h) * DR + col);
-    }
-  }
-#pragma unroll
-  for (int u = 0; u < WLOADS; ++u) {
-    const int ci = tid + u * NTHREADS;
-    const int k = ci / (RB / 8), col = (ci % (RB / 8)) * 8;
-    *reinterpret_cast<uint4*>(&w_s[k * WP + col]) = wv[u];
-  }
-  __syncthreads();
-  const int rs = wave * 32;
-  if (r0 + rs >= R) return;  // wave-uniform; no barrier follows
-  for (int tb = 0; tb < T; tb += 32) {
-    f32x16 acc = zero16();
-    const int t = tb + c;
-#pragma unroll
-    for (int kb = 0; kb < DN / 16; ++kb) {
-      const int krow = kb * 16 + g * 8 + ((lane & 15) >> 2);
-      const int col = rs + ((lane & 31) >> 4) * 16 + 4 * (lane & 3);
-      const bf16x8 a = concat_tr(lds_read_tr16(&w_s[krow * WP + col]), lds_read_tr16(&w_s[(krow + 4) * WP + col]));
-      const bf16x8 b = (tb == 0) ? qb[kb] : load_bf16x8(q_nope + ((size_t)min(t, T - 1) * H + h) * DN + kb * 16 + g * 8);
-      acc = mfma32(a, b, acc);
-    }
-    if (t < T) {
-      uint16_t* dst = q_cat + (size_t)(t * H + h) * DQ + r0 + rs + g * 4;
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        bf16x4 v;
-        v[0] = (__bf16)acc[q4 * 4 + 0];
-        v[1] = (__bf16)acc[q4 * 4 + 1];
-        v[2] = (__bf16)acc[q4 * 4 + 2];
-        v[3] = (__bf16)acc[q4 * 4 + 3];
-        *reinterpret_cast<bf16x4*>(dst + q4 * 8) = v;
-      }
-    }
-  }
-}
-
 // ------------------------------------------------------------------------------------------------ splitkv
 // LDS layout of one 64-row KV tile: the latent rows [64][R] then the rotary rows [64][DR], bf16, row-major.
 // Within a row the 16-byte chunks are XOR-swizzled (chunk c of row r is stored at c ^ swz(r)) so that
@@ -574,6 +496,87 @@ __global__ __launch_bounds__(NTHREADS, 1) void splitkv_kernel(
   for (int idx = tid; idx < M_TILE * CPR; idx += NTHREADS) {
     const int row = idx / CPR, ch = idx % CPR;
     *reinterpret_cast<uint4*>(dst + (size_t)row * R + ch * 8) = *reinterpret_cast<const uint4*>(o_s + row * OP + ch * 8);
+  }
+}
+
+// ------------------------------------------------------------------------------------------------ q_absorb
+// grid (H, ceil(R/128)); each wave produces 32 latent columns for all T nodes of head h.
+// MFMA D[r][t] = sum_k W_UK[h][k][r] q_nope[t,h][k]: the A operand W^T is read from LDS with transposed
+// reads (W_UK is stored k-major), the B operand straight from global memory.
+// The W_UK block arrives by LDS DMA (an LDS-DMA gather moves about 2.5 times the bytes per CU that loads into
+// registers do).  LDS rows are RB/8 = 16 chunks of 16 bytes with chunk c of row k at c ^ 4*(k % 4): a
+// transposed read's 32 lanes cover 4 aligned rows x 4 aligned chunks, which then fall in 16 distinct bank
+// groups.  DMA instruction i fills rows 4i..4i+3, lane l the row's position l % 16.
+template <int DN, int R, int DR>
+__global__ __launch_bounds__(NTHREADS) void q_absorb_kernel(const uint16_t* __restrict__ q_nope,
+                                                            const uint16_t* __restrict__ q_rope,
+                                                            const uint16_t* __restrict__ w_uk,
+                                                            uint16_t* __restrict__ q_cat, int T, int H) {
+  constexpr int DQ = R + DR;
+  constexpr int RB = 128;                    // latent columns per workgroup
+  constexpr int WINS = DN * RB * 2 / 1024;   // DMA instructions for the W_UK block
+  static_assert(WINS % 4 == 0, "W_UK block must split evenly over the four waves");
+  __shared__ __attribute__((aligned(1024))) char w_s[DN * RB * 2];
+  const int h = blockIdx.x, r0 = blockIdx.y * RB;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, c = lane & 31;
+
+  {
+    const char* wh = reinterpret_cast<const char*>(w_uk + (size_t)h * DN * R);
+    const uint32_t wl = lds_address(w_s);
+#pragma unroll
+    for (int k4 = 0; k4 < WINS / 4; ++k4) {
+      const int ins = wave + 4 * k4;
+      const int k = ins * 4 + (lane >> 4);
+      const int col = r0 + (((lane & 15) ^ (4 * (k & 3))) << 3);
+      if (col < R) dma16_lane_addr(wh + ((size_t)k * R + col) * 2, wl + ins * 1024);  // (columns past R: never read)
+    }
+  }
+  // query fragments of the first 32 nodes; rows past T load node T-1 (their results are never stored)
+  bf16x8 qb[DN / 16];
+  {
+    const int tq = min(c, T - 1);
+#pragma unroll
+    for (int kb = 0; kb < DN / 16; ++kb) qb[kb] = load_bf16x8(q_nope + ((size_t)tq * H + h) * DN + kb * 16 + g * 8);
+  }
+  if (blockIdx.y == 0) {
+    for (int ci = tid; ci < T * (DR / 8); ci += NTHREADS) {
+      const int t = ci / (DR / 8), col = (ci % (DR / 8)) * 8;
+      *reinterpret_cast<uint4*>(q_cat + (size_t)(t * H + h) * DQ + R + col) =
+          *reinterpret_cast<const uint4*>(q_rope + ((size_t)t * H + h) * DR + col);
+    }
+  }
+  wait_vmem_all();
+  __syncthreads();
+  const int rs = wave * 32;
+  if (r0 + rs >= R) return;  // wave-uniform; no barrier follows
+  // lane's transposed-read position: rows kb*16 + g*8 + (lane%16)/4 (+4), chunk rs/8 + cl, byte sub
+  const int cl = ((lane & 31) >> 4) * 2 + ((lane & 3) >> 1), sub = (lane & 1) * 8;
+  auto wread = [&](int krow) -> i16x4 {
+    return lds_read_tr16(w_s + krow * (RB * 2) + (((rs / 8 + cl) ^ (4 * (krow & 3))) << 4) + sub);
+  };
+  for (int tb = 0; tb < T; tb += 32) {
+    f32x16 acc = zero16();
+    const int t = tb + c;
+#pragma unroll
+    for (int kb = 0; kb < DN / 16; ++kb) {
+      const int krow = kb * 16 + g * 8 + ((lane & 15) >> 2);
+      const bf16x8 a = concat_tr(wread(krow), wread(krow + 4));
+      const bf16x8 b = (tb == 0) ? qb[kb] : load_bf16x8(q_nope + ((size_t)min(t, T - 1) * H + h) * DN + kb * 16 + g * 8);
+      acc = mfma32(a, b, acc);
+    }
+    if (t < T) {
+      uint16_t* dst = q_cat + (size_t)(t * H + h) * DQ + r0 + rs + g * 4;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        bf16x4 v;
+        v[0] = (__bf16)acc[q4 * 4 + 0];
+        v[1] = (__bf16)acc[q4 * 4 + 1];
+        v[2] = (__bf16)acc[q4 * 4 + 2];
+        v[3] = (__bf16)acc[q4 * 4 + 3];
+        *reinterpret_cast<bf16x4*>(dst + q4 * 8) = v;
+      }
+    }
   }
 }
 
