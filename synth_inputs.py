@@ -78,6 +78,30 @@ def random_parents(rng: np.random.Generator, T: int, depth_cap: int | None = Non
     return parent
 
 
+def accept_inputs(seed: int, T: int, vocab: int = 32000, follow: float = 0.7, dup: float = 0.0,
+                  parent=None) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Seeded (parent, draft tokens, target predictions) for the tree-accept step; int32 arrays of length T.
+
+    A random recursive tree (unless ``parent`` is given) with uniform draft tokens; with probability ``dup``
+    a node copies an earlier sibling's token.  The target's prediction at a node is, with probability
+    ``follow``, the draft token of one of its children drawn uniformly (so drafts get accepted), otherwise
+    a uniform token.  Draw order: parent, tokens, duplicate choices, predictions.
+    """
+    rng = np.random.default_rng(seed)
+    par = random_parents(rng, T) if parent is None else np.asarray(parent, dtype=np.int32)
+    tok = rng.integers(0, vocab, size=T).astype(np.int32)
+    for i in range(1, T):
+        sib = [j for j in range(1, i) if par[j] == par[i]]
+        if sib and rng.random() < dup:
+            tok[i] = tok[sib[int(rng.integers(0, len(sib)))]]
+    pred = rng.integers(0, vocab, size=T).astype(np.int32)
+    for p in range(T):
+        kids = [c for c in range(T) if par[c] == p]
+        if kids and rng.random() < follow:
+            pred[p] = tok[kids[int(rng.integers(0, len(kids)))]]
+    return par, tok, pred
+
+
 @dataclass
 class VerifyInputs:
     """One layer's worth of tree-verify inputs (bf16 bit patterns + their exact float32 values)."""
