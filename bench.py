@@ -45,7 +45,7 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, vendor figure
 COLD_BYTES = 576 << 20
 KERNEL_SOURCES = ("speculative_decoding_tree_parent_amd/csrc/verify.hip",
                   "speculative_decoding_tree_parent_amd/csrc/common.h")
-KERNELS = ("tree_mask_kernel", "q_absorb_kernel", "splitkv_kernel", "combine_up_kernel")
+KERNELS = ("tree_mask_kernel", "q_absorb_kernel", "splitkv_kernel", "combine_up_kernel", "tree_accept_kernel")
 
 
 def log(msg):
@@ -322,11 +322,46 @@ def run(args, torch, si, kdv, dev, hip, stream, sh):
         step_ev(cold_ptrs[i % len(cold_ptrs)], per_step_evs[i])
     torch.cuda.synchronize()
     names = ["q_absorb", "splitkv", "combine_up"]
-    tot = {n: 0.0 for n in names}
+    samples = {n: [] for n in names}
     for ev in ev_list:
         for k, n in enumerate(names):
-            tot[n] += hip.elapsed_ms(ev[2 * k], ev[2 * k + 1])
-    kern_us = {n: 1e3 * tot[n] / n_calls for n in names}
+            samples[n].append(1e3 * hip.elapsed_ms(ev[2 * k], ev[2 * k + 1]))
+    kern_us = {n: float(np.mean(v)) for n, v in samples.items()}
+    kern_pct = {n: [round(float(np.percentile(v, 10)), 3), round(float(np.percentile(v, 90)), 3)]
+                for n, v in samples.items()}
+
+    # The tree mask (once per verify step) and the greedy tree accept that follows verification: launch-bound,
+    # timed as one HIP graph of many launches.
+    def graph_us(launch, n=200):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for _ in range(n):
+                launch()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = hip.event(), hip.event()
+        hip.record(e0, sh)
+        g.replay()
+        hip.record(e1, sh)
+        return 1e3 * hip.elapsed_ms(e0, e1) / n
+
+    def mask_launch():
+        rc = kdv.kdv_build_tree_mask(fixed["parent"], T, fixed["mask"], fixed["status"], sh)
+        if rc:
+            raise kdv.KdvError(rc, "kdv_build_tree_mask")
+    kern_us["tree_mask"] = graph_us(mask_launch)
+    _, acc_tok, acc_pred = si.accept_inputs(0, T, follow=0.8, parent=parent_np)
+    acc_in = [torch.from_numpy(a.astype(np.int32)).to(dev) for a in (acc_tok, acc_pred)]
+    acc_out = [torch.empty((n,), dtype=torch.int32, device=dev) for n in (T, 1, 1, 1)]
+
+    def accept_launch():
+        rc = kdv.kdv_tree_accept(fixed["parent"], acc_in[0].data_ptr(), acc_in[1].data_ptr(), T,
+                                 *[t.data_ptr() for t in acc_out], sh)
+        if rc:
+            raise kdv.KdvError(rc, "kdv_tree_accept")
+    accept_us = graph_us(accept_launch)
+    torch.cuda.synchronize()
+    n_path = int(acc_out[1].item())
 
     us_layer_cold = 1e3 * ms_cold / (K * layers_per_step)
     us_layer_hot = 1e3 * ms_hot / (K * layers_per_step)
@@ -357,6 +392,7 @@ def run(args, torch, si, kdv, dev, hip, stream, sh):
         "hot": {"us_per_layer": round(us_layer_hot, 3), "tflops": round(tflops_hot, 3),
                 "frac_bf16_peak": round(tflops_hot / PEAK_BF16_TFLOPS, 4)},
         "kernels_us": {k: round(v, 3) for k, v in kern_us.items()},
+        "kernels_us_p10_p90": kern_pct,
         "kernel_timing": kern_mode,
         "kernel_calls": n_calls,
         "work_per_layer": {"gflop": round(wk["flops"] / 1e9, 4), "mbytes": round(wk["bytes"] / 1e6, 3)},
@@ -365,6 +401,8 @@ def run(args, torch, si, kdv, dev, hip, stream, sh):
                      "traffic": traffic_from_profile(args.workload),
                      "work_per_launch_gflop": round(wk["flops_splitkv"] / 1e9, 4)},
         "cpu_baseline": None,
+        "next_rows": {"tree_accept": {"us": round(accept_us, 3), "nodes": T, "accepted_path_nodes": n_path,
+                                      "timing": "one HIP graph of 200 launches", "bound": "launch latency"}},
     }
 
     if not args.no_cpu_baseline:
@@ -406,7 +444,19 @@ def cpu_baseline(args, inp, wk, layers_per_step):
             break
     s_per_layer = el / n / frac
     wk1 = work(inp.H, inp.Dn, inp.Dr, inp.R, inp.Dv, inp.L, inp.T, inp.parent)
+    cpu_model, blas = "unknown", "unknown"
+    try:
+        cpu_model = next(ln.split(":", 1)[1].strip() for ln in open("/proc/cpuinfo") if ln.startswith("model name"))
+    except Exception:
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+        blas = ", ".join(sorted({f"{i.get('internal_api')} {i.get('version')}" for i in threadpool_info()
+                                 if i.get("user_api") == "blas"})) or "unknown"
+    except Exception:
+        pass
     return {"value": round(wk1["flops"] / s_per_layer / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "cpu_model": cpu_model, "blas": blas,
             "kind": "oracle", "sample": f"{sample}; {n} calls in {el:.1f} s",
             "seconds_per_layer": round(s_per_layer, 4), "host_cpus": os.cpu_count()}
 
@@ -469,11 +519,17 @@ def _read_csv(path):
 def _phases(bench, kernel):
     """Dispatch index ranges of bench.py's phases for one kernel, in launch order."""
     W, K, lps, n = bench["warmup"], bench["steps"], bench["config"]["layers_per_step"], bench["kernel_calls"]
-    per = 1 if kernel == "tree_mask_kernel" else lps
-    n_eager = n // lps if kernel == "tree_mask_kernel" else n
-    edges = [("warm-up", W * per), ("graph cold, upload replay", K * per), ("graph cold, timed replay", K * per),
-             ("graph hot, upload replay", K * per), ("graph hot, timed replay", K * per),
-             ("eager cold, kernel events", n_eager)]
+    if kernel == "tree_accept_kernel":  # only in the launch-timing graphs at the end
+        edges = [("warm-up", 0), ("graph cold, upload replay", 0), ("graph cold, timed replay", 0),
+                 ("graph hot, upload replay", 0), ("graph hot, timed replay", 0), ("eager cold, kernel events", 0),
+                 ("launch-timing graph", 400)]
+    else:
+        per = 1 if kernel == "tree_mask_kernel" else lps
+        n_eager = n // lps if kernel == "tree_mask_kernel" else n
+        edges = [("warm-up", W * per), ("graph cold, upload replay", K * per), ("graph cold, timed replay", K * per),
+                 ("graph hot, upload replay", K * per), ("graph hot, timed replay", K * per),
+                 ("eager cold, kernel events", n_eager),
+                 ("launch-timing graph", 400 if kernel == "tree_mask_kernel" else 0)]
     out, a = {}, 0
     for name, c in edges:
         out[name] = (a, a + c)

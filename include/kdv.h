@@ -81,6 +81,28 @@ typedef enum kdv_status {
  * KDV_ERR_ALIGN (parent, mask or status not 4-byte aligned), KDV_ERR_HIP. */
 int kdv_build_tree_mask(const int32_t* parent, int32_t T, uint32_t* mask, int32_t* status, void* stream);
 
+/* Greedy acceptance of the verified draft tree: the longest accepted root path, selected on the device
+ * ("The Architecture of Diagnosis...", section "Phase 1: Custom CUDA Kernels", item 3).
+ *
+ *   parent     : device int32 [T], as for kdv_build_tree_mask.  Node 0 is the root, whose token is
+ *                already committed.
+ *   tokens     : device int32 [T]; tokens[t] is node t's draft token (tokens[0] is not read).
+ *   pred       : device int32 [T]; pred[t] is the target model's greedy prediction (argmax) after the
+ *                prefix that ends at node t, e.g. from the verify pass's logits.
+ *   T          : 1 <= T <= 64.
+ *   path       : device int32 [T], written: the accepted root path as node indices, path[0] = 0, each
+ *                next entry the child of the previous one whose draft token equals the previous node's
+ *                prediction (the lowest index if several siblings carry it); entries past *n_path are -1.
+ *   n_path     : device int32, written: number of nodes on the path (>= 1; accepted drafts = n_path - 1).
+ *   next_token : device int32, written: pred[path[n_path - 1]], the target's own token after the accepted
+ *                prefix.  The step commits tokens[path[1..n_path-1]] followed by next_token.
+ *   status     : device int32, nullable: KDV_OK, or KDV_ERR_TREE for a malformed parent array (the mask's
+ *                rules), in which case the path is the root alone.
+ * Host-side return: KDV_OK, KDV_ERR_NULL (a required pointer is NULL), KDV_ERR_SHAPE (T out of range),
+ * KDV_ERR_ALIGN (a pointer not 4-byte aligned), KDV_ERR_HIP.  Nothing is allocated. */
+int kdv_tree_accept(const int32_t* parent, const int32_t* tokens, const int32_t* pred, int32_t T, int32_t* path,
+                    int32_t* n_path, int32_t* next_token, int32_t* status, void* stream);
+
 /* Bytes of device workspace kdv_verify_mla_attn needs for these dims, tree size T and prefix length L
  * on the current device (the split-KV plan depends on the device's compute-unit count).  Returns 0 if
  * the arguments are unsupported.  The environment variable KDV_SPLITS, if set, overrides the number of

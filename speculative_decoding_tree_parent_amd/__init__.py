@@ -26,7 +26,7 @@ KDV_ERR_WORKSPACE = -5
 KDV_ERR_HIP = -6
 KDV_MAX_TREE_NODES = 64
 
-EXPORTED = ("kdv_build_tree_mask", "kdv_verify_workspace_bytes", "kdv_verify_mla_attn",
+EXPORTED = ("kdv_build_tree_mask", "kdv_tree_accept", "kdv_verify_workspace_bytes", "kdv_verify_mla_attn",
             "kdv_verify_mla_attn_profiled", "kdv_verify_num_splits", "kdv_status_string")
 
 
@@ -50,6 +50,8 @@ def _load() -> ctypes.CDLL:
     dims_p = ctypes.POINTER(KdvMlaDims)
     lib.kdv_build_tree_mask.argtypes = [vp, i32, vp, vp, vp]
     lib.kdv_build_tree_mask.restype = ctypes.c_int
+    lib.kdv_tree_accept.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp, vp]
+    lib.kdv_tree_accept.restype = ctypes.c_int
     lib.kdv_verify_workspace_bytes.argtypes = [dims_p, i32, i32]
     lib.kdv_verify_workspace_bytes.restype = sz
     lib.kdv_verify_num_splits.argtypes = [dims_p, i32, i32]
@@ -70,6 +72,11 @@ _lib = _load()
 # ------------------------------------------------------------------------------------------- C ABI, 1:1
 def kdv_build_tree_mask(parent: int, T: int, mask: int, status: int | None, stream: int | None) -> int:
     return _lib.kdv_build_tree_mask(parent, T, mask, status, stream)
+
+
+def kdv_tree_accept(parent: int, tokens: int, pred: int, T: int, path: int, n_path: int, next_token: int,
+                    status: int | None, stream: int | None) -> int:
+    return _lib.kdv_tree_accept(parent, tokens, pred, T, path, n_path, next_token, status, stream)
 
 
 def kdv_verify_workspace_bytes(dims: KdvMlaDims, T: int, L: int) -> int:
@@ -141,6 +148,24 @@ def build_tree_mask(parent, mask=None, status=None, stream=None):
     if rc != KDV_OK:
         raise KdvError(rc, "kdv_build_tree_mask")
     return mask, status
+
+
+def tree_accept(parent, tokens, pred, stream=None):
+    """parent, tokens, pred: int32 [T] device tensors -> (path int32 [T], n_path, next_token, status: int32 [1])."""
+    import torch
+    T = parent.shape[0]
+    dev = parent.device
+    path = torch.empty((T,), dtype=torch.int32, device=dev)
+    n_path = torch.empty((1,), dtype=torch.int32, device=dev)
+    next_token = torch.empty((1,), dtype=torch.int32, device=dev)
+    status = torch.empty((1,), dtype=torch.int32, device=dev)
+    rc = kdv_tree_accept(_ptr(parent, torch.int32, "parent"), _ptr(tokens, torch.int32, "tokens"),
+                         _ptr(pred, torch.int32, "pred"), T, _ptr(path, torch.int32, "path"),
+                         _ptr(n_path, torch.int32, "n_path"), _ptr(next_token, torch.int32, "next_token"),
+                         _ptr(status, torch.int32, "status"), _stream_handle(stream))
+    if rc != KDV_OK:
+        raise KdvError(rc, "kdv_tree_accept")
+    return path, n_path, next_token, status
 
 
 def verify_workspace_bytes(dims: KdvMlaDims, T: int, L: int) -> int:

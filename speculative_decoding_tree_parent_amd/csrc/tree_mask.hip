@@ -1,3 +1,6 @@
+// Tree utilities of the DDTree verify step: the ancestor bitmask, built before verification, and the greedy
+// acceptance of the verified tree.
+//
 // Ancestor bitmask of a DDTree draft tree.
 //
 // A draft-tree node may attend to the prefix, its ancestors and itself ("The Architecture of
@@ -40,6 +43,47 @@ __global__ __launch_bounds__(64) void tree_mask_kernel(const int32_t* __restrict
   if (i == 0 && status != nullptr) status[0] = any_bad ? KDV_ERR_TREE : KDV_OK;
 }
 
+// Greedy acceptance ("The Architecture of Diagnosis...", section "Phase 1: Custom CUDA Kernels", item 3: after
+// verification the longest prefix of accepted tokens is selected on the device).  Node 0 is the root, whose
+// token is already committed; pred[t] is the target's greedy prediction after the prefix that ends at node t.
+// A child is accepted when its draft token equals its parent's prediction.  One wave, one node per lane:
+// each step every lane checks whether it is an accepted child of the current node, and the lowest such
+// lane (ballot, lowest set bit) becomes the current node.  A path has at most T nodes, so at most T - 1
+// steps.  Malformed trees (the mask's rules) give KDV_ERR_TREE and the root alone.
+__global__ __launch_bounds__(64) void tree_accept_kernel(const int32_t* __restrict__ parent,
+                                                         const int32_t* __restrict__ tokens,
+                                                         const int32_t* __restrict__ pred, int T,
+                                                         int32_t* __restrict__ path, int32_t* __restrict__ n_path,
+                                                         int32_t* __restrict__ next_token,
+                                                         int32_t* __restrict__ status) {
+  const int i = threadIdx.x;
+  const bool live = i < T;
+  const int p = live ? parent[i] : -2;
+  const int tk = live ? tokens[i] : 0;
+  const int pr = live ? pred[i] : 0;
+  const bool valid = !live || (i == 0 ? p == -1 : (p >= 0 && p < i));
+  const bool tree_ok = !__any(!valid);
+  int cur = 0, n = 1;
+  if (tree_ok) {
+    for (int step = 1; step < T; ++step) {  // wave-uniform loop
+      const int want = __shfl(pr, cur);
+      const unsigned long long hits = __ballot(live && p == cur && tk == want);
+      if (hits == 0ull) break;
+      cur = __builtin_ctzll(hits);
+      if (i == 0) path[n] = cur;
+      ++n;
+    }
+  }
+  const int nt = __shfl(pr, cur);
+  if (live && i >= n) path[i] = -1;
+  if (i == 0) {
+    path[0] = 0;
+    n_path[0] = n;
+    next_token[0] = nt;
+    if (status != nullptr) status[0] = tree_ok ? KDV_OK : KDV_ERR_TREE;
+  }
+}
+
 }  // namespace kdv
 
 extern "C" int kdv_build_tree_mask(const int32_t* parent, int32_t T, uint32_t* mask, int32_t* status,
@@ -51,5 +95,19 @@ extern "C" int kdv_build_tree_mask(const int32_t* parent, int32_t T, uint32_t* m
     return KDV_ERR_ALIGN;
   hipLaunchKernelGGL(kdv::tree_mask_kernel, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream), parent, T,
                      mask, status);
+  return hipGetLastError() == hipSuccess ? KDV_OK : KDV_ERR_HIP;
+}
+
+extern "C" int kdv_tree_accept(const int32_t* parent, const int32_t* tokens, const int32_t* pred, int32_t T,
+                               int32_t* path, int32_t* n_path, int32_t* next_token, int32_t* status, void* stream) {
+  if (parent == nullptr || tokens == nullptr || pred == nullptr || path == nullptr || n_path == nullptr ||
+      next_token == nullptr)
+    return KDV_ERR_NULL;
+  if (T < 1 || T > KDV_MAX_TREE_NODES) return KDV_ERR_SHAPE;
+  const void* ptrs[] = {parent, tokens, pred, path, n_path, next_token, status};
+  for (const void* q : ptrs)
+    if (reinterpret_cast<uintptr_t>(q) & 3) return KDV_ERR_ALIGN;
+  hipLaunchKernelGGL(kdv::tree_accept_kernel, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream), parent,
+                     tokens, pred, T, path, n_path, next_token, status);
   return hipGetLastError() == hipSuccess ? KDV_OK : KDV_ERR_HIP;
 }

@@ -127,3 +127,19 @@ def test_package_has_no_cpu_fallback():
     import inspect
     src = inspect.getsource(kdv)
     assert "oracle" not in src.replace("never by the product", "")
+
+
+def test_tree_accept_argument_errors():
+    ok = dict(parent=A, tokens=A, pred=A, T=15, path=A, n_path=A, next_token=A, status=None, stream=None)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return kdv.kdv_tree_accept(a["parent"], a["tokens"], a["pred"], a["T"], a["path"], a["n_path"],
+                                   a["next_token"], a["status"], a["stream"])
+    for field in ("parent", "tokens", "pred", "path", "n_path", "next_token"):
+        assert call(**{field: None}) == kdv.KDV_ERR_NULL, field
+    assert call(T=0) == kdv.KDV_ERR_SHAPE
+    assert call(T=65) == kdv.KDV_ERR_SHAPE
+    for field in ("parent", "tokens", "pred", "path", "n_path", "next_token", "status"):
+        assert call(**{field: A + 2}) == kdv.KDV_ERR_ALIGN, field
