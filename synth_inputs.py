@@ -102,6 +102,26 @@ def accept_inputs(seed: int, T: int, vocab: int = 32000, follow: float = 0.7, du
     return par, tok, pred
 
 
+def draft_topk(seed: int, block: int, K: int, vocab: int = 32000, ties: bool = False) -> tuple[np.ndarray, np.ndarray]:
+    """Seeded drafter output for tree construction: (logp float32 [block][K], tok int32 [block][K]).
+
+    Each position's K log-probabilities are drawn as minus exponential variates and sorted in decreasing
+    order; with ``ties`` they are rounded to multiples of 1/4 so that equal scores occur.  Tokens are distinct
+    within a position.  Draw order: log-probabilities, then tokens, position by position.
+    """
+    rng = np.random.default_rng(seed)
+    logp = np.empty((block, K), dtype=np.float32)
+    tok = np.empty((block, K), dtype=np.int32)
+    for d in range(block):
+        v = -rng.exponential(1.5, size=K)
+        if ties:
+            v = np.round(v * 4.0) / 4.0
+        logp[d] = np.sort(v)[::-1].astype(np.float32)
+    for d in range(block):
+        tok[d] = rng.choice(vocab, size=K, replace=False).astype(np.int32)
+    return logp, tok
+
+
 @dataclass
 class VerifyInputs:
     """One layer's worth of tree-verify inputs (bf16 bit patterns + their exact float32 values)."""
