@@ -45,7 +45,8 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, vendor figure
 COLD_BYTES = 576 << 20
 KERNEL_SOURCES = ("speculative_decoding_tree_parent_amd/csrc/verify.hip",
                   "speculative_decoding_tree_parent_amd/csrc/common.h")
-KERNELS = ("tree_mask_kernel", "q_absorb_kernel", "splitkv_kernel", "combine_up_kernel", "tree_accept_kernel")
+KERNELS = ("tree_mask_kernel", "q_absorb_kernel", "splitkv_kernel", "combine_up_kernel", "tree_accept_kernel",
+           "draft_tree_kernel")
 
 
 def log(msg):
@@ -362,6 +363,19 @@ def run(args, torch, si, kdv, dev, hip, stream, sh):
     accept_us = graph_us(accept_launch)
     torch.cuda.synchronize()
     n_path = int(acc_out[1].item())
+    # best-first draft tree at the session's block 16 / budget 32 (top-8 per position)
+    b_logp, b_tok = si.draft_topk(0, 16, 8)
+    b_in = [torch.from_numpy(b_logp).to(dev), torch.from_numpy(b_tok).to(dev),
+            torch.tensor([7], dtype=torch.int32, device=dev)]
+    b_out = [torch.empty((n,), dtype=torch.int32, device=dev) for n in (32, 32, 1)]
+
+    def build_launch():
+        rc = kdv.kdv_build_draft_tree(b_in[0].data_ptr(), b_in[1].data_ptr(), 16, 8, 32, b_in[2].data_ptr(),
+                                      *[t.data_ptr() for t in b_out], sh)
+        if rc:
+            raise kdv.KdvError(rc, "kdv_build_draft_tree")
+    build_us = graph_us(build_launch)
+    torch.cuda.synchronize()
 
     us_layer_cold = 1e3 * ms_cold / (K * layers_per_step)
     us_layer_hot = 1e3 * ms_hot / (K * layers_per_step)
@@ -402,7 +416,10 @@ def run(args, torch, si, kdv, dev, hip, stream, sh):
                      "work_per_launch_gflop": round(wk["flops_splitkv"] / 1e9, 4)},
         "cpu_baseline": None,
         "next_rows": {"tree_accept": {"us": round(accept_us, 3), "nodes": T, "accepted_path_nodes": n_path,
-                                      "timing": "one HIP graph of 200 launches", "bound": "launch latency"}},
+                                      "timing": "one HIP graph of 200 launches", "bound": "launch latency"},
+                      "draft_tree": {"us": round(build_us, 3), "block": 16, "topk": 8, "budget": 32,
+                                     "nodes": int(b_out[2].item()), "timing": "one HIP graph of 200 launches",
+                                     "bound": "latency of 31 dependent wave-wide selections"}},
     }
 
     if not args.no_cpu_baseline:
@@ -519,7 +536,7 @@ def _read_csv(path):
 def _phases(bench, kernel):
     """Dispatch index ranges of bench.py's phases for one kernel, in launch order."""
     W, K, lps, n = bench["warmup"], bench["steps"], bench["config"]["layers_per_step"], bench["kernel_calls"]
-    if kernel == "tree_accept_kernel":  # only in the launch-timing graphs at the end
+    if kernel in ("tree_accept_kernel", "draft_tree_kernel"):  # only in the launch-timing graphs at the end
         edges = [("warm-up", 0), ("graph cold, upload replay", 0), ("graph cold, timed replay", 0),
                  ("graph hot, upload replay", 0), ("graph hot, timed replay", 0), ("eager cold, kernel events", 0),
                  ("launch-timing graph", 400)]

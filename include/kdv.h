@@ -64,6 +64,31 @@ typedef enum kdv_status {
 } kdv_status;
 
 #define KDV_MAX_TREE_NODES 64
+#define KDV_MAX_DRAFT_ENTRIES 4096 /* block x K entries of the drafter's top-K table */
+
+/* Best-first construction of the draft tree on the device ("The Architecture of Diagnosis...", section
+ * "Phase 1: Custom CUDA Kernels", item 1).
+ *
+ *   logp       : device float32 [block][K]: for each position d of the draft block, the log-probabilities of
+ *                the drafter's K best tokens, in decreasing order (logp[d][0] >= logp[d][1] >= ...; finite
+ *                or -inf, no NaN).  Positions are independent: a root path scores the float32 sum of its
+ *                tokens' log-probabilities, added from the root down.
+ *   tok        : device int32 [block][K], the tokens of logp.
+ *   block, K   : 1 <= block <= 63, 1 <= K <= 64, block * K <= KDV_MAX_DRAFT_ENTRIES.
+ *   budget     : maximum number of tree nodes, root included: 1 <= budget <= 64.
+ *   root_token : device int32: the committed token at the root (e.g. kdv_tree_accept's next_token).
+ *   parent     : device int32 [budget], written: the tree in node order; parent[0] = -1, parent[i] < i.
+ *   tokens     : device int32 [budget], written: tokens[0] = *root_token; a node at depth d >= 1 carries a
+ *                token of position d - 1.  Entries past *n_nodes are -1 in both arrays.
+ *   n_nodes    : device int32, written: min(budget, 1 + nodes of the full K-ary tree of depth block).
+ * Nodes join best-first: the highest-scoring candidate next, ties to the smaller depth, then the smaller
+ * parent index, then the better rank; when a node joins, its next-ranked sibling and its best child become
+ * candidates.  The tree is therefore the budget - 1 best nodes, in non-increasing score order, and its
+ * parent array is valid input for kdv_build_tree_mask.
+ * Host-side return: KDV_OK, KDV_ERR_NULL (a pointer is NULL), KDV_ERR_SHAPE (block, K or budget out of
+ * range), KDV_ERR_ALIGN (a pointer not 4-byte aligned), KDV_ERR_HIP.  Nothing is allocated. */
+int kdv_build_draft_tree(const float* logp, const int32_t* tok, int32_t block, int32_t K, int32_t budget,
+                         const int32_t* root_token, int32_t* parent, int32_t* tokens, int32_t* n_nodes, void* stream);
 
 /* Ancestor bitmask of the draft tree ("visibility mask that reflects the tree structure",
  * "The Architecture of Diagnosis...", section "Phase 1: Custom CUDA Kernels", item 2).

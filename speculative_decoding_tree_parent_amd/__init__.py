@@ -25,8 +25,9 @@ KDV_ERR_ALIGN = -4
 KDV_ERR_WORKSPACE = -5
 KDV_ERR_HIP = -6
 KDV_MAX_TREE_NODES = 64
+KDV_MAX_DRAFT_ENTRIES = 4096
 
-EXPORTED = ("kdv_build_tree_mask", "kdv_tree_accept", "kdv_verify_workspace_bytes", "kdv_verify_mla_attn",
+EXPORTED = ("kdv_build_draft_tree", "kdv_build_tree_mask", "kdv_tree_accept", "kdv_verify_workspace_bytes", "kdv_verify_mla_attn",
             "kdv_verify_mla_attn_profiled", "kdv_verify_num_splits", "kdv_status_string")
 
 
@@ -50,6 +51,8 @@ def _load() -> ctypes.CDLL:
     dims_p = ctypes.POINTER(KdvMlaDims)
     lib.kdv_build_tree_mask.argtypes = [vp, i32, vp, vp, vp]
     lib.kdv_build_tree_mask.restype = ctypes.c_int
+    lib.kdv_build_draft_tree.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, vp, vp]
+    lib.kdv_build_draft_tree.restype = ctypes.c_int
     lib.kdv_tree_accept.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp, vp]
     lib.kdv_tree_accept.restype = ctypes.c_int
     lib.kdv_verify_workspace_bytes.argtypes = [dims_p, i32, i32]
@@ -72,6 +75,11 @@ _lib = _load()
 # ------------------------------------------------------------------------------------------- C ABI, 1:1
 def kdv_build_tree_mask(parent: int, T: int, mask: int, status: int | None, stream: int | None) -> int:
     return _lib.kdv_build_tree_mask(parent, T, mask, status, stream)
+
+
+def kdv_build_draft_tree(logp: int, tok: int, block: int, K: int, budget: int, root_token: int, parent: int,
+                         tokens: int, n_nodes: int, stream: int | None) -> int:
+    return _lib.kdv_build_draft_tree(logp, tok, block, K, budget, root_token, parent, tokens, n_nodes, stream)
 
 
 def kdv_tree_accept(parent: int, tokens: int, pred: int, T: int, path: int, n_path: int, next_token: int,
@@ -148,6 +156,24 @@ def build_tree_mask(parent, mask=None, status=None, stream=None):
     if rc != KDV_OK:
         raise KdvError(rc, "kdv_build_tree_mask")
     return mask, status
+
+
+def build_draft_tree(logp, tok, budget: int, root_token, stream=None):
+    """logp float32 [block][K], tok int32 [block][K], root_token int32 [1] (device tensors)
+    -> (parent int32 [budget], tokens int32 [budget], n_nodes int32 [1])."""
+    import torch
+    block, K = logp.shape
+    dev = logp.device
+    parent = torch.empty((budget,), dtype=torch.int32, device=dev)
+    tokens = torch.empty((budget,), dtype=torch.int32, device=dev)
+    n_nodes = torch.empty((1,), dtype=torch.int32, device=dev)
+    rc = kdv_build_draft_tree(_ptr(logp, torch.float32, "logp"), _ptr(tok, torch.int32, "tok"), block, K, budget,
+                              _ptr(root_token, torch.int32, "root_token"), _ptr(parent, torch.int32, "parent"),
+                              _ptr(tokens, torch.int32, "tokens"), _ptr(n_nodes, torch.int32, "n_nodes"),
+                              _stream_handle(stream))
+    if rc != KDV_OK:
+        raise KdvError(rc, "kdv_build_draft_tree")
+    return parent, tokens, n_nodes
 
 
 def tree_accept(parent, tokens, pred, stream=None):

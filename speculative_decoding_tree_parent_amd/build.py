@@ -16,7 +16,7 @@ import sys
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_PATH = os.path.join(PKG_DIR, "libkdv.so")
-SOURCES = ["tree_mask.hip", "verify.hip"]
+SOURCES = ["tree.hip", "verify.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

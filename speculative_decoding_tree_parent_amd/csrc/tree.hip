@@ -1,5 +1,5 @@
-// Tree utilities of the DDTree verify step: the ancestor bitmask, built before verification, and the greedy
-// acceptance of the verified tree.
+// Tree utilities of the DDTree verify step: best-first construction of the draft tree, the ancestor bitmask
+// built before verification, and the greedy acceptance of the verified tree.
 //
 // Ancestor bitmask of a DDTree draft tree.
 //
@@ -41,6 +41,103 @@ __global__ __launch_bounds__(64) void tree_mask_kernel(const int32_t* __restrict
   }
   const bool any_bad = __any(!valid);
   if (i == 0 && status != nullptr) status[0] = any_bad ? KDV_ERR_TREE : KDV_OK;
+}
+
+// Best-first construction of the draft tree ("The Architecture of Diagnosis...", section "Phase 1: Custom
+// CUDA Kernels", item 1: the tree is built on the device instead of with a host-side priority queue).
+// The drafter gives, per position d of the block, its K best tokens tok[d][r] with log-probabilities
+// logp[d][r] sorted in decreasing order.  Node 0 is the root (the committed token); a node at depth d >= 1
+// takes a token of position d - 1 and scores its parent's score plus that token's log-probability (float32).
+// The candidate with the highest score joins next (ties: smaller depth, then parent index, then rank); when a
+// node joins, its next sibling (rank + 1) and its first child (rank 0, depth + 1) become candidates.
+//
+// One wave; lane j holds candidate slot j and, once node j exists, node j's score.  Each step the best
+// candidate is found by a 64-bit max over (orderable score bits, 63 - depth, 63 - parent, 63 - rank), which is
+// unique per candidate.  Every step removes one candidate and adds at most two, so at most budget <= 64 slots
+// are ever in use; the new sibling takes the winner's slot and the new child the lowest free slot.
+__device__ __forceinline__ uint32_t orderable(float f) {
+  const uint32_t u = __float_as_uint(f + 0.f);  // -0 -> +0: equal scores compare equal
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const uint32_t lo = __shfl_xor((uint32_t)v, off), hi = __shfl_xor((uint32_t)(v >> 32), off);
+    const unsigned long long o = ((unsigned long long)hi << 32) | lo;
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+__global__ __launch_bounds__(64) void draft_tree_kernel(const float* __restrict__ logp,
+                                                        const int32_t* __restrict__ tok, int block, int K,
+                                                        int budget, const int32_t* __restrict__ root_token,
+                                                        int32_t* __restrict__ parent, int32_t* __restrict__ tokens,
+                                                        int32_t* __restrict__ n_nodes) {
+  __shared__ float s_logp[KDV_MAX_DRAFT_ENTRIES];
+  __shared__ int32_t s_tok[KDV_MAX_DRAFT_ENTRIES];
+  const int j = threadIdx.x;
+  for (int e = j; e < block * K; e += 64) {
+    s_logp[e] = logp[e];
+    s_tok[e] = tok[e];
+  }
+  __syncthreads();
+  // candidate in this slot
+  bool cand = false;
+  float c_score = 0.f;
+  int c_depth = 0, c_parent = 0, c_rank = 0;
+  // node j (once it exists)
+  float n_score = 0.f;
+  int n_parent = -1, n_token = 0;
+  if (j == 0) {
+    n_token = root_token[0];
+    if (budget > 1) {  // first candidate: best token of position 0
+      cand = true;
+      c_score = 0.f + s_logp[0];
+      c_depth = 1;
+    }
+  }
+  int n = 1;
+  for (; n < budget; ++n) {  // wave-uniform loop, at most budget - 1 <= 63 steps
+    const unsigned long long key =
+        cand ? ((unsigned long long)orderable(c_score) << 32) |
+                   (uint32_t)(((63 - c_depth) << 12) | ((63 - c_parent) << 6) | (63 - c_rank))
+             : 0ull;
+    const unsigned long long best = wave_max_u64(key);
+    if (best == 0ull) break;  // no candidate left: the whole K-ary tree of depth block is in
+    const int w = __builtin_ctzll(__ballot(cand && key == best));
+    const float s = __shfl(c_score, w);
+    const int d = __shfl(c_depth, w), p = __shfl(c_parent, w), r = __shfl(c_rank, w);
+    const float ps = __shfl(n_score, p);  // parent's score, for the sibling
+    if (j == n) {  // node n joins
+      n_score = s;
+      n_parent = p;
+      n_token = s_tok[(d - 1) * K + r];
+    }
+    if (j == w) {  // the winner's slot takes its next sibling, if any
+      cand = r + 1 < K;
+      if (cand) {
+        c_score = ps + s_logp[(d - 1) * K + r + 1];
+        c_rank = r + 1;
+      }
+    }
+    if (d < block) {  // first child of node n, in the lowest free slot
+      const int f = __builtin_ctzll(__ballot(!cand));
+      if (j == f) {
+        cand = true;
+        c_score = s + s_logp[d * K];
+        c_depth = d + 1;
+        c_parent = n;
+        c_rank = 0;
+      }
+    }
+  }
+  if (j < budget) {
+    parent[j] = j < n ? n_parent : -1;
+    tokens[j] = j < n ? n_token : -1;
+  }
+  if (j == 0) n_nodes[0] = n;
 }
 
 // Greedy acceptance ("The Architecture of Diagnosis...", section "Phase 1: Custom CUDA Kernels", item 3: after
@@ -109,5 +206,22 @@ extern "C" int kdv_tree_accept(const int32_t* parent, const int32_t* tokens, con
     if (reinterpret_cast<uintptr_t>(q) & 3) return KDV_ERR_ALIGN;
   hipLaunchKernelGGL(kdv::tree_accept_kernel, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream), parent,
                      tokens, pred, T, path, n_path, next_token, status);
+  return hipGetLastError() == hipSuccess ? KDV_OK : KDV_ERR_HIP;
+}
+
+extern "C" int kdv_build_draft_tree(const float* logp, const int32_t* tok, int32_t block, int32_t K, int32_t budget,
+                                    const int32_t* root_token, int32_t* parent, int32_t* tokens, int32_t* n_nodes,
+                                    void* stream) {
+  if (logp == nullptr || tok == nullptr || root_token == nullptr || parent == nullptr || tokens == nullptr ||
+      n_nodes == nullptr)
+    return KDV_ERR_NULL;
+  if (block < 1 || block > 63 || K < 1 || K > 64 || block * K > KDV_MAX_DRAFT_ENTRIES || budget < 1 ||
+      budget > KDV_MAX_TREE_NODES)
+    return KDV_ERR_SHAPE;
+  const void* ptrs[] = {logp, tok, root_token, parent, tokens, n_nodes};
+  for (const void* q : ptrs)
+    if (reinterpret_cast<uintptr_t>(q) & 3) return KDV_ERR_ALIGN;
+  hipLaunchKernelGGL(kdv::draft_tree_kernel, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream), logp, tok,
+                     block, K, budget, root_token, parent, tokens, n_nodes);
   return hipGetLastError() == hipSuccess ? KDV_OK : KDV_ERR_HIP;
 }

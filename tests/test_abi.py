@@ -143,3 +143,19 @@ def test_tree_accept_argument_errors():
     assert call(T=65) == kdv.KDV_ERR_SHAPE
     for field in ("parent", "tokens", "pred", "path", "n_path", "next_token", "status"):
         assert call(**{field: A + 2}) == kdv.KDV_ERR_ALIGN, field
+
+
+def test_build_draft_tree_argument_errors():
+    ok = dict(logp=A, tok=A, block=16, K=8, budget=32, root=A, parent=A, tokens=A, n=A)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return kdv.kdv_build_draft_tree(a["logp"], a["tok"], a["block"], a["K"], a["budget"], a["root"],
+                                        a["parent"], a["tokens"], a["n"], None)
+    for field in ("logp", "tok", "root", "parent", "tokens", "n"):
+        assert call(**{field: None}) == kdv.KDV_ERR_NULL, field
+    for bad in (dict(block=0), dict(block=64), dict(K=0), dict(K=65), dict(budget=0), dict(budget=65)):
+        assert call(**bad) == kdv.KDV_ERR_SHAPE, bad
+    for field in ("logp", "tok", "root", "parent", "tokens", "n"):
+        assert call(**{field: A + 1}) == kdv.KDV_ERR_ALIGN, field
