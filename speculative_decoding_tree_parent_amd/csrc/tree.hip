@@ -52,22 +52,28 @@ __global__ __launch_bounds__(64) void tree_mask_kernel(const int32_t* __restrict
 // node joins, its next sibling (rank + 1) and its first child (rank 0, depth + 1) become candidates.
 //
 // One wave; lane j holds candidate slot j and, once node j exists, node j's score.  Each step the best
-// candidate is found by a 64-bit max over (orderable score bits, 63 - depth, 63 - parent, 63 - rank), which is
-// unique per candidate.  Every step removes one candidate and adds at most two, so at most budget <= 64 slots
+// candidate is found by a wave-wide max of its orderable score bits and, only on an exact tie, a min of
+// (depth, parent, rank), which is unique per candidate.  Every step removes one candidate and adds at most two, so at most budget <= 64 slots
 // are ever in use; the new sibling takes the winner's slot and the new child the lowest free slot.
 __device__ __forceinline__ uint32_t orderable(float f) {
   const uint32_t u = __float_as_uint(f + 0.f);  // -0 -> +0: equal scores compare equal
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const uint32_t lo = __shfl_xor((uint32_t)v, off), hi = __shfl_xor((uint32_t)(v >> 32), off);
-    const unsigned long long o = ((unsigned long long)hi << 32) | lo;
-    v = o > v ? o : v;
-  }
-  return v;
+// Wave-wide unsigned max / min with DPP row shifts and row broadcasts (no LDS permutes): lane i first takes
+// the extreme of lanes [row start, i] of its 16-lane row (shifts by 1, 2, 4, 8), then rows 1 and 3 fold in
+// rows 0 and 2 (broadcast of lane 15), then rows 2 and 3 fold in row 1 (broadcast of lane 31); lane 63 ends
+// up with the wave's extreme.  A lane whose source is outside its row keeps its own value.
+template <bool MAX>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v) {
+  auto step = [&](uint32_t x, uint32_t y) { return MAX ? (x > y ? x : y) : (x < y ? x : y); };
+  v = step(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x111, 0xf, 0xf, false));  // row_shr:1
+  v = step(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x112, 0xf, 0xf, false));  // row_shr:2
+  v = step(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x114, 0xf, 0xf, false));  // row_shr:4
+  v = step(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x118, 0xf, 0xf, false));  // row_shr:8
+  v = step(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x142, 0xa, 0xf, false));  // row_bcast:15
+  v = step(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x143, 0xc, 0xf, false));  // row_bcast:31
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
 __global__ __launch_bounds__(64) void draft_tree_kernel(const float* __restrict__ logp,
@@ -100,16 +106,23 @@ __global__ __launch_bounds__(64) void draft_tree_kernel(const float* __restrict_
   }
   int n = 1;
   for (; n < budget; ++n) {  // wave-uniform loop, at most budget - 1 <= 63 steps
-    const unsigned long long key =
-        cand ? ((unsigned long long)orderable(c_score) << 32) |
-                   (uint32_t)(((63 - c_depth) << 12) | ((63 - c_parent) << 6) | (63 - c_rank))
-             : 0ull;
-    const unsigned long long best = wave_max_u64(key);
-    if (best == 0ull) break;  // no candidate left: the whole K-ary tree of depth block is in
-    const int w = __builtin_ctzll(__ballot(cand && key == best));
-    const float s = __shfl(c_score, w);
-    const int d = __shfl(c_depth, w), p = __shfl(c_parent, w), r = __shfl(c_rank, w);
-    const float ps = __shfl(n_score, p);  // parent's score, for the sibling
+    // best candidate: highest score, then smaller (depth, parent, rank); candidates have keys >= 1
+    const uint32_t skey = cand ? orderable(c_score) : 0u;
+    const uint32_t smax = wave_reduce_u32<true>(skey);
+    if (smax == 0u) break;  // no candidate left: the whole K-ary tree of depth block is in
+    const unsigned long long top = __ballot(cand && skey == smax);
+    if (top == 0ull) break;  // (cannot happen: smax is some candidate's key)
+    int w = __builtin_ctzll(top);
+    if (top & (top - 1)) {  // equal scores: the tie key decides (unique per candidate)
+      const uint32_t tkey = (cand && skey == smax) ? (uint32_t)((c_depth << 12) | (c_parent << 6) | c_rank)
+                                                   : 0xffffffffu;
+      const uint32_t tmin = wave_reduce_u32<false>(tkey);
+      w = __builtin_ctzll(__ballot(tkey == tmin));
+    }
+    const float s = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c_score), w));
+    const int d = __builtin_amdgcn_readlane(c_depth, w), p = __builtin_amdgcn_readlane(c_parent, w);
+    const int r = __builtin_amdgcn_readlane(c_rank, w);
+    const float ps = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(n_score), p));  // parent's score
     if (j == n) {  // node n joins
       n_score = s;
       n_parent = p;
