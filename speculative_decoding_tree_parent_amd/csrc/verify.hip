@@ -91,7 +91,19 @@ __device__ __forceinline__ void dma16_lane_addr(const void* vaddr, uint32_t lds_
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(vaddr), "s"(lds_addr)
                : "memory", "m0");
 }
+// 4 bytes per lane: lane l's word lands at lds_addr + 4 l.
+__device__ __forceinline__ void dma4_lane_addr(const void* vaddr, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(vaddr), "s"(lds_addr)
+               : "memory", "m0");
+}
 #pragma clang diagnostic pop
+// Wait until at most N vector-memory loads of this wave are outstanding.  Loads complete in issue order, so
+// this covers every load issued before the last N (the compiler's own waits do not count the DMA asm).
+template <int N>
+__device__ __forceinline__ void wait_vmem_below() {
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 __device__ __forceinline__ uint32_t lds_address(const void* p) {
   return (uint32_t)(size_t)(const __attribute__((address_space(3))) char*)(p);
 }
@@ -175,7 +187,7 @@ __device__ __forceinline__ void tile_compute(const char* tile, const bf16x8 (&q)
                                              float (*mxch)[2][32], float (*psum)[2][32], int wi, int wj, int wave,
                                              int lane, const TileDma<R, DR>& dma, bool dma_on) {
   using TL = TileLayout<R, DR>;
-  constexpr int KB = (R + DR) / 16, DB = R / 64;
+  constexpr int KB = (R + DR) / 16;
   const int g = lane >> 5, c = lane & 31;
   // ---- scores S^T[n][m] for tile rows n = wj*32 + (r/4)*8 + g*4 + r%4
   // The swizzle only touches the low log2(F) bits of a chunk index, so a row's fragment offsets repeat with
@@ -366,7 +378,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void splitkv_kernel(
     int m_tiles, int tiles_per_split, int num_splits, float scale_log2, uint16_t* __restrict__ part_o,
     float2* __restrict__ part_ml, int Mp) {
   using TL = TileLayout<R, DR>;
-  constexpr int DQ = R + DR, KB = DQ / 16, DB = R / 64;
+  constexpr int DQ = R + DR, KB = DQ / 16;
   __shared__ __attribute__((aligned(1024))) char kvbuf[2 * TL::BYTES];
   __shared__ uint4 pbuf[2][2][2][64];  // [row block][kv half][16-row k-step][lane]: P^T fragments (bf16)
   __shared__ float mxch[2][2][32];     // [row block][kv half][row]: proposed reference
@@ -388,17 +400,20 @@ __global__ __launch_bounds__(NTHREADS, 1) void splitkv_kernel(
   const int tile_begin = split * tiles_per_split;
   const int tile_end = min(tile_begin + tiles_per_split, ntiles);
 
-  // Prologue.  The query tile (64 rows of q_cat) is gathered once per workgroup by DMA into the second KV
-  // buffer, which is idle until the loop's first iteration, while the first tile's page-table slice and the
-  // mask words load; the first tile's gather follows the page-table slice.  Each wave then reads its query
-  // fragments from LDS.  (Each DMA asm clobbers memory, so no load is moved past it.)
-  // Padding rows (m >= M) repeat the last real row; their partials are never read.
+  // Prologue.  Each wave first gathers the first tile's page-table slice by DMA into its own 256 bytes of the
+  // (still idle) exchange buffer; the mask words load; then the query tile (64 rows of q_cat) is gathered by
+  // DMA into the second KV buffer, which is idle until the loop's first iteration.  A counted wait lets the
+  // page-table slice land without waiting for the query tile, and the first tile's gather goes out behind it.
+  // Each wave then reads its query fragments from LDS.  (Each DMA asm clobbers memory, so no load or LDS
+  // access is moved past it.)  Padding rows (m >= M) repeat the last real row; their partials are never read.
   const int me = min(m, M - 1);
-  const int slot0 = page_table[min(tile_begin * KV_TILE + lane, N - 1)];  // rows past N reuse a real row (masked)
-  const int t_row = me / H, W = (T + 31) >> 5;
+  int* pt_s = reinterpret_cast<int*>(&pbuf[0][0][0][0]) + wave * 64;
+  dma4_lane_addr(page_table + min(tile_begin * KV_TILE + lane, N - 1), lds_address(pt_s));  // rows past N reuse
+  const int t_row = me / H, W = (T + 31) >> 5;                                              // a real row (masked)
   const uint32_t mw0 = mask[t_row * W];
   const uint32_t mw1 = (W == 2) ? mask[t_row * W + 1] : 0u;
   char* qbuf = kvbuf + TL::BYTES;
+  constexpr int QINS = (M_TILE * (DQ / 8) + 63) / 64;  // query-tile DMA instructions (all waves)
   {
     // LDS holds the tile's rows back to back, DQ/8 chunks each; within aligned groups of 8 chunks, chunk ch of
     // row r sits at position ch ^ ((r >> 1) & 7), so the 16 rows a quarter-wave reads at one chunk fall in 16
@@ -417,6 +432,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void splitkv_kernel(
       }
     }
   }
+  wait_vmem_below<QINS / 4>();  // every wave issued at least QINS / 4 query-tile loads after its page-table load
+  const int slot0 = pt_s[lane];
   TileDma<R, DR> dma(c_kv, k_pe, wave, lane);
   dma.target(kvbuf, slot0);
 #pragma unroll
