@@ -171,6 +171,38 @@ int kdv_verify_mla_attn_profiled(const kdv_mla_dims* d, const uint16_t* q_nope, 
                                  int32_t T, const uint32_t* mask, uint16_t* out, float* lse, void* workspace,
                                  size_t workspace_bytes, void* stream, void* const* events);
 
+/* Prefix part of a split verify step: the pages' production arrangement gives the long prefix to a dense MLA
+ * decode kernel and only the small tree tail to the tree kernel ("The Three Acts of Engineering: Diagnosis,
+ * Extension, and Analytical Pivot in a Speculative Decoding Stack", section "References", item [1]).
+ * Every query row (t, h) attends to all L prefix positions and to nothing else: no tree rows, no mask.
+ * Arguments as kdv_verify_mla_attn, except:
+ *   page_table : device int32 [L] (prefix positions only).
+ *   L          : >= 1.
+ *   lse        : nullable as before, but the merge below needs it.
+ *   workspace  : kdv_verify_workspace_bytes(d, T, L) bytes always suffice.
+ * The tail part is kdv_verify_mla_attn with L = 0 and a page table of the T tree rows; the two results
+ * combine with kdv_merge_attn_states into the result of one kdv_verify_mla_attn over the whole cache.
+ * Returns KDV_OK or a negative kdv_status (KDV_ERR_SHAPE for L < 1; nothing enqueued on error). */
+int kdv_prefix_mla_attn(const kdv_mla_dims* d, const uint16_t* q_nope, const uint16_t* q_rope, const uint16_t* w_uk,
+                        const uint16_t* w_uv, const uint16_t* c_kv, const uint16_t* k_pe, int64_t pool_slots,
+                        const int32_t* page_table, int32_t L, int32_t T, uint16_t* out, float* lse, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/* Merge of two attention results over disjoint sets of KV positions into the result over their union (the
+ * merge that joins the prefix and tree-tail parts above; the same operator merges the KV splits inside
+ * kdv_verify_mla_attn).  For each row r, with M = max(lse_a[r], lse_b[r]) and w_x = exp(lse_x[r] - M):
+ *   out[r] = (w_a out_a[r] + w_b out_b[r]) / (w_a + w_b),   lse[r] = M + ln(w_a + w_b).
+ * A part with lse = -inf (it saw no position) has weight 0; if both do, out[r] = 0 and lse[r] = -inf.
+ *   out_a, out_b : device bf16 [rows][dv], 16-byte aligned (e.g. two kdv_*_mla_attn outputs, rows = T*H).
+ *   lse_a, lse_b : device fp32 [rows] (natural log, as the attention entry points write it).
+ *   rows, dv     : rows >= 1; 8 <= dv <= 4096, dv % 8 == 0.
+ *   out          : device bf16 [rows][dv], written; lse: device fp32 [rows], nullable, written.  Neither may
+ *                  overlap an input.
+ * Arithmetic in fp32 from the bf16 inputs, out rounded to bf16 (nearest even).
+ * Host-side return: KDV_OK, KDV_ERR_NULL, KDV_ERR_SHAPE, KDV_ERR_ALIGN, KDV_ERR_HIP.  Nothing is allocated. */
+int kdv_merge_attn_states(const uint16_t* out_a, const float* lse_a, const uint16_t* out_b, const float* lse_b,
+                          int64_t rows, int32_t dv, uint16_t* out, float* lse, void* stream);
+
 /* Number of KV splits kdv_verify_mla_attn will use for these arguments on the current device
  * (diagnostic; 0 if unsupported). */
 int32_t kdv_verify_num_splits(const kdv_mla_dims* d, int32_t T, int32_t L);

@@ -27,8 +27,9 @@ KDV_ERR_HIP = -6
 KDV_MAX_TREE_NODES = 64
 KDV_MAX_DRAFT_ENTRIES = 4096
 
-EXPORTED = ("kdv_build_draft_tree", "kdv_build_tree_mask", "kdv_tree_accept", "kdv_verify_workspace_bytes", "kdv_verify_mla_attn",
-            "kdv_verify_mla_attn_profiled", "kdv_verify_num_splits", "kdv_status_string")
+EXPORTED = ("kdv_build_draft_tree", "kdv_build_tree_mask", "kdv_merge_attn_states", "kdv_prefix_mla_attn",
+            "kdv_tree_accept", "kdv_verify_workspace_bytes", "kdv_verify_mla_attn", "kdv_verify_mla_attn_profiled",
+            "kdv_verify_num_splits", "kdv_status_string")
 
 
 class KdvMlaDims(ctypes.Structure):
@@ -64,6 +65,10 @@ def _load() -> ctypes.CDLL:
     lib.kdv_verify_mla_attn_profiled.argtypes = [dims_p, vp, vp, vp, vp, vp, vp, i64, vp, i32, i32, vp, vp, vp, vp,
                                                  sz, vp, vp]
     lib.kdv_verify_mla_attn_profiled.restype = ctypes.c_int
+    lib.kdv_prefix_mla_attn.argtypes = [dims_p, vp, vp, vp, vp, vp, vp, i64, vp, i32, i32, vp, vp, vp, sz, vp]
+    lib.kdv_prefix_mla_attn.restype = ctypes.c_int
+    lib.kdv_merge_attn_states.argtypes = [vp, vp, vp, vp, i64, i32, vp, vp, vp]
+    lib.kdv_merge_attn_states.restype = ctypes.c_int
     lib.kdv_status_string.argtypes = [ctypes.c_int]
     lib.kdv_status_string.restype = ctypes.c_char_p
     return lib
@@ -110,6 +115,18 @@ def kdv_verify_mla_attn_profiled(dims: KdvMlaDims, q_nope: int, q_rope: int, w_u
     return _lib.kdv_verify_mla_attn_profiled(ctypes.byref(dims), q_nope, q_rope, w_uk, w_uv, c_kv, k_pe, pool_slots,
                                              page_table, L, T, mask, out, lse, workspace, workspace_bytes, stream,
                                              events)
+
+
+def kdv_prefix_mla_attn(dims: KdvMlaDims, q_nope: int, q_rope: int, w_uk: int, w_uv: int, c_kv: int, k_pe: int,
+                        pool_slots: int, page_table: int, L: int, T: int, out: int, lse: int | None, workspace: int,
+                        workspace_bytes: int, stream: int | None) -> int:
+    return _lib.kdv_prefix_mla_attn(ctypes.byref(dims), q_nope, q_rope, w_uk, w_uv, c_kv, k_pe, pool_slots,
+                                    page_table, L, T, out, lse, workspace, workspace_bytes, stream)
+
+
+def kdv_merge_attn_states(out_a: int, lse_a: int, out_b: int, lse_b: int, rows: int, dv: int, out: int,
+                          lse: int | None, stream: int | None) -> int:
+    return _lib.kdv_merge_attn_states(out_a, lse_a, out_b, lse_b, rows, dv, out, lse, stream)
 
 
 def kdv_status_string(status: int) -> str:
@@ -226,4 +243,56 @@ def verify_mla_attn(dims: KdvMlaDims, q_nope, q_rope, w_uk, w_uv, c_kv, k_pe, pa
                              _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream_handle(stream))
     if rc != KDV_OK:
         raise KdvError(rc, "kdv_verify_mla_attn")
+    return out, lse
+
+
+def prefix_mla_attn(dims: KdvMlaDims, q_nope, q_rope, w_uk, w_uv, c_kv, k_pe, page_table, L: int, out=None,
+                    lse=None, workspace=None, stream=None):
+    """Prefix part of a split verify step: every (node, head) row over the L prefix positions only.
+
+    page_table: int32 [L] device tensor.  Returns (out [T][H][Dv] bf16, lse [T][H] fp32)."""
+    import torch
+    T = q_nope.shape[0]
+    H = dims.num_heads
+
+    def bf(t, what):
+        if t.dtype == torch.bfloat16:
+            return _ptr(t, torch.bfloat16, what)
+        return _ptr(t, torch.int16, what)
+
+    if out is None:
+        out = torch.empty((T, H, dims.v_head_dim), dtype=torch.bfloat16, device=q_nope.device)
+    if lse is None:
+        lse = torch.empty((T, H), dtype=torch.float32, device=q_nope.device)
+    if workspace is None:
+        workspace = torch.empty((verify_workspace_bytes(dims, T, L),), dtype=torch.uint8, device=q_nope.device)
+    rc = kdv_prefix_mla_attn(dims, bf(q_nope, "q_nope"), bf(q_rope, "q_rope"), bf(w_uk, "w_uk"), bf(w_uv, "w_uv"),
+                             bf(c_kv, "c_kv"), bf(k_pe, "k_pe"), c_kv.shape[0],
+                             _ptr(page_table, torch.int32, "page_table"), L, T, bf(out, "out"),
+                             _ptr(lse, torch.float32, "lse"), _ptr(workspace, torch.uint8, "workspace"),
+                             workspace.numel(), _stream_handle(stream))
+    if rc != KDV_OK:
+        raise KdvError(rc, "kdv_prefix_mla_attn")
+    return out, lse
+
+
+def merge_attn_states(out_a, lse_a, out_b, lse_b, out=None, lse=None, stream=None):
+    """LSE merge of two attention results over disjoint KV position sets.
+
+    out_a, out_b: bf16 [..., dv]; lse_a, lse_b: fp32 [...] (same leading shape).  Returns (out, lse)."""
+    import torch
+    dv = out_a.shape[-1]
+    rows = lse_a.numel()
+    if out_b.shape != out_a.shape or lse_b.shape != lse_a.shape or out_a.numel() != rows * dv:
+        raise ValueError("merge_attn_states: shapes of the two parts differ")
+    if out is None:
+        out = torch.empty_like(out_a)
+    if lse is None:
+        lse = torch.empty_like(lse_a)
+    rc = kdv_merge_attn_states(_ptr(out_a, torch.bfloat16, "out_a"), _ptr(lse_a, torch.float32, "lse_a"),
+                               _ptr(out_b, torch.bfloat16, "out_b"), _ptr(lse_b, torch.float32, "lse_b"), rows, dv,
+                               _ptr(out, torch.bfloat16, "out"), _ptr(lse, torch.float32, "lse"),
+                               _stream_handle(stream))
+    if rc != KDV_OK:
+        raise KdvError(rc, "kdv_merge_attn_states")
     return out, lse

@@ -410,8 +410,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void splitkv_kernel(
   int* pt_s = reinterpret_cast<int*>(&pbuf[0][0][0][0]) + wave * 64;
   dma4_lane_addr(page_table + min(tile_begin * KV_TILE + lane, N - 1), lds_address(pt_s));  // rows past N reuse
   const int t_row = me / H, W = (T + 31) >> 5;                                              // a real row (masked)
-  const uint32_t mw0 = mask[t_row * W];
-  const uint32_t mw1 = (W == 2) ? mask[t_row * W + 1] : 0u;
+  const bool tree_rows = N > L;  // (a prefix-only pass has no tree rows and no mask)
+  const uint32_t mw0 = tree_rows ? mask[t_row * W] : 0u;
+  const uint32_t mw1 = (tree_rows && W == 2) ? mask[t_row * W + 1] : 0u;
   char* qbuf = kvbuf + TL::BYTES;
   constexpr int QINS = (M_TILE * (DQ / 8) + 63) / 64;  // query-tile DMA instructions (all waves)
   {
@@ -728,6 +729,43 @@ __global__ __launch_bounds__(NTHREADS) void combine_up_kernel(const uint16_t* __
   }
 }
 
+// ------------------------------------------------------------------------------------------------ state merge
+// Two attention results over disjoint sets of KV positions, (out_a, lse_a) and (out_b, lse_b), combine into
+// the result over their union.  With M = max(lse_a, lse_b) and w_x = e^(lse_x - M) (each part's softmax
+// denominator relative to a common reference):
+//   out = (w_a out_a + w_b out_b) / (w_a + w_b),   lse = M + ln(w_a + w_b).
+// This is the split merge of the combine step with two parts; it is exact (up to rounding) whether the parts'
+// outputs are latent rows or their W_UV projections, since W_UV is linear.  A part that saw no position has
+// lse = -inf and weight 0; if neither did, out = 0 and lse = -inf.  One thread per 8 output elements.
+__global__ __launch_bounds__(NTHREADS) void merge_states_kernel(const uint16_t* __restrict__ out_a,
+                                                                const float* __restrict__ lse_a,
+                                                                const uint16_t* __restrict__ out_b,
+                                                                const float* __restrict__ lse_b, int64_t chunks,
+                                                                int cpr, uint16_t* __restrict__ out,
+                                                                float* __restrict__ lse) {
+  const int64_t idx = (int64_t)blockIdx.x * NTHREADS + threadIdx.x;
+  if (idx >= chunks) return;
+  const int64_t r = idx / cpr;
+  const float la = lse_a[r], lb = lse_b[r];
+  const float M = fmaxf(la, lb);
+  bf16x8 o;
+  float lo = -INFINITY;
+  if (M == -INFINITY) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = (__bf16)0.f;
+  } else {
+    const float wa = expf(la - M), wb = expf(lb - M);  // a part with lse = -inf gets weight 0
+    const float inv = 1.f / (wa + wb);
+    const bf16x8 a = *reinterpret_cast<const bf16x8*>(out_a + idx * 8);
+    const bf16x8 b = *reinterpret_cast<const bf16x8*>(out_b + idx * 8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = (__bf16)((wa * (float)a[e] + wb * (float)b[e]) * inv);
+    lo = M + logf(wa + wb);
+  }
+  *reinterpret_cast<bf16x8*>(out + idx * 8) = o;
+  if (lse != nullptr && idx % cpr == 0) lse[r] = lo;
+}
+
 // ------------------------------------------------------------------------------------------------ host side
 struct Plan {
   int H, M, Mp, m_tiles, N, ntiles, tiles_per_split, splits;
@@ -754,9 +792,9 @@ static int device_cu_count() {
   return cus;
 }
 
-// Split the KV sequence so that (query tiles x splits) fills the device once; every split gets the
-// same whole number of 64-row tiles except possibly the last.
-static int make_plan(const kdv_mla_dims* d, int T, int L, Plan* p) {
+// Split the KV sequence (L prefix rows, then `kv_tree` = T or 0 tree rows) so that (query tiles x splits) fills
+// the device once; every split gets the same whole number of 64-row tiles except possibly the last.
+static int make_plan(const kdv_mla_dims* d, int T, int L, Plan* p, bool with_tree = true) {
   if (d == nullptr) return KDV_ERR_NULL;
   if (shape_of(d) == SHAPE_NONE) return KDV_ERR_SHAPE;
   if (T < 1 || T > KDV_MAX_TREE_NODES || L < 0 || (int64_t)L + T > 0x7fffff00LL) return KDV_ERR_SHAPE;
@@ -764,7 +802,8 @@ static int make_plan(const kdv_mla_dims* d, int T, int L, Plan* p) {
   p->M = T * d->num_heads;
   p->m_tiles = (p->M + M_TILE - 1) / M_TILE;
   p->Mp = p->m_tiles * M_TILE;
-  p->N = L + T;
+  p->N = L + (with_tree ? T : 0);
+  if (p->N < 1) return KDV_ERR_SHAPE;
   p->ntiles = (p->N + KV_TILE - 1) / KV_TILE;
   int want = 0;
   if (const char* env = getenv("KDV_SPLITS")) want = atoi(env);
@@ -840,20 +879,21 @@ static int verify_impl(const kdv_mla_dims* d, const uint16_t* q_nope, const uint
                        const uint16_t* w_uk, const uint16_t* w_uv, const uint16_t* c_kv, const uint16_t* k_pe,
                        int64_t pool_slots, const int32_t* page_table, int32_t L, int32_t T, const uint32_t* mask,
                        uint16_t* out, float* lse, void* workspace, size_t workspace_bytes, void* stream,
-                       hipEvent_t const* ev) {
+                       hipEvent_t const* ev, bool with_tree = true) {
   using namespace kdv;
   if (d == nullptr || q_nope == nullptr || q_rope == nullptr || w_uk == nullptr || w_uv == nullptr ||
-      c_kv == nullptr || k_pe == nullptr || page_table == nullptr || mask == nullptr || out == nullptr ||
-      workspace == nullptr)
+      c_kv == nullptr || k_pe == nullptr || page_table == nullptr || (with_tree && mask == nullptr) ||
+      out == nullptr || workspace == nullptr)
     return KDV_ERR_NULL;
   const ShapeId sid = shape_of(d);
-  if (sid == SHAPE_NONE || pool_slots < 1 || T < 1 || T > KDV_MAX_TREE_NODES || L < 0) return KDV_ERR_SHAPE;
+  if (sid == SHAPE_NONE || pool_slots < 1 || T < 1 || T > KDV_MAX_TREE_NODES || L < (with_tree ? 0 : 1))
+    return KDV_ERR_SHAPE;
   if (misaligned(q_nope, 16) || misaligned(q_rope, 16) || misaligned(w_uk, 16) || misaligned(w_uv, 16) ||
       misaligned(c_kv, 16) || misaligned(k_pe, 16) || misaligned(out, 16) || misaligned(workspace, 16) ||
       misaligned(page_table, 4) || misaligned(mask, 4) || misaligned(lse, 4))
     return KDV_ERR_ALIGN;
   Plan pl;
-  const int st = make_plan(d, T, L, &pl);
+  const int st = make_plan(d, T, L, &pl, with_tree);
   if (st != KDV_OK) return st;
   if (workspace_bytes < pl.total) return KDV_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -886,6 +926,33 @@ extern "C" int kdv_verify_mla_attn_profiled(const kdv_mla_dims* d, const uint16_
   if (events == nullptr) return KDV_ERR_NULL;
   return verify_impl(d, q_nope, q_rope, w_uk, w_uv, c_kv, k_pe, pool_slots, page_table, L, T, mask, out, lse,
                      workspace, workspace_bytes, stream, reinterpret_cast<hipEvent_t const*>(events));
+}
+
+extern "C" int kdv_prefix_mla_attn(const kdv_mla_dims* d, const uint16_t* q_nope, const uint16_t* q_rope,
+                                   const uint16_t* w_uk, const uint16_t* w_uv, const uint16_t* c_kv,
+                                   const uint16_t* k_pe, int64_t pool_slots, const int32_t* page_table, int32_t L,
+                                   int32_t T, uint16_t* out, float* lse, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  return verify_impl(d, q_nope, q_rope, w_uk, w_uv, c_kv, k_pe, pool_slots, page_table, L, T, nullptr, out, lse,
+                     workspace, workspace_bytes, stream, nullptr, /*with_tree=*/false);
+}
+
+extern "C" int kdv_merge_attn_states(const uint16_t* out_a, const float* lse_a, const uint16_t* out_b,
+                                     const float* lse_b, int64_t rows, int32_t dv, uint16_t* out, float* lse,
+                                     void* stream) {
+  using namespace kdv;
+  if (out_a == nullptr || lse_a == nullptr || out_b == nullptr || lse_b == nullptr || out == nullptr)
+    return KDV_ERR_NULL;
+  if (rows < 1 || dv < 8 || dv % 8 != 0 || dv > 4096 || rows > (int64_t(1) << 34) / dv) return KDV_ERR_SHAPE;
+  if (misaligned(out_a, 16) || misaligned(out_b, 16) || misaligned(out, 16) || misaligned(lse_a, 4) ||
+      misaligned(lse_b, 4) || misaligned(lse, 4))
+    return KDV_ERR_ALIGN;
+  const int64_t chunks = rows * (dv / 8);
+  const int64_t blocks = (chunks + NTHREADS - 1) / NTHREADS;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(merge_states_kernel, dim3((unsigned)blocks), dim3(NTHREADS), 0, static_cast<hipStream_t>(stream),
+                     out_a, lse_a, out_b, lse_b, chunks, dv / 8, out, lse);
+  return hipGetLastError() == hipSuccess ? KDV_OK : KDV_ERR_HIP;
 }
 
 extern "C" const char* kdv_status_string(int status) {

@@ -159,3 +159,50 @@ def test_build_draft_tree_argument_errors():
         assert call(**bad) == kdv.KDV_ERR_SHAPE, bad
     for field in ("logp", "tok", "root", "parent", "tokens", "n"):
         assert call(**{field: A + 1}) == kdv.KDV_ERR_ALIGN, field
+
+
+def _prefix(dims, L=100, T=15, ws_bytes=1 << 40, **override):
+    args = dict(q_nope=A, q_rope=A, w_uk=A, w_uv=A, c_kv=A, k_pe=A, pool_slots=1 << 20, page_table=A, L=L, T=T,
+                out=A, lse=A, workspace=A, workspace_bytes=ws_bytes, stream=None)
+    args.update(override)
+    return kdv.kdv_prefix_mla_attn(dims, **args)
+
+
+@pytest.mark.parametrize("field", ["q_nope", "q_rope", "w_uk", "w_uv", "c_kv", "k_pe", "page_table", "out",
+                                   "workspace"])
+def test_prefix_null_pointer_rejected(field, fixed_splits):
+    assert _prefix(kdv.make_dims(**KIMI), **{field: None}) == kdv.KDV_ERR_NULL
+
+
+@pytest.mark.parametrize("T,L", [(15, 0), (15, -3), (0, 10), (65, 10)])
+def test_prefix_bad_shape_rejected(T, L, fixed_splits):
+    assert _prefix(kdv.make_dims(**KIMI), T=T, L=L) == kdv.KDV_ERR_SHAPE
+
+
+@pytest.mark.parametrize("field,off", [("q_nope", 8), ("c_kv", 2), ("out", 8), ("workspace", 8), ("page_table", 2),
+                                       ("lse", 2)])
+def test_prefix_misaligned_rejected(field, off, fixed_splits):
+    assert _prefix(kdv.make_dims(**KIMI), **{field: A + off}) == kdv.KDV_ERR_ALIGN
+
+
+def test_prefix_workspace_too_small_rejected(fixed_splits):
+    d = kdv.make_dims(**KIMI)
+    assert kdv.kdv_verify_workspace_bytes(d, 15, 5553) > 0
+    assert _prefix(d, T=15, L=5553, ws_bytes=0) == kdv.KDV_ERR_WORKSPACE
+    assert _prefix(d, T=15, L=5553, ws_bytes=255) == kdv.KDV_ERR_WORKSPACE
+
+
+def test_merge_argument_errors():
+    ok = dict(out_a=A, lse_a=A, out_b=A, lse_b=A, rows=960, dv=128, out=A, lse=A)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return kdv.kdv_merge_attn_states(a["out_a"], a["lse_a"], a["out_b"], a["lse_b"], a["rows"], a["dv"],
+                                         a["out"], a["lse"], None)
+    for field in ("out_a", "lse_a", "out_b", "lse_b", "out"):
+        assert call(**{field: None}) == kdv.KDV_ERR_NULL, field
+    for bad in (dict(rows=0), dict(rows=-1), dict(dv=0), dict(dv=4), dict(dv=12), dict(dv=4104)):
+        assert call(**bad) == kdv.KDV_ERR_SHAPE, bad
+    for field, off in (("out_a", 8), ("out_b", 2), ("out", 8), ("lse_a", 2), ("lse_b", 1), ("lse", 2)):
+        assert call(**{field: A + off}) == kdv.KDV_ERR_ALIGN, field
