@@ -256,22 +256,45 @@ def run(args, torch, si, kdv, dev, hip, stream, sh):
             if rc:
                 raise kdv.KdvError(rc, "kdv_verify_mla_attn")
 
-    def run_steps(sets, K):
-        for i in range(K):
-            step(sets[i % len(sets)])
+    # The prefix/tail split of the same step: per layer, a prefix-only call over the L prefix rows, the tree
+    # call over the T tail rows (L = 0) and the LSE merge of the two (one stream, so they share a workspace).
+    split_bufs = [torch.empty_like(out_t), torch.empty_like(lse_t), torch.empty_like(out_t), torch.empty_like(lse_t)]
+    split_ptr = [t.data_ptr() for t in split_bufs]
 
-    def timed(sets, K):
+    def split_step(set_ptrs):
+        rc = kdv.kdv_build_tree_mask(fixed["parent"], T, fixed["mask"], fixed["status"], sh)
+        if rc:
+            raise kdv.KdvError(rc, "kdv_build_tree_mask")
+        for lp in set_ptrs:
+            rc = kdv.kdv_prefix_mla_attn(dims, *lp, pool_slots, fixed["pt"], L, T, split_ptr[0], split_ptr[1],
+                                         fixed["ws"], ws_bytes, sh)
+            if rc:
+                raise kdv.KdvError(rc, "kdv_prefix_mla_attn")
+            rc = kdv.kdv_verify_mla_attn(dims, *lp, pool_slots, fixed["pt"] + 4 * L, 0, T, fixed["mask"],
+                                         split_ptr[2], split_ptr[3], fixed["ws"], ws_bytes, sh)
+            if rc:
+                raise kdv.KdvError(rc, "kdv_verify_mla_attn")
+            rc = kdv.kdv_merge_attn_states(split_ptr[0], split_ptr[1], split_ptr[2], split_ptr[3], T * H, Dv,
+                                           fixed["out"], fixed["lse"], sh)
+            if rc:
+                raise kdv.KdvError(rc, "kdv_merge_attn_states")
+
+    def run_steps(sets, K, fn=step):
+        for i in range(K):
+            fn(sets[i % len(sets)])
+
+    def timed(sets, K, fn=step):
         """Device time (ms) of K steps: graph-captured unless --no-graph."""
         e0, e1 = hip.event(), hip.event()
         if args.no_graph:
             torch.cuda.synchronize()
             hip.record(e0, sh)
-            run_steps(sets, K)
+            run_steps(sets, K, fn)
             hip.record(e1, sh)
             return hip.elapsed_ms(e0, e1)
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
-            run_steps(sets, K)
+            run_steps(sets, K, fn)
         g.replay()                       # untimed replay: graph upload, first-touch
         torch.cuda.synchronize()
         hip.record(e0, sh)
@@ -292,6 +315,11 @@ def run(args, torch, si, kdv, dev, hip, stream, sh):
     ms_cold = timed(cold_ptrs, K)
     log(f"[bench] timing {K} steps (hot)")
     ms_hot = timed(hot_ptrs, K)
+    ms_split = None
+    if L >= 1:
+        log(f"[bench] timing {K} steps of the prefix/tail split (cold)")
+        run_steps(cold_ptrs, 2, split_step)
+        ms_split = timed(cold_ptrs, K, split_step)
 
     # per-kernel device time: events stamped by each kernel's own dispatch
     log("[bench] per-kernel timing")
@@ -377,6 +405,14 @@ def run(args, torch, si, kdv, dev, hip, stream, sh):
     build_us = graph_us(build_launch)
     torch.cuda.synchronize()
 
+    def merge_launch():
+        rc = kdv.kdv_merge_attn_states(split_ptr[0], split_ptr[1], split_ptr[2], split_ptr[3], T * H, Dv,
+                                       fixed["out"], fixed["lse"], sh)
+        if rc:
+            raise kdv.KdvError(rc, "kdv_merge_attn_states")
+    merge_us = graph_us(merge_launch) if L >= 1 else None
+    torch.cuda.synchronize()
+
     us_layer_cold = 1e3 * ms_cold / (K * layers_per_step)
     us_layer_hot = 1e3 * ms_hot / (K * layers_per_step)
     tflops_cold = wk["flops"] / (us_layer_cold * 1e-6) / 1e12
@@ -421,6 +457,13 @@ def run(args, torch, si, kdv, dev, hip, stream, sh):
                                      "nodes": int(b_out[2].item()), "timing": "one HIP graph of 200 launches",
                                      "bound": "latency of 31 dependent wave-wide selections"}},
     }
+    if ms_split is not None:
+        result["next_rows"]["prefix_tail_split"] = {
+            "us_per_layer": round(1e3 * ms_split / (K * layers_per_step), 3),
+            "single_call_us_per_layer": round(us_layer_cold, 3),
+            "merge_us": round(merge_us, 3),
+            "parts": "prefix-only attention over L rows + tree attention over the T tail rows + LSE merge",
+            "timing": "one HIP graph of K steps, cold rotation; merge alone: one HIP graph of 200 launches"}
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, inp, wk, layers_per_step)
