@@ -64,6 +64,7 @@ typedef enum kdv_status {
 } kdv_status;
 
 #define KDV_MAX_TREE_NODES 64
+#define KDV_MAX_BATCH 16           /* requests per kdv_verify_mla_attn_batch call */
 #define KDV_MAX_DRAFT_ENTRIES 4096 /* block x K entries of the drafter's top-K table */
 
 /* Best-first construction of the draft tree on the device ("The Architecture of Diagnosis...", section
@@ -170,6 +171,33 @@ int kdv_verify_mla_attn_profiled(const kdv_mla_dims* d, const uint16_t* q_nope, 
                                  const uint16_t* k_pe, int64_t pool_slots, const int32_t* page_table, int32_t L,
                                  int32_t T, const uint32_t* mask, uint16_t* out, float* lse, void* workspace,
                                  size_t workspace_bytes, void* stream, void* const* events);
+
+/* Batched verify: C requests in one call, each with its own prefix length, tree, page table and queries, over a
+ * shared latent pool and the same layer weights.  The pages measure the service at ten concurrent streams
+ * beside one ("The Three Acts of Engineering: Diagnosis, Extension, and Analytical Pivot in a Speculative
+ * Decoding Stack", section "References", item [3]) and list batching among the throughput levers ("From
+ * Diagnosis to Deployment: Three Threads of Inference Engineering for Kimi K2.6", section "The Diagnostic
+ * Infrastructure").  Request c's result is what kdv_verify_mla_attn computes for it alone; the requests only
+ * share the launches, so that small trees fill the device together.
+ *   C          : 1 <= C <= KDV_MAX_BATCH.
+ *   L, T       : host int32 [C]: prefix length (>= 0) and tree size (1..64) of each request.
+ *   Requests are packed in order.  With n_c = T[0] + ... + T[c-1]:
+ *   q_nope     : device bf16 [sum T][H][Dn]; request c's nodes are rows n_c .. n_c + T[c] - 1 (same for
+ *                q_rope [sum T][H][Dr], out [sum T][H][Dv] and lse [sum T][H]).
+ *   page_table : device int32 [sum (L+T)]; request c's L[c] + T[c] entries follow those of requests < c, laid
+ *                out as for kdv_verify_mla_attn.
+ *   mask       : device uint32; request c's [T[c]][(T[c]+31)/32] words (kdv_build_tree_mask of its parent
+ *                array) follow those of requests < c.
+ *   workspace  : >= kdv_verify_batch_workspace_bytes(d, C, L, T) bytes, 16-byte aligned.
+ * Other arguments and errors as kdv_verify_mla_attn. */
+int kdv_verify_mla_attn_batch(const kdv_mla_dims* d, int32_t C, const int32_t* L, const int32_t* T,
+                              const uint16_t* q_nope, const uint16_t* q_rope, const uint16_t* w_uk,
+                              const uint16_t* w_uv, const uint16_t* c_kv, const uint16_t* k_pe, int64_t pool_slots,
+                              const int32_t* page_table, const uint32_t* mask, uint16_t* out, float* lse,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes for kdv_verify_mla_attn_batch (host arrays L, T of C entries); 0 if unsupported. */
+size_t kdv_verify_batch_workspace_bytes(const kdv_mla_dims* d, int32_t C, const int32_t* L, const int32_t* T);
 
 /* Prefix part of a split verify step: the pages' production arrangement gives the long prefix to a dense MLA
  * decode kernel and only the small tree tail to the tree kernel ("The Three Acts of Engineering: Diagnosis,

@@ -26,9 +26,11 @@ KDV_ERR_WORKSPACE = -5
 KDV_ERR_HIP = -6
 KDV_MAX_TREE_NODES = 64
 KDV_MAX_DRAFT_ENTRIES = 4096
+KDV_MAX_BATCH = 16
 
 EXPORTED = ("kdv_build_draft_tree", "kdv_build_tree_mask", "kdv_merge_attn_states", "kdv_prefix_mla_attn",
-            "kdv_tree_accept", "kdv_verify_workspace_bytes", "kdv_verify_mla_attn", "kdv_verify_mla_attn_profiled",
+            "kdv_tree_accept", "kdv_verify_batch_workspace_bytes", "kdv_verify_mla_attn_batch",
+            "kdv_verify_workspace_bytes", "kdv_verify_mla_attn", "kdv_verify_mla_attn_profiled",
             "kdv_verify_num_splits", "kdv_status_string")
 
 
@@ -65,6 +67,11 @@ def _load() -> ctypes.CDLL:
     lib.kdv_verify_mla_attn_profiled.argtypes = [dims_p, vp, vp, vp, vp, vp, vp, i64, vp, i32, i32, vp, vp, vp, vp,
                                                  sz, vp, vp]
     lib.kdv_verify_mla_attn_profiled.restype = ctypes.c_int
+    lib.kdv_verify_mla_attn_batch.argtypes = [dims_p, i32, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, vp,
+                                              sz, vp]
+    lib.kdv_verify_mla_attn_batch.restype = ctypes.c_int
+    lib.kdv_verify_batch_workspace_bytes.argtypes = [dims_p, i32, vp, vp]
+    lib.kdv_verify_batch_workspace_bytes.restype = sz
     lib.kdv_prefix_mla_attn.argtypes = [dims_p, vp, vp, vp, vp, vp, vp, i64, vp, i32, i32, vp, vp, vp, sz, vp]
     lib.kdv_prefix_mla_attn.restype = ctypes.c_int
     lib.kdv_merge_attn_states.argtypes = [vp, vp, vp, vp, i64, i32, vp, vp, vp]
@@ -115,6 +122,28 @@ def kdv_verify_mla_attn_profiled(dims: KdvMlaDims, q_nope: int, q_rope: int, w_u
     return _lib.kdv_verify_mla_attn_profiled(ctypes.byref(dims), q_nope, q_rope, w_uk, w_uv, c_kv, k_pe, pool_slots,
                                              page_table, L, T, mask, out, lse, workspace, workspace_bytes, stream,
                                              events)
+
+
+def _host_i32(values):
+    """(ctypes int32 array, its address) for a host array argument; None passes NULL."""
+    if values is None:
+        return None, None
+    arr = (ctypes.c_int32 * len(values))(*[int(v) for v in values])
+    return arr, ctypes.addressof(arr)
+
+
+def kdv_verify_batch_workspace_bytes(dims: KdvMlaDims, C: int, L: int | None, T: int | None) -> int:
+    """L, T: addresses of host int32 arrays (see _host_i32)."""
+    return _lib.kdv_verify_batch_workspace_bytes(ctypes.byref(dims), C, L, T)
+
+
+def kdv_verify_mla_attn_batch(dims: KdvMlaDims, C: int, L: int | None, T: int | None, q_nope: int, q_rope: int,
+                              w_uk: int, w_uv: int, c_kv: int, k_pe: int, pool_slots: int, page_table: int,
+                              mask: int, out: int, lse: int | None, workspace: int, workspace_bytes: int,
+                              stream: int | None) -> int:
+    """L, T: addresses of host int32 arrays of C entries (see _host_i32)."""
+    return _lib.kdv_verify_mla_attn_batch(ctypes.byref(dims), C, L, T, q_nope, q_rope, w_uk, w_uv, c_kv, k_pe,
+                                          pool_slots, page_table, mask, out, lse, workspace, workspace_bytes, stream)
 
 
 def kdv_prefix_mla_attn(dims: KdvMlaDims, q_nope: int, q_rope: int, w_uk: int, w_uv: int, c_kv: int, k_pe: int,
@@ -295,4 +324,64 @@ def merge_attn_states(out_a, lse_a, out_b, lse_b, out=None, lse=None, stream=Non
                                _stream_handle(stream))
     if rc != KDV_OK:
         raise KdvError(rc, "kdv_merge_attn_states")
+    return out, lse
+
+
+def build_tree_masks(parents, stream=None):
+    """Packed ancestor masks of several trees (one kdv_build_tree_mask launch each), in the layout
+    kdv_verify_mla_attn_batch takes.  parents: list of int32 device tensors.  Returns (mask int32 tensor,
+    status int32 [len(parents)])."""
+    import torch
+    dev = parents[0].device
+    words = [p.shape[0] * ((p.shape[0] + 31) // 32) for p in parents]
+    mask = torch.empty((sum(words),), dtype=torch.int32, device=dev)
+    status = torch.empty((len(parents),), dtype=torch.int32, device=dev)
+    off = 0
+    for i, (p, w) in enumerate(zip(parents, words)):
+        rc = kdv_build_tree_mask(_ptr(p, torch.int32, "parent"), p.shape[0], mask.data_ptr() + 4 * off,
+                                 status.data_ptr() + 4 * i, _stream_handle(stream))
+        if rc != KDV_OK:
+            raise KdvError(rc, "kdv_build_tree_mask")
+        off += w
+    return mask, status
+
+
+def verify_batch_workspace_bytes(dims: KdvMlaDims, Ls, Ts) -> int:
+    la, lp = _host_i32(Ls)
+    ta, tp = _host_i32(Ts)
+    n = kdv_verify_batch_workspace_bytes(dims, len(Ls), lp, tp)
+    if n == 0:
+        raise KdvError(KDV_ERR_SHAPE, "kdv_verify_batch_workspace_bytes")
+    return n
+
+
+def verify_mla_attn_batch(dims: KdvMlaDims, q_nope, q_rope, w_uk, w_uv, c_kv, k_pe, page_table, Ls, Ts, mask,
+                          out=None, lse=None, workspace=None, stream=None):
+    """Batched verify over packed requests (include/kdv.h): q_nope [sum T][H][Dn], page_table [sum (L+T)],
+    mask from build_tree_masks.  Returns (out [sum T][H][Dv] bf16, lse [sum T][H] fp32 or None)."""
+    import torch
+    n_nodes = int(sum(Ts))
+    H = dims.num_heads
+
+    def bf(t, what):
+        if t.dtype == torch.bfloat16:
+            return _ptr(t, torch.bfloat16, what)
+        return _ptr(t, torch.int16, what)
+
+    if out is None:
+        out = torch.empty((n_nodes, H, dims.v_head_dim), dtype=torch.bfloat16, device=q_nope.device)
+    if workspace is None:
+        workspace = torch.empty((verify_batch_workspace_bytes(dims, Ls, Ts),), dtype=torch.uint8,
+                                device=q_nope.device)
+    la, lp = _host_i32(Ls)
+    ta, tp = _host_i32(Ts)
+    lse_ptr = None if lse is None else _ptr(lse, torch.float32, "lse")
+    rc = kdv_verify_mla_attn_batch(dims, len(Ls), lp, tp, bf(q_nope, "q_nope"), bf(q_rope, "q_rope"),
+                                   bf(w_uk, "w_uk"), bf(w_uv, "w_uv"), bf(c_kv, "c_kv"), bf(k_pe, "k_pe"),
+                                   c_kv.shape[0], _ptr(page_table, torch.int32, "page_table"),
+                                   _ptr(mask, torch.int32, "mask"), bf(out, "out"), lse_ptr,
+                                   _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
+                                   _stream_handle(stream))
+    if rc != KDV_OK:
+        raise KdvError(rc, "kdv_verify_mla_attn_batch")
     return out, lse

@@ -14,6 +14,7 @@
 //   combine_up : log-sum-exp merge of the splits -> lse and the latent output o[t,h] (bf16, in LDS), then
 //              out[t,h] = W_UV[h] o[t,h]                                   (bf16 MFMA)
 #include <hip/hip_ext.h>
+#include <algorithm>
 #include <math.h>
 #include <stdlib.h>
 
@@ -25,6 +26,32 @@ constexpr int KV_TILE = 64;   // KV rows per LDS tile
 constexpr int M_TILE = 64;    // query rows (node, head) per split-KV workgroup
 constexpr int NTHREADS = 256;
 constexpr int NUM_XCD = 8;    // MI355X: 8 accelerator complex dies, each with its own L2
+constexpr int MAX_BATCH = KDV_MAX_BATCH;
+
+// Launch parameters of one request of a (possibly batched) call, computed on the host and passed by value in
+// the kernel arguments.  Requests are packed: their nodes, page-table entries and mask words follow one another.
+struct ReqArgs {
+  int L, T, N;                  // prefix rows, tree nodes, KV rows attended (L + T, or L for a prefix-only pass)
+  int node0, pt0, mask0;        // first node (q, out and lse rows), first page-table entry, first mask word
+  int m_tiles, Mp;              // 64-row query tiles of the request's T*H rows, and their padded row count
+  int tiles_per_split, splits;  // KV split plan
+  int xoff;                     // the request's splits start at this XCD (spreads small requests over the dies)
+  long long po, pml;            // element offsets of the request's partials in part_o and part_ml
+};
+// NB = capacity: 1 for the single-request entry points (a small kernel-argument block), MAX_BATCH for batches.
+template <int NB>
+struct BatchArgs {
+  int n, H;
+  int blk_split[NB + 1];  // first split-KV workgroup of each request (multiples of NUM_XCD)
+  int blk_comb[NB + 1];   // first combine workgroup of each request (multiples of NUM_XCD)
+  ReqArgs r[NB];
+};
+// Request owning workgroup b (uniform): the last one whose first workgroup is <= b.
+__device__ __forceinline__ int request_of(const int* first, int n, int b) {
+  int c = 0;
+  while (c + 1 < n && b >= first[c + 1]) ++c;
+  return c;
+}
 
 template <int R, int DR>
 struct Shape {
@@ -371,12 +398,11 @@ __device__ __forceinline__ void tile_compute(const char* tile, const bf16x8 (&q)
 // Workgroup = 4 waves over 64 query rows (m = t*H + h).  Wave (wi, wj) = (w / 2, w % 2): scores of rows wi*32..+31
 // against KV rows wj*32..+31 of each tile; values for latent columns w*CPW..+CPW of all 64 rows.
 // Two LDS tiles: while one is computed, the next is gathered by DMA (spread over the score MFMAs).
-template <int R, int DR>
+template <int R, int DR, int NB>
 __global__ __launch_bounds__(NTHREADS, 1) void splitkv_kernel(
-    const uint16_t* __restrict__ q_cat, const uint16_t* __restrict__ c_kv, const uint16_t* __restrict__ k_pe,
-    const int32_t* __restrict__ page_table, const uint32_t* __restrict__ mask, int L, int T, int H, int M, int N,
-    int m_tiles, int tiles_per_split, int num_splits, float scale_log2, uint16_t* __restrict__ part_o,
-    float2* __restrict__ part_ml, int Mp) {
+    const uint16_t* __restrict__ q_cat_all, const uint16_t* __restrict__ c_kv, const uint16_t* __restrict__ k_pe,
+    const int32_t* __restrict__ page_table_all, const uint32_t* __restrict__ mask_all, const BatchArgs<NB> ba,
+    float scale_log2, uint16_t* __restrict__ part_o_all, float2* __restrict__ part_ml_all) {
   using TL = TileLayout<R, DR>;
   constexpr int DQ = R + DR, KB = DQ / 16;
   __shared__ __attribute__((aligned(1024))) char kvbuf[2 * TL::BYTES];
@@ -384,10 +410,26 @@ __global__ __launch_bounds__(NTHREADS, 1) void splitkv_kernel(
   __shared__ float mxch[2][2][32];     // [row block][kv half][row]: proposed reference
   __shared__ float psum[2][2][32];     // [row block][kv half][row]: half-tile row sum
 
-  // Workgroups are dealt to the XCDs round-robin (block b -> XCD b % NUM_XCD).  Every query tile of one KV
-  // split is kept on one XCD so that split's rows are fetched into that XCD's L2 once and then shared.
-  const int xcd = blockIdx.x % NUM_XCD, j = blockIdx.x / NUM_XCD;
-  const int split = xcd + NUM_XCD * (j / m_tiles);
+  // This workgroup's request; its arrays start at the request's offsets.
+  const int rqi = NB > 1 ? request_of(ba.blk_split, ba.n, blockIdx.x) : 0;  // (a constant index for one request)
+  const ReqArgs& rq = ba.r[rqi];
+  const int L = rq.L, T = rq.T, H = ba.H, M = rq.T * ba.H, N = rq.N, m_tiles = rq.m_tiles, Mp = rq.Mp;
+  const int tiles_per_split = rq.tiles_per_split, num_splits = rq.splits;
+  const uint16_t* q_cat = q_cat_all + (size_t)rq.node0 * H * DQ;
+  const int32_t* page_table = page_table_all + rq.pt0;
+  const uint32_t* mask = (N > L) ? mask_all + rq.mask0 : nullptr;
+  // (the offsets are materialised here: the compiler would otherwise sink their loads to the epilogue, where
+  // they wait; pinning the integers, not the pointers, keeps the stores global rather than flat)
+  long long po = rq.po, pml = rq.pml;
+  asm volatile("" : "+s"(po), "+s"(pml));
+  uint16_t* part_o = part_o_all + po;
+  float2* part_ml = part_ml_all + pml;
+  // Workgroups are dealt to the XCDs round-robin (block b -> XCD b % NUM_XCD; a request's first block is a
+  // multiple of NUM_XCD).  Every query tile of one KV split is kept on one XCD so that split's rows are fetched
+  // into that XCD's L2 once and then shared; the request's splits start at XCD xoff.
+  const int bid = blockIdx.x - ba.blk_split[rqi];
+  const int xcd = bid % NUM_XCD, j = bid / NUM_XCD;
+  const int split = (xcd - rq.xoff + NUM_XCD) % NUM_XCD + NUM_XCD * (j / m_tiles);
   const int mt = j % m_tiles;
   if (split >= num_splits) return;  // padding block (uniform; before any barrier)
   const int tid = threadIdx.x, lane = tid & 63;
@@ -615,11 +657,13 @@ __global__ __launch_bounds__(NTHREADS) void q_absorb_kernel(const uint16_t* __re
 //     the row, so the MFMA's quarter-wave reads (16 rows, one chunk) hit 16 distinct bank groups.
 // After one barrier, wave w computes D[v][t] = sum_r W_UV[h][v][r] o[t][r] for its 32 columns v, both
 // operands read from LDS (r-contiguous); columns t >= RT of the product repeat the last row, never stored.
-template <int R, int DV>
-__global__ __launch_bounds__(NTHREADS) void combine_up_kernel(const uint16_t* __restrict__ part_o,
-                                                              const float2* __restrict__ part_ml, int S, int Mp,
-                                                              int T, int H, const uint16_t* __restrict__ w_uv,
-                                                              uint16_t* __restrict__ out, float* __restrict__ lse) {
+template <int R, int DV, int NB>
+__global__ __launch_bounds__(NTHREADS) void combine_up_kernel(const uint16_t* __restrict__ part_o_all,
+                                                              const float2* __restrict__ part_ml_all,
+                                                              const BatchArgs<NB> ba,
+                                                              const uint16_t* __restrict__ w_uv,
+                                                              uint16_t* __restrict__ out_all,
+                                                              float* __restrict__ lse_all) {
   constexpr int RT = 4;                      // tree nodes per workgroup
   constexpr int CPR = R / 8;                 // 16-byte chunks per latent row
   constexpr int KS = R / 16;                 // MFMA k-steps
@@ -635,7 +679,20 @@ __global__ __launch_bounds__(NTHREADS) void combine_up_kernel(const uint16_t* __
   static_assert(WBYTES % 2048 == 0, "W_UV must split evenly over two fetching waves");
   __shared__ __attribute__((aligned(16))) uint16_t o_s[RT * OP];
   __shared__ __attribute__((aligned(1024))) char w_s[WBYTES];
-  const int xcd = blockIdx.x % NUM_XCD, j = blockIdx.x / NUM_XCD;
+  const int rqi = NB > 1 ? request_of(ba.blk_comb, ba.n, blockIdx.x) : 0;
+  const ReqArgs& rq = ba.r[rqi];
+  const int T = rq.T, H = ba.H;
+  // (offsets loaded up front rather than next to their first use; pinning integers, not pointers, keeps the
+  // memory accesses global rather than flat)
+  long long po = rq.po, pml = rq.pml, obase = (long long)rq.node0 * H;
+  int S = rq.splits, Mp = rq.Mp;
+  asm volatile("" : "+s"(po), "+s"(pml), "+s"(obase), "+s"(S), "+s"(Mp));
+  const uint16_t* part_o = part_o_all + po;
+  const float2* part_ml = part_ml_all + pml;
+  uint16_t* out = out_all + obase * DV;
+  float* lse = (lse_all != nullptr) ? lse_all + obase : nullptr;
+  const int bid = blockIdx.x - ba.blk_comb[rqi];  // (a request's first block is a multiple of NUM_XCD)
+  const int xcd = bid % NUM_XCD, j = bid / NUM_XCD;
   const int TB = (T + RT - 1) / RT;
   const int h = xcd + NUM_XCD * (j / TB), t0 = (j % TB) * RT;
   if (h >= H) return;  // padding block (uniform; before any barrier)
@@ -768,7 +825,9 @@ __global__ __launch_bounds__(NTHREADS) void merge_states_kernel(const uint16_t* 
 
 // ------------------------------------------------------------------------------------------------ host side
 struct Plan {
-  int H, M, Mp, m_tiles, N, ntiles, tiles_per_split, splits;
+  int H, nodes;           // heads, nodes of all requests
+  int split_blocks, comb_blocks;
+  BatchArgs<MAX_BATCH> ba;
   size_t off_qcat, off_po, off_pml, total;
 };
 
@@ -792,40 +851,85 @@ static int device_cu_count() {
   return cus;
 }
 
-// Split the KV sequence (L prefix rows, then `kv_tree` = T or 0 tree rows) so that (query tiles x splits) fills
-// the device once; every split gets the same whole number of 64-row tiles except possibly the last.
-static int make_plan(const kdv_mla_dims* d, int T, int L, Plan* p, bool with_tree = true) {
-  if (d == nullptr) return KDV_ERR_NULL;
-  if (shape_of(d) == SHAPE_NONE) return KDV_ERR_SHAPE;
-  if (T < 1 || T > KDV_MAX_TREE_NODES || L < 0 || (int64_t)L + T > 0x7fffff00LL) return KDV_ERR_SHAPE;
-  p->H = d->num_heads;
-  p->M = T * d->num_heads;
-  p->m_tiles = (p->M + M_TILE - 1) / M_TILE;
-  p->Mp = p->m_tiles * M_TILE;
-  p->N = L + (with_tree ? T : 0);
-  if (p->N < 1) return KDV_ERR_SHAPE;
-  p->ntiles = (p->N + KV_TILE - 1) / KV_TILE;
-  int want = 0;
-  if (const char* env = getenv("KDV_SPLITS")) want = atoi(env);
-  if (want <= 0) {
-    // One workgroup per CU, all query tiles of a split on one XCD: NUM_XCD * floor(CUs per XCD / query tiles).
-    const int cus = device_cu_count();
-    if (cus <= 0) return KDV_ERR_HIP;
-    const int per_xcd = cus / NUM_XCD;
-    want = (p->m_tiles <= per_xcd) ? NUM_XCD * (per_xcd / p->m_tiles) : cus / p->m_tiles;
-    if (want < 1) want = 1;
+// Plan of a call over C packed requests (C = 1 for the single-request entry points).  Each request's KV
+// sequence (L prefix rows, then its T tree rows unless `with_tree` is false) is split so that (query tiles x
+// splits) fills the request's share of the device once: one workgroup per CU with all query tiles of a split
+// on one XCD, i.e. NUM_XCD * floor(CUs per XCD / query tiles) splits, the CUs shared among the requests in
+// proportion to their tile work.  Every split gets the same whole number of 64-row tiles except possibly the
+// last.  The environment variable KDV_SPLITS, if set, fixes every request's split count instead.
+static int make_plan(const kdv_mla_dims* d, int C, const int32_t* Ls, const int32_t* Ts, Plan* p,
+                     bool with_tree = true) {
+  if (d == nullptr || Ls == nullptr || Ts == nullptr) return KDV_ERR_NULL;
+  if (shape_of(d) == SHAPE_NONE || C < 1 || C > MAX_BATCH) return KDV_ERR_SHAPE;
+  const int H = d->num_heads;
+  int64_t nodes = 0, pt = 0, mwords = 0, work = 0;
+  int m_tiles[MAX_BATCH], ntiles[MAX_BATCH];
+  for (int c = 0; c < C; ++c) {
+    const int L = Ls[c], T = Ts[c];
+    if (T < 1 || T > KDV_MAX_TREE_NODES || L < (with_tree ? 0 : 1) || (int64_t)L + T > 0x7fffff00LL)
+      return KDV_ERR_SHAPE;
+    const int N = L + (with_tree ? T : 0);
+    m_tiles[c] = (T * H + M_TILE - 1) / M_TILE;
+    ntiles[c] = (N + KV_TILE - 1) / KV_TILE;
+    work += (int64_t)m_tiles[c] * ntiles[c];
+    ReqArgs& r = p->ba.r[c];
+    r.L = L;
+    r.T = T;
+    r.N = N;
+    r.node0 = (int)nodes;
+    r.pt0 = (int)pt;
+    r.mask0 = (int)mwords;
+    r.m_tiles = m_tiles[c];
+    r.Mp = m_tiles[c] * M_TILE;
+    nodes += T;
+    pt += (int64_t)L + T;
+    mwords += (int64_t)T * ((T + 31) / 32);
+    if (pt > 0x7fffff00LL) return KDV_ERR_SHAPE;
   }
-  if (want > p->ntiles) want = p->ntiles;
-  p->tiles_per_split = (p->ntiles + want - 1) / want;
-  p->splits = (p->ntiles + p->tiles_per_split - 1) / p->tiles_per_split;
+  int env_splits = 0;
+  if (const char* env = getenv("KDV_SPLITS")) env_splits = atoi(env);
+  const int cus = env_splits > 0 ? 0 : device_cu_count();
+  if (env_splits <= 0 && cus <= 0) return KDV_ERR_HIP;
   const int R = d->kv_lora_rank, DQ = R + d->qk_rope_dim;
+  p->H = H;
+  p->nodes = (int)nodes;
+  p->ba.n = C;
+  p->ba.H = H;
+  p->ba.blk_split[0] = p->ba.blk_comb[0] = 0;
+  int64_t po = 0, pml = 0, blk_s = 0, blk_c = 0, xoff = 0;
+  for (int c = 0; c < C; ++c) {
+    ReqArgs& r = p->ba.r[c];
+    int want = env_splits;
+    if (want <= 0) {
+      const int share = (C == 1) ? cus : (int)std::max<int64_t>(NUM_XCD, (int64_t)cus * m_tiles[c] * ntiles[c] / work);
+      const int per_xcd = share / NUM_XCD;
+      want = (r.m_tiles <= per_xcd) ? NUM_XCD * (per_xcd / r.m_tiles) : share / r.m_tiles;
+      if (want < 1) want = 1;
+    }
+    if (want > ntiles[c]) want = ntiles[c];
+    r.tiles_per_split = (ntiles[c] + want - 1) / want;
+    r.splits = (ntiles[c] + r.tiles_per_split - 1) / r.tiles_per_split;
+    r.xoff = (int)(xoff % NUM_XCD);
+    xoff += r.splits;
+    r.po = po;
+    r.pml = pml;
+    po += (int64_t)r.splits * r.Mp * R;
+    pml += (int64_t)r.splits * r.Mp;
+    blk_s += (int64_t)NUM_XCD * r.m_tiles * ((r.splits + NUM_XCD - 1) / NUM_XCD);
+    blk_c += (int64_t)NUM_XCD * ((H + NUM_XCD - 1) / NUM_XCD) * ((r.T + 3) / 4);
+    if (blk_s > 0x7fffffff || blk_c > 0x7fffffff) return KDV_ERR_SHAPE;
+    p->ba.blk_split[c + 1] = (int)blk_s;
+    p->ba.blk_comb[c + 1] = (int)blk_c;
+  }
+  p->split_blocks = (int)blk_s;
+  p->comb_blocks = (int)blk_c;
   size_t off = 0;
   p->off_qcat = off;
-  off += align256((size_t)p->M * DQ * 2);
+  off += align256((size_t)nodes * H * DQ * 2);
   p->off_po = off;
-  off += align256((size_t)p->splits * p->Mp * R * 2);
+  off += align256((size_t)po * 2);
   p->off_pml = off;
-  off += align256((size_t)p->splits * p->Mp * 8);
+  off += align256((size_t)pml * 8);
   p->total = off;
   return KDV_OK;
 }
@@ -842,21 +946,33 @@ static void launch(void (*k)(KArgs...), dim3 grid, hipStream_t st, hipEvent_t co
 template <int DN, int R, int DR, int DV>
 static void launch_all(const Plan& pl, float sm_scale, const uint16_t* q_nope, const uint16_t* q_rope,
                        const uint16_t* w_uk, const uint16_t* w_uv, const uint16_t* c_kv, const uint16_t* k_pe,
-                       const int32_t* page_table, int L, int T, const uint32_t* mask, uint16_t* out, float* lse,
-                       char* ws, hipStream_t st, hipEvent_t const* ev) {
+                       const int32_t* page_table, const uint32_t* mask, uint16_t* out, float* lse, char* ws,
+                       hipStream_t st, hipEvent_t const* ev) {
   uint16_t* q_cat = reinterpret_cast<uint16_t*>(ws + pl.off_qcat);
   uint16_t* part_o = reinterpret_cast<uint16_t*>(ws + pl.off_po);
   float2* part_ml = reinterpret_cast<float2*>(ws + pl.off_pml);
+  // the query absorption is per node: the packed nodes of all requests in one grid
   launch(q_absorb_kernel<DN, R, DR>, dim3(pl.H, (R + 127) / 128), st, ev ? ev + 0 : nullptr, q_nope, q_rope, w_uk,
-         q_cat, T, pl.H);
+         q_cat, pl.nodes, pl.H);
   const float scale_log2 = sm_scale * 1.44269504088896340736f;
-  const int grid = NUM_XCD * pl.m_tiles * ((pl.splits + NUM_XCD - 1) / NUM_XCD);
-  launch(splitkv_kernel<R, DR>, dim3(grid), st, ev ? ev + 2 : nullptr, (const uint16_t*)q_cat, c_kv, k_pe,
-         page_table, mask, L, T, pl.H, pl.M, pl.N, pl.m_tiles, pl.tiles_per_split, pl.splits, scale_log2, part_o,
-         part_ml, pl.Mp);
-  const int cgrid = NUM_XCD * ((pl.H + NUM_XCD - 1) / NUM_XCD) * ((T + 3) / 4);
-  launch(combine_up_kernel<R, DV>, dim3(cgrid), st, ev ? ev + 4 : nullptr, (const uint16_t*)part_o,
-         (const float2*)part_ml, pl.splits, pl.Mp, T, pl.H, w_uv, out, lse);
+  if (pl.ba.n == 1) {
+    BatchArgs<1> one;
+    one.n = 1;
+    one.H = pl.ba.H;
+    one.blk_split[0] = one.blk_comb[0] = 0;
+    one.blk_split[1] = pl.ba.blk_split[1];
+    one.blk_comb[1] = pl.ba.blk_comb[1];
+    one.r[0] = pl.ba.r[0];
+    launch(splitkv_kernel<R, DR, 1>, dim3(pl.split_blocks), st, ev ? ev + 2 : nullptr, (const uint16_t*)q_cat, c_kv,
+           k_pe, page_table, mask, one, scale_log2, part_o, part_ml);
+    launch(combine_up_kernel<R, DV, 1>, dim3(pl.comb_blocks), st, ev ? ev + 4 : nullptr, (const uint16_t*)part_o,
+           (const float2*)part_ml, one, w_uv, out, lse);
+  } else {
+    launch(splitkv_kernel<R, DR, MAX_BATCH>, dim3(pl.split_blocks), st, ev ? ev + 2 : nullptr,
+           (const uint16_t*)q_cat, c_kv, k_pe, page_table, mask, pl.ba, scale_log2, part_o, part_ml);
+    launch(combine_up_kernel<R, DV, MAX_BATCH>, dim3(pl.comb_blocks), st, ev ? ev + 4 : nullptr,
+           (const uint16_t*)part_o, (const float2*)part_ml, pl.ba, w_uv, out, lse);
+  }
 }
 
 static bool misaligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
@@ -865,46 +981,54 @@ static bool misaligned(const void* p, uintptr_t a) { return (reinterpret_cast<ui
 
 extern "C" size_t kdv_verify_workspace_bytes(const kdv_mla_dims* d, int32_t T, int32_t L) {
   kdv::Plan p;
-  if (kdv::make_plan(d, T, L, &p) != KDV_OK) return 0;
+  if (kdv::make_plan(d, 1, &L, &T, &p) != KDV_OK) return 0;
+  return p.total;
+}
+
+extern "C" size_t kdv_verify_batch_workspace_bytes(const kdv_mla_dims* d, int32_t C, const int32_t* L,
+                                                   const int32_t* T) {
+  kdv::Plan p;
+  if (kdv::make_plan(d, C, L, T, &p) != KDV_OK) return 0;
   return p.total;
 }
 
 extern "C" int32_t kdv_verify_num_splits(const kdv_mla_dims* d, int32_t T, int32_t L) {
   kdv::Plan p;
-  if (kdv::make_plan(d, T, L, &p) != KDV_OK) return 0;
-  return p.splits;
+  if (kdv::make_plan(d, 1, &L, &T, &p) != KDV_OK) return 0;
+  return p.ba.r[0].splits;
 }
 
-static int verify_impl(const kdv_mla_dims* d, const uint16_t* q_nope, const uint16_t* q_rope,
-                       const uint16_t* w_uk, const uint16_t* w_uv, const uint16_t* c_kv, const uint16_t* k_pe,
-                       int64_t pool_slots, const int32_t* page_table, int32_t L, int32_t T, const uint32_t* mask,
-                       uint16_t* out, float* lse, void* workspace, size_t workspace_bytes, void* stream,
-                       hipEvent_t const* ev, bool with_tree = true) {
+static int verify_impl(const kdv_mla_dims* d, int32_t C, const int32_t* Ls, const int32_t* Ts,
+                       const uint16_t* q_nope, const uint16_t* q_rope, const uint16_t* w_uk, const uint16_t* w_uv,
+                       const uint16_t* c_kv, const uint16_t* k_pe, int64_t pool_slots, const int32_t* page_table,
+                       const uint32_t* mask, uint16_t* out, float* lse, void* workspace, size_t workspace_bytes,
+                       void* stream, hipEvent_t const* ev, bool with_tree = true) {
   using namespace kdv;
-  if (d == nullptr || q_nope == nullptr || q_rope == nullptr || w_uk == nullptr || w_uv == nullptr ||
-      c_kv == nullptr || k_pe == nullptr || page_table == nullptr || (with_tree && mask == nullptr) ||
-      out == nullptr || workspace == nullptr)
+  if (d == nullptr || Ls == nullptr || Ts == nullptr || q_nope == nullptr || q_rope == nullptr ||
+      w_uk == nullptr || w_uv == nullptr || c_kv == nullptr || k_pe == nullptr || page_table == nullptr ||
+      (with_tree && mask == nullptr) || out == nullptr || workspace == nullptr)
     return KDV_ERR_NULL;
   const ShapeId sid = shape_of(d);
-  if (sid == SHAPE_NONE || pool_slots < 1 || T < 1 || T > KDV_MAX_TREE_NODES || L < (with_tree ? 0 : 1))
-    return KDV_ERR_SHAPE;
+  if (sid == SHAPE_NONE || pool_slots < 1 || C < 1 || C > MAX_BATCH) return KDV_ERR_SHAPE;
+  for (int c = 0; c < C; ++c)
+    if (Ts[c] < 1 || Ts[c] > KDV_MAX_TREE_NODES || Ls[c] < (with_tree ? 0 : 1)) return KDV_ERR_SHAPE;
   if (misaligned(q_nope, 16) || misaligned(q_rope, 16) || misaligned(w_uk, 16) || misaligned(w_uv, 16) ||
       misaligned(c_kv, 16) || misaligned(k_pe, 16) || misaligned(out, 16) || misaligned(workspace, 16) ||
       misaligned(page_table, 4) || misaligned(mask, 4) || misaligned(lse, 4))
     return KDV_ERR_ALIGN;
   Plan pl;
-  const int st = make_plan(d, T, L, &pl, with_tree);
+  const int st = make_plan(d, C, Ls, Ts, &pl, with_tree);
   if (st != KDV_OK) return st;
   if (workspace_bytes < pl.total) return KDV_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   (void)hipGetLastError();
   if (sid == SHAPE_KIMI)
-    launch_all<128, 512, 64, 128>(pl, d->sm_scale, q_nope, q_rope, w_uk, w_uv, c_kv, k_pe, page_table, L, T, mask,
-                                  out, lse, ws, s, ev);
+    launch_all<128, 512, 64, 128>(pl, d->sm_scale, q_nope, q_rope, w_uk, w_uv, c_kv, k_pe, page_table, mask, out,
+                                  lse, ws, s, ev);
   else
-    launch_all<32, 64, 16, 32>(pl, d->sm_scale, q_nope, q_rope, w_uk, w_uv, c_kv, k_pe, page_table, L, T, mask,
-                               out, lse, ws, s, ev);
+    launch_all<32, 64, 16, 32>(pl, d->sm_scale, q_nope, q_rope, w_uk, w_uv, c_kv, k_pe, page_table, mask, out, lse,
+                               ws, s, ev);
   return hipGetLastError() == hipSuccess ? KDV_OK : KDV_ERR_HIP;
 }
 
@@ -913,7 +1037,7 @@ extern "C" int kdv_verify_mla_attn(const kdv_mla_dims* d, const uint16_t* q_nope
                                    const uint16_t* k_pe, int64_t pool_slots, const int32_t* page_table, int32_t L,
                                    int32_t T, const uint32_t* mask, uint16_t* out, float* lse, void* workspace,
                                    size_t workspace_bytes, void* stream) {
-  return verify_impl(d, q_nope, q_rope, w_uk, w_uv, c_kv, k_pe, pool_slots, page_table, L, T, mask, out, lse,
+  return verify_impl(d, 1, &L, &T, q_nope, q_rope, w_uk, w_uv, c_kv, k_pe, pool_slots, page_table, mask, out, lse,
                      workspace, workspace_bytes, stream, nullptr);
 }
 
@@ -924,8 +1048,18 @@ extern "C" int kdv_verify_mla_attn_profiled(const kdv_mla_dims* d, const uint16_
                                             void* workspace, size_t workspace_bytes, void* stream,
                                             void* const* events) {
   if (events == nullptr) return KDV_ERR_NULL;
-  return verify_impl(d, q_nope, q_rope, w_uk, w_uv, c_kv, k_pe, pool_slots, page_table, L, T, mask, out, lse,
+  return verify_impl(d, 1, &L, &T, q_nope, q_rope, w_uk, w_uv, c_kv, k_pe, pool_slots, page_table, mask, out, lse,
                      workspace, workspace_bytes, stream, reinterpret_cast<hipEvent_t const*>(events));
+}
+
+extern "C" int kdv_verify_mla_attn_batch(const kdv_mla_dims* d, int32_t C, const int32_t* L, const int32_t* T,
+                                         const uint16_t* q_nope, const uint16_t* q_rope, const uint16_t* w_uk,
+                                         const uint16_t* w_uv, const uint16_t* c_kv, const uint16_t* k_pe,
+                                         int64_t pool_slots, const int32_t* page_table, const uint32_t* mask,
+                                         uint16_t* out, float* lse, void* workspace, size_t workspace_bytes,
+                                         void* stream) {
+  return verify_impl(d, C, L, T, q_nope, q_rope, w_uk, w_uv, c_kv, k_pe, pool_slots, page_table, mask, out, lse,
+                     workspace, workspace_bytes, stream, nullptr);
 }
 
 extern "C" int kdv_prefix_mla_attn(const kdv_mla_dims* d, const uint16_t* q_nope, const uint16_t* q_rope,
@@ -933,8 +1067,8 @@ extern "C" int kdv_prefix_mla_attn(const kdv_mla_dims* d, const uint16_t* q_nope
                                    const uint16_t* k_pe, int64_t pool_slots, const int32_t* page_table, int32_t L,
                                    int32_t T, uint16_t* out, float* lse, void* workspace, size_t workspace_bytes,
                                    void* stream) {
-  return verify_impl(d, q_nope, q_rope, w_uk, w_uv, c_kv, k_pe, pool_slots, page_table, L, T, nullptr, out, lse,
-                     workspace, workspace_bytes, stream, nullptr, /*with_tree=*/false);
+  return verify_impl(d, 1, &L, &T, q_nope, q_rope, w_uk, w_uv, c_kv, k_pe, pool_slots, page_table, nullptr, out,
+                     lse, workspace, workspace_bytes, stream, nullptr, /*with_tree=*/false);
 }
 
 extern "C" int kdv_merge_attn_states(const uint16_t* out_a, const float* lse_a, const uint16_t* out_b,

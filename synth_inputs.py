@@ -231,6 +231,43 @@ def make_inputs(*, num_heads: int, qk_nope_dim: int, qk_rope_dim: int, kv_lora_r
                         page_table=page_table, seed=seed, dist=dist)
 
 
+def batch_inputs(dims: dict, Ls, Ts, seed: int = 0, dist: str = "literal", pool_slots: int | None = None,
+                 parents=None) -> list[VerifyInputs]:
+    """C requests of one layer: shared weights and latent pool, each request with its own queries, tree and page
+    table (disjoint pool slots, drawn as one permutation of the pool).
+
+    The shared arrays come from make_inputs(L=Ls[0], T=Ts[0], seed, pool_slots=P); request c's parent and
+    queries are drawn from default_rng([seed, c + 1]) in the order parent, q_nope, q_rope, with the scales of
+    `dist`.  Each returned VerifyInputs describes one request and refers to the shared arrays."""
+    C = len(Ls)
+    if len(Ts) != C or C < 1:
+        raise ValueError("Ls and Ts must have the same length >= 1")
+    total = int(sum(int(L) + int(T) for L, T in zip(Ls, Ts)))
+    P = total if pool_slots is None else int(pool_slots)
+    if P < total:
+        raise ValueError("pool smaller than the requests' rows")
+    base = make_inputs(**dims, L=int(Ls[0]), T=int(Ts[0]), seed=seed, dist=dist, pool_slots=P)
+    H, Dn, Dr = base.H, base.Dn, base.Dr
+    if dist == "literal":
+        s_qn, s_qr = 1 / math.sqrt(Dn), 1 / math.sqrt(Dr)
+    else:
+        s_qn = s_qr = 4.0 if dist == "peak4" else 1.0
+    perm = np.random.default_rng([seed, 0]).permutation(P)[:total].astype(np.int32)
+    reqs, off = [], 0
+    for c in range(C):
+        L, T = int(Ls[c]), int(Ts[c])
+        rng = np.random.default_rng([seed, c + 1])
+        par = random_parents(rng, T) if parents is None else np.asarray(parents[c], dtype=np.int32).copy()
+        q_nope = f32_to_bf16_bits(_normal(rng, (T, H, Dn), s_qn))
+        q_rope = f32_to_bf16_bits(_normal(rng, (T, H, Dr), s_qr))
+        reqs.append(VerifyInputs(H=H, Dn=Dn, Dr=Dr, R=base.R, Dv=base.Dv, L=L, T=T, sm_scale=base.sm_scale,
+                                 parent=par, q_nope=q_nope, q_rope=q_rope, w_uk=base.w_uk, w_uv=base.w_uv,
+                                 c_kv=base.c_kv, k_pe=base.k_pe, page_table=perm[off:off + L + T].copy(),
+                                 seed=seed, dist=dist))
+        off += L + T
+    return reqs
+
+
 # Named workloads (sizes from the tree-verify problem statement; see DESIGN.md for the recipe).
 def tiny(seed: int = 0, dist: str = "literal", **kw) -> VerifyInputs:
     """4 heads, 32/16/64/32 dims, 128-token contiguous prefix, 7-node full binary tree."""

@@ -206,3 +206,60 @@ def test_merge_argument_errors():
         assert call(**bad) == kdv.KDV_ERR_SHAPE, bad
     for field, off in (("out_a", 8), ("out_b", 2), ("out", 8), ("lse_a", 2), ("lse_b", 1), ("lse", 2)):
         assert call(**{field: A + off}) == kdv.KDV_ERR_ALIGN, field
+
+
+def _batch(dims, Ls, Ts, ws_bytes=1 << 40, C=None, **override):
+    la, lp = kdv._host_i32(Ls)
+    ta, tp = kdv._host_i32(Ts)
+    args = dict(q_nope=A, q_rope=A, w_uk=A, w_uv=A, c_kv=A, k_pe=A, pool_slots=1 << 20, page_table=A, mask=A, out=A,
+                lse=None, workspace=A, workspace_bytes=ws_bytes, stream=None)
+    args.update(override)
+    n = len(Ls) if C is None else C
+    return kdv.kdv_verify_mla_attn_batch(dims, n, lp, tp, args["q_nope"], args["q_rope"], args["w_uk"],
+                                         args["w_uv"], args["c_kv"], args["k_pe"], args["pool_slots"],
+                                         args["page_table"], args["mask"], args["out"], args["lse"],
+                                         args["workspace"], args["workspace_bytes"], args["stream"])
+
+
+def test_batch_workspace_of_one_is_single(fixed_splits):
+    d = kdv.make_dims(**KIMI)
+    la, lp = kdv._host_i32([5553])
+    ta, tp = kdv._host_i32([15])
+    assert kdv.kdv_verify_batch_workspace_bytes(d, 1, lp, tp) == kdv.kdv_verify_workspace_bytes(d, 15, 5553)
+
+
+def test_batch_workspace_formula(fixed_splits):
+    # packed q_cat of all nodes + each request's split partials (KDV_SPLITS = 4 splits, capped by its tiles)
+    d = kdv.make_dims(**KIMI)
+    Ls, Ts = [5553, 0, 100], [15, 1, 33]
+    la, lp = kdv._host_i32(Ls)
+    ta, tp = kdv._host_i32(Ts)
+    up = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    rows = 0
+    for L, T in zip(Ls, Ts):
+        tiles = (L + T + 63) // 64
+        want = min(4, tiles)
+        tps = (tiles + want - 1) // want
+        S = (tiles + tps - 1) // tps
+        rows += S * ((T * 64 + 63) // 64) * 64
+    expect = up(sum(Ts) * 64 * 576 * 2) + up(rows * 512 * 2) + up(rows * 8)
+    assert kdv.kdv_verify_batch_workspace_bytes(d, 3, lp, tp) == expect
+
+
+def test_batch_argument_errors(fixed_splits):
+    d = kdv.make_dims(**KIMI)
+    assert _batch(d, [10], [15], C=0) == kdv.KDV_ERR_SHAPE
+    assert _batch(d, [10] * 17, [15] * 17) == kdv.KDV_ERR_SHAPE
+    assert kdv.kdv_verify_mla_attn_batch(d, 1, None, None, A, A, A, A, A, A, 1 << 20, A, A, A, None, A, 1 << 40,
+                                         None) == kdv.KDV_ERR_NULL
+    for Ls, Ts in (([10, 10], [15, 0]), ([10, 10], [15, 65]), ([10, -1], [15, 3])):
+        assert _batch(d, Ls, Ts) == kdv.KDV_ERR_SHAPE, (Ls, Ts)
+    for field in ("q_nope", "page_table", "mask", "out", "workspace"):
+        assert _batch(d, [10, 20], [15, 9], **{field: None}) == kdv.KDV_ERR_NULL, field
+    for field, off in (("q_nope", 8), ("c_kv", 2), ("mask", 2), ("lse", 2), ("workspace", 8)):
+        assert _batch(d, [10, 20], [15, 9], **{field: A + off}) == kdv.KDV_ERR_ALIGN, field
+    la, lp = kdv._host_i32([5553, 20])
+    ta, tp = kdv._host_i32([15, 9])
+    need = kdv.kdv_verify_batch_workspace_bytes(d, 2, lp, tp)
+    assert need > 0
+    assert _batch(d, [5553, 20], [15, 9], ws_bytes=need - 1) == kdv.KDV_ERR_WORKSPACE
