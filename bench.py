@@ -413,6 +413,9 @@ def run(args, torch, si, kdv, dev, hip, stream, sh):
     merge_us = graph_us(merge_launch) if L >= 1 else None
     torch.cuda.synchronize()
 
+    batch_row = batched_verify_row(args, torch, si, kdv, dev, hip, stream, sh, graph_us) if args.workload != "full61" \
+        else None
+
     us_layer_cold = 1e3 * ms_cold / (K * layers_per_step)
     us_layer_hot = 1e3 * ms_hot / (K * layers_per_step)
     tflops_cold = wk["flops"] / (us_layer_cold * 1e-6) / 1e12
@@ -457,6 +460,8 @@ def run(args, torch, si, kdv, dev, hip, stream, sh):
                                      "nodes": int(b_out[2].item()), "timing": "one HIP graph of 200 launches",
                                      "bound": "latency of 31 dependent wave-wide selections"}},
     }
+    if batch_row is not None:
+        result["next_rows"]["batched_verify"] = batch_row
     if ms_split is not None:
         result["next_rows"]["prefix_tail_split"] = {
             "us_per_layer": round(1e3 * ms_split / (K * layers_per_step), 3),
@@ -468,6 +473,61 @@ def run(args, torch, si, kdv, dev, hip, stream, sh):
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, inp, wk, layers_per_step)
     print(json.dumps(result), flush=True)
+
+
+def batched_verify_row(args, torch, si, kdv, dev, hip, stream, sh, graph_us, C=10, L=5553, T=15):
+    """Ten concurrent 15-node trees over 5553-token prefixes (the pages' C = 10 serving level, at the headline
+    shape): one kdv_verify_mla_attn_batch call against the same requests as C single calls (hot buffers)."""
+    log(f"[bench] batched verify: {C} requests")
+    reqs = si.batch_inputs(si.KIMI_DIMS, [L] * C, [T] * C, seed=11)
+    r0 = reqs[0]
+
+    def b16(arrs):
+        return torch.from_numpy(np.ascontiguousarray(np.concatenate(arrs)).view(np.int16)).to(dev)
+    qn, qr = b16([r.q_nope for r in reqs]), b16([r.q_rope for r in reqs])
+    wuk, wuv, ckv, kpe = b16([r0.w_uk]), b16([r0.w_uv]), b16([r0.c_kv]), b16([r0.k_pe])
+    pt = torch.from_numpy(np.concatenate([r.page_table for r in reqs]).astype(np.int32)).to(dev)
+    mask, status = kdv.build_tree_masks([torch.from_numpy(r.parent.astype(np.int32)).to(dev) for r in reqs])
+    dims = kdv.make_dims(**r0.dims())
+    H, Dv = r0.H, r0.Dv
+    out = torch.empty((C * T, H, Dv), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((C * T, H), dtype=torch.float32, device=dev)
+    Ls, Ts = [L] * C, [T] * C
+    ws_b = kdv.verify_batch_workspace_bytes(dims, Ls, Ts)
+    ws = torch.empty((ws_b,), dtype=torch.uint8, device=dev)
+    la, lp = kdv._host_i32(Ls)
+    ta, tp = kdv._host_i32(Ts)
+    base = [t.data_ptr() for t in (wuk, wuv, ckv, kpe)]
+    W = (T + 31) // 32
+
+    def batch_launch():
+        rc = kdv.kdv_verify_mla_attn_batch(dims, C, lp, tp, qn.data_ptr(), qr.data_ptr(), *base, ckv.shape[0],
+                                           pt.data_ptr(), mask.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                           ws.data_ptr(), ws_b, sh)
+        if rc:
+            raise kdv.KdvError(rc, "kdv_verify_mla_attn_batch")
+
+    ws1 = kdv.verify_workspace_bytes(dims, T, L)
+
+    def singles_launch():
+        for c in range(C):
+            rc = kdv.kdv_verify_mla_attn(dims, qn.data_ptr() + c * T * H * r0.Dn * 2,
+                                         qr.data_ptr() + c * T * H * r0.Dr * 2, *base, ckv.shape[0],
+                                         pt.data_ptr() + 4 * c * (L + T), L, T, mask.data_ptr() + 4 * c * T * W,
+                                         out.data_ptr() + c * T * H * Dv * 2, lse.data_ptr() + 4 * c * T * H,
+                                         ws.data_ptr(), ws1, sh)
+            if rc:
+                raise kdv.KdvError(rc, "kdv_verify_mla_attn")
+    batch_us = graph_us(batch_launch, n=20)
+    single_us = graph_us(singles_launch, n=20)
+    torch.cuda.synchronize()
+    assert int(status.sum().item()) == 0
+    flops = sum(work(H, r0.Dn, r0.Dr, r0.R, Dv, L, T, r.parent)["flops"] for r in reqs)
+    return {"requests": C, "prefix_len": L, "tree_nodes": T, "us_per_layer": round(batch_us, 3),
+            "sequential_single_calls_us": round(single_us, 3), "speedup": round(single_us / batch_us, 3),
+            "tflops": round(flops / (batch_us * 1e-6) / 1e12, 2),
+            "frac_bf16_peak": round(flops / (batch_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "timing": "one HIP graph of 20 calls, hot buffers (shared pool of the ten requests: 64 MiB)"}
 
 
 def cpu_baseline(args, inp, wk, layers_per_step):
