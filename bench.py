@@ -46,7 +46,7 @@ COLD_BYTES = 576 << 20
 KERNEL_SOURCES = ("speculative_decoding_tree_parent_amd/csrc/verify.hip",
                   "speculative_decoding_tree_parent_amd/csrc/common.h")
 KERNELS = ("tree_mask_kernel", "q_absorb_kernel", "splitkv_kernel", "combine_up_kernel", "tree_accept_kernel",
-           "draft_tree_kernel")
+           "draft_tree_kernel", "merge_states_kernel")
 
 
 def log(msg):
@@ -304,6 +304,27 @@ def run(args, torch, si, kdv, dev, hip, stream, sh):
         torch.cuda.synchronize()
         return ms
 
+    # Dispatch ledger: (phase, {kernel: dispatches}) in launch order, so that the profile summaries can split a
+    # trace of this run by phase.
+    ledger = []
+    lps = layers_per_step
+
+    def note(phase, counts, n=1):
+        names = {p for p, _ in ledger}
+        name, i = phase, 2
+        while name in names:  # phase names are unique keys
+            name, i = f"{phase} #{i}", i + 1
+        ledger.append([name, {f"{k}_kernel": v * n for k, v in counts.items() if v}])
+    per_step = dict(tree_mask=1, q_absorb=lps, splitkv=lps, combine_up=lps)
+    per_split_step = dict(tree_mask=1, q_absorb=2 * lps, splitkv=2 * lps, combine_up=2 * lps, merge_states=lps)
+
+    def note_timed(what, counts, K):
+        if args.no_graph:
+            note(f"{what}, eager", counts, K)
+        else:
+            note(f"graph {what}, upload replay", counts, K)
+            note(f"graph {what}, timed replay", counts, K)
+
     K, Wm = args.steps, args.warmup
     log(f"[bench] warmup {Wm} steps")
     torch.cuda.synchronize()
@@ -311,15 +332,20 @@ def run(args, torch, si, kdv, dev, hip, stream, sh):
     torch.cuda.synchronize()
     if int(status_t.item()) != 0:
         raise SystemExit("tree status not OK")
+    note("warm-up", per_step, Wm)
     log(f"[bench] timing {K} steps (cold)")
     ms_cold = timed(cold_ptrs, K)
+    note_timed("cold", per_step, K)
     log(f"[bench] timing {K} steps (hot)")
     ms_hot = timed(hot_ptrs, K)
+    note_timed("hot", per_step, K)
     ms_split = None
     if L >= 1:
         log(f"[bench] timing {K} steps of the prefix/tail split (cold)")
         run_steps(cold_ptrs, 2, split_step)
+        note("split warm-up", per_split_step, 2)
         ms_split = timed(cold_ptrs, K, split_step)
+        note_timed("split cold", per_split_step, K)
 
     # per-kernel device time: events stamped by each kernel's own dispatch
     log("[bench] per-kernel timing")
@@ -350,6 +376,7 @@ def run(args, torch, si, kdv, dev, hip, stream, sh):
     for i in range(Kp):
         step_ev(cold_ptrs[i % len(cold_ptrs)], per_step_evs[i])
     torch.cuda.synchronize()
+    note("eager cold, kernel events", per_step, Kp)
     names = ["q_absorb", "splitkv", "combine_up"]
     samples = {n: [] for n in names}
     for ev in ev_list:
@@ -361,7 +388,10 @@ def run(args, torch, si, kdv, dev, hip, stream, sh):
 
     # The tree mask (once per verify step) and the greedy tree accept that follows verification: launch-bound,
     # timed as one HIP graph of many launches.
-    def graph_us(launch, n=200):
+    def graph_us(launch, n=200, counts=None, label=None):
+        """Device time per launch of a graph of n launches (`counts`: dispatches of one launch, for the
+        ledger; uploading replay + timed replay)."""
+        note(label or "launch-timing graph: " + ", ".join(counts or {}), counts or {}, 2 * n)
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
             for _ in range(n):
@@ -378,7 +408,7 @@ def run(args, torch, si, kdv, dev, hip, stream, sh):
         rc = kdv.kdv_build_tree_mask(fixed["parent"], T, fixed["mask"], fixed["status"], sh)
         if rc:
             raise kdv.KdvError(rc, "kdv_build_tree_mask")
-    kern_us["tree_mask"] = graph_us(mask_launch)
+    kern_us["tree_mask"] = graph_us(mask_launch, counts=dict(tree_mask=1))
     _, acc_tok, acc_pred = si.accept_inputs(0, T, follow=0.8, parent=parent_np)
     acc_in = [torch.from_numpy(a.astype(np.int32)).to(dev) for a in (acc_tok, acc_pred)]
     acc_out = [torch.empty((n,), dtype=torch.int32, device=dev) for n in (T, 1, 1, 1)]
@@ -388,7 +418,7 @@ def run(args, torch, si, kdv, dev, hip, stream, sh):
                                  *[t.data_ptr() for t in acc_out], sh)
         if rc:
             raise kdv.KdvError(rc, "kdv_tree_accept")
-    accept_us = graph_us(accept_launch)
+    accept_us = graph_us(accept_launch, counts=dict(tree_accept=1))
     torch.cuda.synchronize()
     n_path = int(acc_out[1].item())
     # best-first draft tree at the session's block 16 / budget 32 (top-8 per position)
@@ -402,7 +432,7 @@ def run(args, torch, si, kdv, dev, hip, stream, sh):
                                       *[t.data_ptr() for t in b_out], sh)
         if rc:
             raise kdv.KdvError(rc, "kdv_build_draft_tree")
-    build_us = graph_us(build_launch)
+    build_us = graph_us(build_launch, counts=dict(draft_tree=1))
     torch.cuda.synchronize()
 
     def merge_launch():
@@ -410,11 +440,10 @@ def run(args, torch, si, kdv, dev, hip, stream, sh):
                                        fixed["out"], fixed["lse"], sh)
         if rc:
             raise kdv.KdvError(rc, "kdv_merge_attn_states")
-    merge_us = graph_us(merge_launch) if L >= 1 else None
+    merge_us = graph_us(merge_launch, counts=dict(merge_states=1)) if L >= 1 else None
     torch.cuda.synchronize()
 
-    batch_row = batched_verify_row(args, torch, si, kdv, dev, hip, stream, sh, graph_us) if args.workload != "full61" \
-        else None
+    batch_row = batched_verify_row(torch, si, kdv, dev, sh, graph_us, note) if args.workload != "full61" else None
 
     us_layer_cold = 1e3 * ms_cold / (K * layers_per_step)
     us_layer_hot = 1e3 * ms_hot / (K * layers_per_step)
@@ -454,6 +483,7 @@ def run(args, torch, si, kdv, dev, hip, stream, sh):
                      "traffic": traffic_from_profile(args.workload),
                      "work_per_launch_gflop": round(wk["flops_splitkv"] / 1e9, 4)},
         "cpu_baseline": None,
+        "dispatch_phases": ledger,
         "next_rows": {"tree_accept": {"us": round(accept_us, 3), "nodes": T, "accepted_path_nodes": n_path,
                                       "timing": "one HIP graph of 200 launches", "bound": "launch latency"},
                       "draft_tree": {"us": round(build_us, 3), "block": 16, "topk": 8, "budget": 32,
@@ -475,7 +505,7 @@ def run(args, torch, si, kdv, dev, hip, stream, sh):
     print(json.dumps(result), flush=True)
 
 
-def batched_verify_row(args, torch, si, kdv, dev, hip, stream, sh, graph_us, C=10, L=5553, T=15):
+def batched_verify_row(torch, si, kdv, dev, sh, graph_us, note, C=10, L=5553, T=15):
     """Ten concurrent 15-node trees over 5553-token prefixes (the pages' C = 10 serving level, at the headline
     shape): one kdv_verify_mla_attn_batch call against the same requests as C single calls (hot buffers)."""
     log(f"[bench] batched verify: {C} requests")
@@ -488,6 +518,7 @@ def batched_verify_row(args, torch, si, kdv, dev, hip, stream, sh, graph_us, C=1
     wuk, wuv, ckv, kpe = b16([r0.w_uk]), b16([r0.w_uv]), b16([r0.c_kv]), b16([r0.k_pe])
     pt = torch.from_numpy(np.concatenate([r.page_table for r in reqs]).astype(np.int32)).to(dev)
     mask, status = kdv.build_tree_masks([torch.from_numpy(r.parent.astype(np.int32)).to(dev) for r in reqs])
+    note("batch: tree masks", dict(tree_mask=C))
     dims = kdv.make_dims(**r0.dims())
     H, Dv = r0.H, r0.Dv
     out = torch.empty((C * T, H, Dv), dtype=torch.bfloat16, device=dev)
@@ -518,8 +549,10 @@ def batched_verify_row(args, torch, si, kdv, dev, hip, stream, sh, graph_us, C=1
                                          ws.data_ptr(), ws1, sh)
             if rc:
                 raise kdv.KdvError(rc, "kdv_verify_mla_attn")
-    batch_us = graph_us(batch_launch, n=20)
-    single_us = graph_us(singles_launch, n=20)
+    call = dict(q_absorb=1, splitkv=1, combine_up=1)
+    batch_us = graph_us(batch_launch, n=20, counts=call, label="batch: graph of batched calls")
+    single_us = graph_us(singles_launch, n=20, counts={k: C * v for k, v in call.items()},
+                         label="batch: graph of single calls")
     torch.cuda.synchronize()
     assert int(status.sum().item()) == 0
     flops = sum(work(H, r0.Dn, r0.Dr, r0.R, Dv, L, T, r.parent)["flops"] for r in reqs)
@@ -637,21 +670,10 @@ def _read_csv(path):
 
 
 def _phases(bench, kernel):
-    """Dispatch index ranges of bench.py's phases for one kernel, in launch order."""
-    W, K, lps, n = bench["warmup"], bench["steps"], bench["config"]["layers_per_step"], bench["kernel_calls"]
-    if kernel in ("tree_accept_kernel", "draft_tree_kernel"):  # only in the launch-timing graphs at the end
-        edges = [("warm-up", 0), ("graph cold, upload replay", 0), ("graph cold, timed replay", 0),
-                 ("graph hot, upload replay", 0), ("graph hot, timed replay", 0), ("eager cold, kernel events", 0),
-                 ("launch-timing graph", 400)]
-    else:
-        per = 1 if kernel == "tree_mask_kernel" else lps
-        n_eager = n // lps if kernel == "tree_mask_kernel" else n
-        edges = [("warm-up", W * per), ("graph cold, upload replay", K * per), ("graph cold, timed replay", K * per),
-                 ("graph hot, upload replay", K * per), ("graph hot, timed replay", K * per),
-                 ("eager cold, kernel events", n_eager),
-                 ("launch-timing graph", 400 if kernel == "tree_mask_kernel" else 0)]
+    """Dispatch index ranges of one kernel in each phase of a bench.py run (its dispatch ledger), in order."""
     out, a = {}, 0
-    for name, c in edges:
+    for name, counts in bench["dispatch_phases"]:
+        c = counts.get(kernel, 0)
         out[name] = (a, a + c)
         a += c
     return out, a
@@ -690,9 +712,12 @@ def summarize_profile(d, workload):
              f"bench.py without the tracer: {plain['us_per_layer']} us/layer cold, "
              f"{plain['hot']['us_per_layer']} us/layer hot, {plain['value']} {plain['unit']}; under the tracer: "
              f"{bench['us_per_layer']} us/layer cold.", "",
-             "Average kernel duration (us) from rocprofv3 `--kernel-trace`, by phase of the bench run:", ""]
-    kinds = None
-    rows_out = []
+             "Average kernel duration (us) from rocprofv3 `--kernel-trace`, by phase of the bench run (phases "
+             "from the run's dispatch ledger; the 'batch' phases run the ten-request workload, the 'split' phases "
+             "the prefix/tail split, so their durations are of other shapes):", "",
+             "| kernel | phase | dispatches | average us |", "|---|---|---|---|"]
+    ev = {f"{k}_kernel": v for k, v in plain["kernels_us"].items()}
+    eager = {}
     for k in KERNELS:
         if k not in durs:
             continue
@@ -700,18 +725,17 @@ def summarize_profile(d, workload):
         ph, total = _phases(bench, k)
         if len(lst) != total:
             raise SystemExit(f"{k}: {len(lst)} dispatches traced, {total} expected")
-        kinds = list(ph)
-        avg = {}
         for name, (a, b) in ph.items():
             seg = lst[a:b]
-            avg[name] = sum(e - s for _, s, e in seg) / len(seg) / 1e3 if seg else float("nan")
-        rows_out.append((k, len(lst), avg))
-    lines.append("| kernel | dispatches | " + " | ".join(kinds) + " | bench.py events, no tracer |")
-    lines.append("|---|---|" + "---|" * (len(kinds) + 1))
-    ev = {f"{k}_kernel": v for k, v in plain["kernels_us"].items()}
-    for k, n, avg in rows_out:
-        lines.append(f"| {k} | {n} | " + " | ".join(f"{avg[p]:.2f}" for p in kinds) +
-                     f" | {ev.get(k, float('nan')):.2f} |")
+            if seg:
+                avg = sum(e - s for _, s, e in seg) / len(seg) / 1e3
+                lines.append(f"| {k} | {name} | {len(seg)} | {avg:.2f} |")
+                if name == "eager cold, kernel events":
+                    eager[k] = avg
+    lines += ["", "Eager cold launches under the tracer against bench.py's kernel-stamped HIP events without it:", "",
+              "| kernel | traced average us | bench.py events us |", "|---|---|---|"]
+    for k, v in eager.items():
+        lines.append(f"| {k} | {v:.2f} | {ev.get(k, float('nan')):.2f} |")
     # step span in the timed cold replay (includes gaps between kernels)
     tm = sorted(durs["tree_mask_kernel"])
     ph, _ = _phases(bench, "tree_mask_kernel")
@@ -758,6 +782,8 @@ def summarize_profile(d, workload):
         fv, wv = fetch[k][a:b], write[k][a:b]
         if len(fetch[k]) != total or len(write[k]) != total:
             raise SystemExit(f"{k}: counter dispatch count mismatch")
+        if not fv:  # a kernel of the other measurements only (not launched by the verify call)
+            continue
         fk, wk_ = sum(fv) / len(fv), sum(wv) / len(wv)
         fb_bytes, wb_bytes = fk * f_fac * 1024, wk_ * w_fac * 1024
         lines.append(f"| {k} | {fk:.1f} | {wk_:.1f} | {fb_bytes / 1e6:.3f} | {wb_bytes / 1e6:.3f} |")
