@@ -207,7 +207,7 @@ size_t kdv_verify_batch_workspace_bytes(const kdv_mla_dims* d, int32_t C, const 
  *   page_table : device int32 [L] (prefix positions only).
  *   L          : >= 1.
  *   lse        : nullable as before, but the merge below needs it.
- *   workspace  : kdv_verify_workspace_bytes(d, T, L) bytes always suffice.
+ *   workspace  : kdv_prefix_workspace_bytes(d, T, L) bytes, which never exceeds kdv_verify_workspace_bytes(d, T, L).
  * The tail part is kdv_verify_mla_attn with L = 0 and a page table of the T tree rows; the two results
  * combine with kdv_merge_attn_states into the result of one kdv_verify_mla_attn over the whole cache.
  * Returns KDV_OK or a negative kdv_status (KDV_ERR_SHAPE for L < 1; nothing enqueued on error). */
@@ -215,6 +215,9 @@ int kdv_prefix_mla_attn(const kdv_mla_dims* d, const uint16_t* q_nope, const uin
                         const uint16_t* w_uv, const uint16_t* c_kv, const uint16_t* k_pe, int64_t pool_slots,
                         const int32_t* page_table, int32_t L, int32_t T, uint16_t* out, float* lse, void* workspace,
                         size_t workspace_bytes, void* stream);
+
+/* Workspace bytes for kdv_prefix_mla_attn (L >= 1); 0 if unsupported.  At most kdv_verify_workspace_bytes(d, T, L). */
+size_t kdv_prefix_workspace_bytes(const kdv_mla_dims* d, int32_t T, int32_t L);
 
 /* Merge of two attention results over disjoint sets of KV positions into the result over their union (the
  * merge that joins the prefix and tree-tail parts above; the same operator merges the KV splits inside

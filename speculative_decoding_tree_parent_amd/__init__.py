@@ -29,6 +29,7 @@ KDV_MAX_DRAFT_ENTRIES = 4096
 KDV_MAX_BATCH = 16
 
 EXPORTED = ("kdv_build_draft_tree", "kdv_build_tree_mask", "kdv_merge_attn_states", "kdv_prefix_mla_attn",
+            "kdv_prefix_workspace_bytes",
             "kdv_tree_accept", "kdv_verify_batch_workspace_bytes", "kdv_verify_mla_attn_batch",
             "kdv_verify_workspace_bytes", "kdv_verify_mla_attn", "kdv_verify_mla_attn_profiled",
             "kdv_verify_num_splits", "kdv_status_string")
@@ -74,6 +75,8 @@ def _load() -> ctypes.CDLL:
     lib.kdv_verify_batch_workspace_bytes.restype = sz
     lib.kdv_prefix_mla_attn.argtypes = [dims_p, vp, vp, vp, vp, vp, vp, i64, vp, i32, i32, vp, vp, vp, sz, vp]
     lib.kdv_prefix_mla_attn.restype = ctypes.c_int
+    lib.kdv_prefix_workspace_bytes.argtypes = [dims_p, i32, i32]
+    lib.kdv_prefix_workspace_bytes.restype = sz
     lib.kdv_merge_attn_states.argtypes = [vp, vp, vp, vp, i64, i32, vp, vp, vp]
     lib.kdv_merge_attn_states.restype = ctypes.c_int
     lib.kdv_status_string.argtypes = [ctypes.c_int]
@@ -151,6 +154,10 @@ def kdv_prefix_mla_attn(dims: KdvMlaDims, q_nope: int, q_rope: int, w_uk: int, w
                         workspace_bytes: int, stream: int | None) -> int:
     return _lib.kdv_prefix_mla_attn(ctypes.byref(dims), q_nope, q_rope, w_uk, w_uv, c_kv, k_pe, pool_slots,
                                     page_table, L, T, out, lse, workspace, workspace_bytes, stream)
+
+
+def kdv_prefix_workspace_bytes(dims: KdvMlaDims, T: int, L: int) -> int:
+    return _lib.kdv_prefix_workspace_bytes(ctypes.byref(dims), T, L)
 
 
 def kdv_merge_attn_states(out_a: int, lse_a: int, out_b: int, lse_b: int, rows: int, dv: int, out: int,
@@ -294,7 +301,10 @@ def prefix_mla_attn(dims: KdvMlaDims, q_nope, q_rope, w_uk, w_uv, c_kv, k_pe, pa
     if lse is None:
         lse = torch.empty((T, H), dtype=torch.float32, device=q_nope.device)
     if workspace is None:
-        workspace = torch.empty((verify_workspace_bytes(dims, T, L),), dtype=torch.uint8, device=q_nope.device)
+        n = kdv_prefix_workspace_bytes(dims, T, L)
+        if n == 0:
+            raise KdvError(KDV_ERR_SHAPE, "kdv_prefix_workspace_bytes")
+        workspace = torch.empty((n,), dtype=torch.uint8, device=q_nope.device)
     rc = kdv_prefix_mla_attn(dims, bf(q_nope, "q_nope"), bf(q_rope, "q_rope"), bf(w_uk, "w_uk"), bf(w_uv, "w_uv"),
                              bf(c_kv, "c_kv"), bf(k_pe, "k_pe"), c_kv.shape[0],
                              _ptr(page_table, torch.int32, "page_table"), L, T, bf(out, "out"),

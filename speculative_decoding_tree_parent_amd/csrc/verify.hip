@@ -857,6 +857,8 @@ static int device_cu_count() {
 // on one XCD, i.e. NUM_XCD * floor(CUs per XCD / query tiles) splits, the CUs shared among the requests in
 // proportion to their tile work.  Every split gets the same whole number of 64-row tiles except possibly the
 // last.  The environment variable KDV_SPLITS, if set, fixes every request's split count instead.
+// The tiles per split are always sized for the L + T rows of the full verify, also for a prefix-only pass,
+// so that a prefix-only pass never has more splits (nor needs more workspace) than the full call.
 static int make_plan(const kdv_mla_dims* d, int C, const int32_t* Ls, const int32_t* Ts, Plan* p,
                      bool with_tree = true) {
   if (d == nullptr || Ls == nullptr || Ts == nullptr) return KDV_ERR_NULL;
@@ -906,8 +908,9 @@ static int make_plan(const kdv_mla_dims* d, int C, const int32_t* Ls, const int3
       want = (r.m_tiles <= per_xcd) ? NUM_XCD * (per_xcd / r.m_tiles) : share / r.m_tiles;
       if (want < 1) want = 1;
     }
-    if (want > ntiles[c]) want = ntiles[c];
-    r.tiles_per_split = (ntiles[c] + want - 1) / want;
+    const int nt_plan = (r.L + r.T + KV_TILE - 1) / KV_TILE;  // tiles of the full verify (see above)
+    if (want > nt_plan) want = nt_plan;
+    r.tiles_per_split = (nt_plan + want - 1) / want;
     r.splits = (ntiles[c] + r.tiles_per_split - 1) / r.tiles_per_split;
     r.xoff = (int)(xoff % NUM_XCD);
     xoff += r.splits;
@@ -989,6 +992,12 @@ extern "C" size_t kdv_verify_batch_workspace_bytes(const kdv_mla_dims* d, int32_
                                                    const int32_t* T) {
   kdv::Plan p;
   if (kdv::make_plan(d, C, L, T, &p) != KDV_OK) return 0;
+  return p.total;
+}
+
+extern "C" size_t kdv_prefix_workspace_bytes(const kdv_mla_dims* d, int32_t T, int32_t L) {
+  kdv::Plan p;
+  if (kdv::make_plan(d, 1, &L, &T, &p, /*with_tree=*/false) != KDV_OK) return 0;
   return p.total;
 }
 

@@ -263,3 +263,16 @@ def test_batch_argument_errors(fixed_splits):
     need = kdv.kdv_verify_batch_workspace_bytes(d, 2, lp, tp)
     assert need > 0
     assert _batch(d, [5553, 20], [15, 9], ws_bytes=need - 1) == kdv.KDV_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("splits", ["1", "3", "16", "63", "64", "100"])
+def test_prefix_workspace_never_exceeds_verify(splits, monkeypatch):
+    # sizing only (no call is made): a prefix pass's plan never has more splits than the full verify's
+    monkeypatch.setenv("KDV_SPLITS", splits)
+    for dims in (KIMI, dict(KIMI, num_heads=8), TINY):
+        d = kdv.make_dims(**dims)
+        for T in (1, 15, 32, 64):
+            for L in (1, 63, 64, 65, 2048 * 64, 131072, 200000):
+                p, v = kdv.kdv_prefix_workspace_bytes(d, T, L), kdv.kdv_verify_workspace_bytes(d, T, L)
+                assert 0 < p <= v, (dims, T, L, p, v)
+    assert kdv.kdv_prefix_workspace_bytes(kdv.make_dims(**KIMI), 15, 0) == 0

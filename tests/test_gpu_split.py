@@ -63,7 +63,10 @@ CASES = [(si.tiny, dict(seed=0), None), (si.tiny, dict(seed=1, dist="peak4"), No
          (si.make_inputs, dict(**si.TINY_DIMS, L=1, T=7, seed=4, parent=[-1, 0, 0, 1, 1, 2, 2]), None),
          (si.make_inputs, dict(**si.TINY_DIMS, L=65, T=33, seed=5), None),
          (si.kimi, dict(L=64, T=15, seed=1), [0, 5, 63]), (si.kimi, dict(L=300, T=9, seed=2), [1, 40]),
-         (si.kimi, dict(L=5553, T=15, seed=0), [0, 31, 63])]
+         (si.kimi, dict(L=5553, T=15, seed=0), [0, 31, 63]),
+         # one GPU's share of the 61-layer step: 8 heads, 32 nodes, 131072-token prefix (the prefix pass plans
+         # 64 splits of 32 tiles, the full verify 63 of 33)
+         (si.make_inputs, dict(**si.FULL61_SHAPE, L=131072, T=32, seed=3), [0, 7])]
 
 
 @pytest.mark.parametrize("maker,kw,heads", CASES)
