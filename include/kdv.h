@@ -162,6 +162,19 @@ int kdv_verify_mla_attn(const kdv_mla_dims* d, const uint16_t* q_nope, const uin
                         int64_t pool_slots, const int32_t* page_table, int32_t L, int32_t T, const uint32_t* mask,
                         uint16_t* out, float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
+/* kdv_verify_mla_attn that builds the tree's ancestor mask itself: the mask of kdv_build_tree_mask(parent, T)
+ * is written to `mask` (device uint32 [T][(T+31)/32], written; the caller can pass it to kdv_verify_mla_attn
+ * for the other layers of the step) and `status` (device int32, nullable) by one extra block of the call's
+ * first kernel, so the verify step needs no separate mask launch.  Other arguments and results as
+ * kdv_verify_mla_attn; KDV_ERR_NULL if parent is NULL, KDV_ERR_ALIGN if parent or status is not 4-byte
+ * aligned.  A malformed tree is reported in `status` as for kdv_build_tree_mask, and its rows attend as that
+ * mask says. */
+int kdv_verify_mla_attn_tree(const kdv_mla_dims* d, const uint16_t* q_nope, const uint16_t* q_rope,
+                             const uint16_t* w_uk, const uint16_t* w_uv, const uint16_t* c_kv, const uint16_t* k_pe,
+                             int64_t pool_slots, const int32_t* page_table, int32_t L, int32_t T,
+                             const int32_t* parent, uint32_t* mask, int32_t* status, uint16_t* out, float* lse,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
 /* Same computation as kdv_verify_mla_attn, for measurement: `events` points to six hipEvent_t created by the
  * caller.  events[2k] and events[2k+1] receive the start and end timestamps of kernel k as the hardware dispatches
  * it (k = 0 q absorption, 1 split-KV pass, 2 split combine with the W_UV up-projection), so hipEventElapsedTime

@@ -32,6 +32,7 @@ EXPORTED = ("kdv_build_draft_tree", "kdv_build_tree_mask", "kdv_merge_attn_state
             "kdv_prefix_workspace_bytes",
             "kdv_tree_accept", "kdv_verify_batch_workspace_bytes", "kdv_verify_mla_attn_batch",
             "kdv_verify_workspace_bytes", "kdv_verify_mla_attn", "kdv_verify_mla_attn_profiled",
+            "kdv_verify_mla_attn_tree",
             "kdv_verify_num_splits", "kdv_status_string")
 
 
@@ -68,6 +69,9 @@ def _load() -> ctypes.CDLL:
     lib.kdv_verify_mla_attn_profiled.argtypes = [dims_p, vp, vp, vp, vp, vp, vp, i64, vp, i32, i32, vp, vp, vp, vp,
                                                  sz, vp, vp]
     lib.kdv_verify_mla_attn_profiled.restype = ctypes.c_int
+    lib.kdv_verify_mla_attn_tree.argtypes = [dims_p, vp, vp, vp, vp, vp, vp, i64, vp, i32, i32, vp, vp, vp, vp, vp,
+                                             vp, sz, vp]
+    lib.kdv_verify_mla_attn_tree.restype = ctypes.c_int
     lib.kdv_verify_mla_attn_batch.argtypes = [dims_p, i32, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, vp,
                                               sz, vp]
     lib.kdv_verify_mla_attn_batch.restype = ctypes.c_int
@@ -125,6 +129,15 @@ def kdv_verify_mla_attn_profiled(dims: KdvMlaDims, q_nope: int, q_rope: int, w_u
     return _lib.kdv_verify_mla_attn_profiled(ctypes.byref(dims), q_nope, q_rope, w_uk, w_uv, c_kv, k_pe, pool_slots,
                                              page_table, L, T, mask, out, lse, workspace, workspace_bytes, stream,
                                              events)
+
+
+def kdv_verify_mla_attn_tree(dims: KdvMlaDims, q_nope: int, q_rope: int, w_uk: int, w_uv: int, c_kv: int, k_pe: int,
+                             pool_slots: int, page_table: int, L: int, T: int, parent: int, mask: int,
+                             status: int | None, out: int, lse: int | None, workspace: int, workspace_bytes: int,
+                             stream: int | None) -> int:
+    return _lib.kdv_verify_mla_attn_tree(ctypes.byref(dims), q_nope, q_rope, w_uk, w_uv, c_kv, k_pe, pool_slots,
+                                         page_table, L, T, parent, mask, status, out, lse, workspace,
+                                         workspace_bytes, stream)
 
 
 def _host_i32(values):
@@ -395,3 +408,38 @@ def verify_mla_attn_batch(dims: KdvMlaDims, q_nope, q_rope, w_uk, w_uv, c_kv, k_
     if rc != KDV_OK:
         raise KdvError(rc, "kdv_verify_mla_attn_batch")
     return out, lse
+
+
+def verify_mla_attn_tree(dims: KdvMlaDims, q_nope, q_rope, w_uk, w_uv, c_kv, k_pe, page_table, L: int, parent,
+                         mask=None, status=None, out=None, lse=None, workspace=None, stream=None):
+    """verify_mla_attn that builds the ancestor mask from `parent` (int32 [T] device tensor) in the same call.
+
+    Returns (out, lse or None, mask int32 [T][W], status int32 [1])."""
+    import torch
+    T = q_nope.shape[0]
+    H = dims.num_heads
+    dev = q_nope.device
+
+    def bf(t, what):
+        if t.dtype == torch.bfloat16:
+            return _ptr(t, torch.bfloat16, what)
+        return _ptr(t, torch.int16, what)
+
+    if mask is None:
+        mask = torch.empty((T, (T + 31) // 32), dtype=torch.int32, device=dev)
+    if status is None:
+        status = torch.empty((1,), dtype=torch.int32, device=dev)
+    if out is None:
+        out = torch.empty((T, H, dims.v_head_dim), dtype=torch.bfloat16, device=dev)
+    if workspace is None:
+        workspace = torch.empty((verify_workspace_bytes(dims, T, L),), dtype=torch.uint8, device=dev)
+    lse_ptr = None if lse is None else _ptr(lse, torch.float32, "lse")
+    rc = kdv_verify_mla_attn_tree(dims, bf(q_nope, "q_nope"), bf(q_rope, "q_rope"), bf(w_uk, "w_uk"),
+                                  bf(w_uv, "w_uv"), bf(c_kv, "c_kv"), bf(k_pe, "k_pe"), c_kv.shape[0],
+                                  _ptr(page_table, torch.int32, "page_table"), L, T, _ptr(parent, torch.int32, "parent"),
+                                  _ptr(mask, torch.int32, "mask"), _ptr(status, torch.int32, "status"),
+                                  bf(out, "out"), lse_ptr, _ptr(workspace, torch.uint8, "workspace"),
+                                  workspace.numel(), _stream_handle(stream))
+    if rc != KDV_OK:
+        raise KdvError(rc, "kdv_verify_mla_attn_tree")
+    return out, lse, mask, status

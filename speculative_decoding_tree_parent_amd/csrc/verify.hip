@@ -19,6 +19,7 @@
 #include <stdlib.h>
 
 #include "common.h"
+#include "tree_mask.h"
 
 namespace kdv {
 
@@ -571,7 +572,14 @@ template <int DN, int R, int DR>
 __global__ __launch_bounds__(NTHREADS) void q_absorb_kernel(const uint16_t* __restrict__ q_nope,
                                                             const uint16_t* __restrict__ q_rope,
                                                             const uint16_t* __restrict__ w_uk,
-                                                            uint16_t* __restrict__ q_cat, int T, int H) {
+                                                            uint16_t* __restrict__ q_cat, int T, int H,
+                                                            const int32_t* __restrict__ parent,
+                                                            uint32_t* __restrict__ mask,
+                                                            int32_t* __restrict__ status) {
+  if (blockIdx.x == H) {  // a call that builds its own tree mask has one extra column of blocks (uniform exit)
+    if (blockIdx.y == 0 && threadIdx.x < 64) build_ancestor_mask(parent, T, mask, status, threadIdx.x);
+    return;
+  }
   constexpr int DQ = R + DR;
   constexpr int RB = 128;                    // latent columns per workgroup
   constexpr int WINS = DN * RB * 2 / 1024;   // DMA instructions for the W_UK block
@@ -950,13 +958,15 @@ template <int DN, int R, int DR, int DV>
 static void launch_all(const Plan& pl, float sm_scale, const uint16_t* q_nope, const uint16_t* q_rope,
                        const uint16_t* w_uk, const uint16_t* w_uv, const uint16_t* c_kv, const uint16_t* k_pe,
                        const int32_t* page_table, const uint32_t* mask, uint16_t* out, float* lse, char* ws,
-                       hipStream_t st, hipEvent_t const* ev) {
+                       hipStream_t st, hipEvent_t const* ev, const int32_t* parent, int32_t* status) {
   uint16_t* q_cat = reinterpret_cast<uint16_t*>(ws + pl.off_qcat);
   uint16_t* part_o = reinterpret_cast<uint16_t*>(ws + pl.off_po);
   float2* part_ml = reinterpret_cast<float2*>(ws + pl.off_pml);
-  // the query absorption is per node: the packed nodes of all requests in one grid
-  launch(q_absorb_kernel<DN, R, DR>, dim3(pl.H, (R + 127) / 128), st, ev ? ev + 0 : nullptr, q_nope, q_rope, w_uk,
-         q_cat, pl.nodes, pl.H);
+  // The query absorption is per node: the packed nodes of all requests in one grid.  With `parent` (one
+  // request) an extra block builds the tree mask the split-KV kernel then reads.
+  launch(q_absorb_kernel<DN, R, DR>, dim3(pl.H + (parent != nullptr ? 1 : 0), (R + 127) / 128), st,
+         ev ? ev + 0 : nullptr, q_nope, q_rope, w_uk, q_cat, pl.nodes, pl.H, parent, const_cast<uint32_t*>(mask),
+         status);
   const float scale_log2 = sm_scale * 1.44269504088896340736f;
   if (pl.ba.n == 1) {
     BatchArgs<1> one;
@@ -1011,7 +1021,8 @@ static int verify_impl(const kdv_mla_dims* d, int32_t C, const int32_t* Ls, cons
                        const uint16_t* q_nope, const uint16_t* q_rope, const uint16_t* w_uk, const uint16_t* w_uv,
                        const uint16_t* c_kv, const uint16_t* k_pe, int64_t pool_slots, const int32_t* page_table,
                        const uint32_t* mask, uint16_t* out, float* lse, void* workspace, size_t workspace_bytes,
-                       void* stream, hipEvent_t const* ev, bool with_tree = true) {
+                       void* stream, hipEvent_t const* ev, bool with_tree = true,
+                       const int32_t* parent = nullptr, int32_t* status = nullptr) {
   using namespace kdv;
   if (d == nullptr || Ls == nullptr || Ts == nullptr || q_nope == nullptr || q_rope == nullptr ||
       w_uk == nullptr || w_uv == nullptr || c_kv == nullptr || k_pe == nullptr || page_table == nullptr ||
@@ -1023,7 +1034,8 @@ static int verify_impl(const kdv_mla_dims* d, int32_t C, const int32_t* Ls, cons
     if (Ts[c] < 1 || Ts[c] > KDV_MAX_TREE_NODES || Ls[c] < (with_tree ? 0 : 1)) return KDV_ERR_SHAPE;
   if (misaligned(q_nope, 16) || misaligned(q_rope, 16) || misaligned(w_uk, 16) || misaligned(w_uv, 16) ||
       misaligned(c_kv, 16) || misaligned(k_pe, 16) || misaligned(out, 16) || misaligned(workspace, 16) ||
-      misaligned(page_table, 4) || misaligned(mask, 4) || misaligned(lse, 4))
+      misaligned(page_table, 4) || misaligned(mask, 4) || misaligned(lse, 4) || misaligned(parent, 4) ||
+      misaligned(status, 4))
     return KDV_ERR_ALIGN;
   Plan pl;
   const int st = make_plan(d, C, Ls, Ts, &pl, with_tree);
@@ -1034,10 +1046,10 @@ static int verify_impl(const kdv_mla_dims* d, int32_t C, const int32_t* Ls, cons
   (void)hipGetLastError();
   if (sid == SHAPE_KIMI)
     launch_all<128, 512, 64, 128>(pl, d->sm_scale, q_nope, q_rope, w_uk, w_uv, c_kv, k_pe, page_table, mask, out,
-                                  lse, ws, s, ev);
+                                  lse, ws, s, ev, parent, status);
   else
     launch_all<32, 64, 16, 32>(pl, d->sm_scale, q_nope, q_rope, w_uk, w_uv, c_kv, k_pe, page_table, mask, out, lse,
-                               ws, s, ev);
+                               ws, s, ev, parent, status);
   return hipGetLastError() == hipSuccess ? KDV_OK : KDV_ERR_HIP;
 }
 
@@ -1059,6 +1071,17 @@ extern "C" int kdv_verify_mla_attn_profiled(const kdv_mla_dims* d, const uint16_
   if (events == nullptr) return KDV_ERR_NULL;
   return verify_impl(d, 1, &L, &T, q_nope, q_rope, w_uk, w_uv, c_kv, k_pe, pool_slots, page_table, mask, out, lse,
                      workspace, workspace_bytes, stream, reinterpret_cast<hipEvent_t const*>(events));
+}
+
+extern "C" int kdv_verify_mla_attn_tree(const kdv_mla_dims* d, const uint16_t* q_nope, const uint16_t* q_rope,
+                                        const uint16_t* w_uk, const uint16_t* w_uv, const uint16_t* c_kv,
+                                        const uint16_t* k_pe, int64_t pool_slots, const int32_t* page_table,
+                                        int32_t L, int32_t T, const int32_t* parent, uint32_t* mask, int32_t* status,
+                                        uint16_t* out, float* lse, void* workspace, size_t workspace_bytes,
+                                        void* stream) {
+  if (parent == nullptr) return KDV_ERR_NULL;
+  return verify_impl(d, 1, &L, &T, q_nope, q_rope, w_uk, w_uv, c_kv, k_pe, pool_slots, page_table, mask, out, lse,
+                     workspace, workspace_bytes, stream, nullptr, true, parent, status);
 }
 
 extern "C" int kdv_verify_mla_attn_batch(const kdv_mla_dims* d, int32_t C, const int32_t* L, const int32_t* T,

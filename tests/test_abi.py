@@ -276,3 +276,18 @@ def test_prefix_workspace_never_exceeds_verify(splits, monkeypatch):
                 p, v = kdv.kdv_prefix_workspace_bytes(d, T, L), kdv.kdv_verify_workspace_bytes(d, T, L)
                 assert 0 < p <= v, (dims, T, L, p, v)
     assert kdv.kdv_prefix_workspace_bytes(kdv.make_dims(**KIMI), 15, 0) == 0
+
+
+def test_tree_verify_argument_errors(fixed_splits):
+    d = kdv.make_dims(**KIMI)
+
+    def call(**kw):
+        a = dict(parent=A, mask=A, status=None, q_nope=A, out=A)
+        a.update(kw)
+        return kdv.kdv_verify_mla_attn_tree(d, a["q_nope"], A, A, A, A, A, 1 << 20, A, 100, 15, a["parent"],
+                                            a["mask"], a["status"], a["out"], None, A, 0, None)
+    assert call(parent=None) == kdv.KDV_ERR_NULL
+    assert call(mask=None) == kdv.KDV_ERR_NULL
+    assert call(parent=A + 2) == kdv.KDV_ERR_ALIGN
+    assert call(status=A + 1) == kdv.KDV_ERR_ALIGN
+    assert call() == kdv.KDV_ERR_WORKSPACE  # workspace_bytes = 0: rejected before any launch
