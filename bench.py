@@ -167,9 +167,10 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build measures one GPU only: the tree-verify attention of one layer "
-                                   "runs on a single MI355X; multi-GPU sharding is described in DESIGN.md, "
-                                   "not run", "n_gpus": args.gpus}), flush=True)
+        print(json.dumps({"error": "one GPU only: the tree-verify attention of one layer runs on a single "
+                                   "MI355X; splitting it over several GPUs (heads, or the KV sequence with one "
+                                   "exchange of split partials) is not implemented", "n_gpus": args.gpus}),
+              flush=True)
         sys.exit(2)
 
     import torch

@@ -6,7 +6,7 @@ Source: "The Architecture of Diagnosis...", section "Phase 1: Custom CUDA Kernel
 forward pass the engine selects, greedily and on the device, the longest prefix of accepted tokens; the same
 page's composition test chains build -> verify -> accept with no host round trip.
 
-Readings where the page is silent (listed again in the design doc):
+Readings where the page is silent:
   * node 0 is the root, the position whose token is already committed; parent[i] < i (as for the mask);
   * pred[t] is the target model's greedy prediction after the prefix that ends at node t (its argmax);
   * a child c of node p is accepted when its draft token equals pred[p]; the walk starts at the root and

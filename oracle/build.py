@@ -6,7 +6,7 @@ Source: "The Architecture of Diagnosis...", section "Phase 1: Custom CUDA Kernel
 built best-first on the device instead of with a host-side priority queue; the session's DDTree settings are
 block 16 and budget 32 ("Three Acts of Engineering...", the B300 projection).
 
-Readings where the pages are silent (listed again in the design doc):
+Readings where the pages are silent:
   * the drafter gives, for each of the `block` positions after the committed token, its K best tokens tok[d][r]
     with log-probabilities logp[d][r], sorted so that logp[d][0] >= logp[d][1] >= ... (the top-k of each
     position's distribution); positions are independent, so a root path's score is the float32 sum of its

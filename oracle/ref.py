@@ -24,7 +24,7 @@ What is computed (sources are the three pages on the DDTree engine):
   un-absorbed form (K = W_UK c, V = W_UV c materialised per head) so that the
   two can be checked against each other.
 
-Readings where the pages are silent (listed again in the design doc):
+Readings where the pages are silent:
   * node 0 is the root (parent -1); parent[i] < i (topological order);
   * tree node i's own latent row sits at logical position L + i;
   * q_rope and k_pe arrive after RoPE; the softmax scale is an argument;

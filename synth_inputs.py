@@ -268,7 +268,7 @@ def batch_inputs(dims: dict, Ls, Ts, seed: int = 0, dist: str = "literal", pool_
     return reqs
 
 
-# Named workloads (sizes from the tree-verify problem statement; see the design doc for the recipe).
+# Named workloads (the shapes of the pages' verify workloads).
 def tiny(seed: int = 0, dist: str = "literal", **kw) -> VerifyInputs:
     """4 heads, 32/16/64/32 dims, 128-token contiguous prefix, 7-node full binary tree."""
     args = dict(TINY_DIMS, L=128, T=7, seed=seed, parent=[-1, 0, 0, 1, 1, 2, 2], dist=dist)
