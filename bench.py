@@ -451,6 +451,8 @@ def run(args, torch, si, kdv, dev, hip, stream, sh):
 
     batch_row = batched_verify_row(torch, si, kdv, dev, sh, graph_us, note) if args.workload != "full61" else None
 
+    mfma_peak = measured_mfma_peak(torch, kdv, dev, hip, sh, note)
+
     us_layer_cold = 1e3 * ms_cold / (K * layers_per_step)
     us_layer_hot = 1e3 * ms_hot / (K * layers_per_step)
     tflops_cold = wk["flops"] / (us_layer_cold * 1e-6) / 1e12
@@ -487,6 +489,8 @@ def run(args, torch, si, kdv, dev, hip, stream, sh):
         "roofline": {"bound": "mfma", "kernel": "splitkv", "achieved": round(sk_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(sk_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_from_profile(args.workload),
+                     "measured_mfma_peak": round(mfma_peak, 1),
+                     "frac_of_measured_peak": round(sk_tflops / mfma_peak, 4),
                      "work_per_launch_gflop": round(wk["flops_splitkv"] / 1e9, 4)},
         "cpu_baseline": None,
         "dispatch_phases": ledger,
@@ -509,6 +513,25 @@ def run(args, torch, si, kdv, dev, hip, stream, sh):
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, inp, wk, layers_per_step)
     print(json.dumps(result), flush=True)
+
+
+def measured_mfma_peak(torch, kdv, dev, hip, sh, note, iters=2048):
+    """bf16 MFMA issue-rate ceiling on this GPU, TFLOP/s: two 4-wave workgroups per CU, each wave four
+    independent 32x32x16 chains (kdv_mfma_probe), timed with HIP events on the bench stream."""
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    blocks = 2 * cus
+    sink = torch.empty((blocks * 256,), dtype=torch.float32, device=dev)
+    for _ in range(2):  # the first launch is untimed
+        e0, e1 = hip.event(), hip.event()
+        hip.record(e0, sh)
+        rc = kdv.kdv_mfma_probe(iters, sink.data_ptr(), blocks, sh)
+        if rc:
+            raise kdv.KdvError(rc, "kdv_mfma_probe")
+        hip.record(e1, sh)
+        torch.cuda.synchronize()
+        ms = hip.elapsed_ms(e0, e1)
+    note("mfma probe", {}, 0)
+    return blocks * 4 * iters * 4 * 32768 / (ms * 1e-3) / 1e12
 
 
 def batched_verify_row(torch, si, kdv, dev, sh, graph_us, note, C=10, L=5553, T=15):

@@ -251,6 +251,13 @@ int kdv_merge_attn_states(const uint16_t* out_a, const float* lse_a, const uint1
  * (diagnostic; 0 if unsupported). */
 int32_t kdv_verify_num_splits(const kdv_mla_dims* d, int32_t T, int32_t L);
 
+/* Diagnostic, for measurement: launches `blocks` workgroups of 256 threads in which every wave issues `iters`
+ * rounds of four independent 32x32x16 bf16 MFMA chains (4 * iters * 32768 flop per wave), the issue-rate
+ * ceiling the verify kernels are compared with.  sink: device float [blocks * 256], written (zeros).  Time
+ * it with events on `stream`.  Returns KDV_OK, KDV_ERR_NULL, KDV_ERR_SHAPE (iters < 1, blocks outside
+ * [1, 2^20]), KDV_ERR_ALIGN, KDV_ERR_HIP. */
+int kdv_mfma_probe(int32_t iters, float* sink, int32_t blocks, void* stream);
+
 /* Static English description of a kdv_status value. */
 const char* kdv_status_string(int status);
 

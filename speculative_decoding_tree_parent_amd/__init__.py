@@ -33,7 +33,7 @@ EXPORTED = ("kdv_build_draft_tree", "kdv_build_tree_mask", "kdv_merge_attn_state
             "kdv_tree_accept", "kdv_verify_batch_workspace_bytes", "kdv_verify_mla_attn_batch",
             "kdv_verify_workspace_bytes", "kdv_verify_mla_attn", "kdv_verify_mla_attn_profiled",
             "kdv_verify_mla_attn_tree",
-            "kdv_verify_num_splits", "kdv_status_string")
+            "kdv_verify_num_splits", "kdv_mfma_probe", "kdv_status_string")
 
 
 class KdvMlaDims(ctypes.Structure):
@@ -83,6 +83,8 @@ def _load() -> ctypes.CDLL:
     lib.kdv_prefix_workspace_bytes.restype = sz
     lib.kdv_merge_attn_states.argtypes = [vp, vp, vp, vp, i64, i32, vp, vp, vp]
     lib.kdv_merge_attn_states.restype = ctypes.c_int
+    lib.kdv_mfma_probe.argtypes = [i32, vp, i32, vp]
+    lib.kdv_mfma_probe.restype = ctypes.c_int
     lib.kdv_status_string.argtypes = [ctypes.c_int]
     lib.kdv_status_string.restype = ctypes.c_char_p
     return lib
@@ -176,6 +178,10 @@ def kdv_prefix_workspace_bytes(dims: KdvMlaDims, T: int, L: int) -> int:
 def kdv_merge_attn_states(out_a: int, lse_a: int, out_b: int, lse_b: int, rows: int, dv: int, out: int,
                           lse: int | None, stream: int | None) -> int:
     return _lib.kdv_merge_attn_states(out_a, lse_a, out_b, lse_b, rows, dv, out, lse, stream)
+
+
+def kdv_mfma_probe(iters: int, sink: int, blocks: int, stream: int | None) -> int:
+    return _lib.kdv_mfma_probe(iters, sink, blocks, stream)
 
 
 def kdv_status_string(status: int) -> str:

@@ -831,6 +831,31 @@ __global__ __launch_bounds__(NTHREADS) void merge_states_kernel(const uint16_t* 
   if (lse != nullptr && idx % cpr == 0) lse[r] = lo;
 }
 
+// ------------------------------------------------------------------------------------------------ MFMA ceiling probe
+// Diagnostic: every wave runs `iters` rounds of four independent 32x32x16 bf16 MFMA chains (the issue rate of
+// back-to-back independent MFMAs, the ceiling the verify kernels are measured against).  Operands are zero, so
+// the sums are zero; each thread writes its sum to `sink` so that nothing is optimised away.
+__global__ __launch_bounds__(NTHREADS) void mfma_probe_kernel(int iters, float* __restrict__ sink) {
+  const int lane = threadIdx.x & 63;
+  bf16x8 a, b;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    a[e] = (__bf16)(0.f * lane);
+    b[e] = (__bf16)0.f;
+  }
+  f32x16 c0 = zero16(), c1 = zero16(), c2 = zero16(), c3 = zero16();
+  for (int it = 0; it < iters; ++it) {
+    c0 = mfma32(a, b, c0);
+    c1 = mfma32(a, b, c1);
+    c2 = mfma32(a, b, c2);
+    c3 = mfma32(a, b, c3);
+  }
+  float t = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) t += c0[r] + c1[r] + c2[r] + c3[r];
+  sink[(size_t)blockIdx.x * NTHREADS + threadIdx.x] = t;
+}
+
 // ------------------------------------------------------------------------------------------------ host side
 struct Plan {
   int H, nodes;           // heads, nodes of all requests
@@ -1118,6 +1143,17 @@ extern "C" int kdv_merge_attn_states(const uint16_t* out_a, const float* lse_a, 
   (void)hipGetLastError();
   hipLaunchKernelGGL(merge_states_kernel, dim3((unsigned)blocks), dim3(NTHREADS), 0, static_cast<hipStream_t>(stream),
                      out_a, lse_a, out_b, lse_b, chunks, dv / 8, out, lse);
+  return hipGetLastError() == hipSuccess ? KDV_OK : KDV_ERR_HIP;
+}
+
+extern "C" int kdv_mfma_probe(int32_t iters, float* sink, int32_t blocks, void* stream) {
+  using namespace kdv;
+  if (sink == nullptr) return KDV_ERR_NULL;
+  if (iters < 1 || blocks < 1 || blocks > (1 << 20)) return KDV_ERR_SHAPE;
+  if (misaligned(sink, 4)) return KDV_ERR_ALIGN;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(mfma_probe_kernel, dim3(blocks), dim3(NTHREADS), 0, static_cast<hipStream_t>(stream), iters,
+                     sink);
   return hipGetLastError() == hipSuccess ? KDV_OK : KDV_ERR_HIP;
 }
 

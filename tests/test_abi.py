@@ -291,3 +291,10 @@ def test_tree_verify_argument_errors(fixed_splits):
     assert call(parent=A + 2) == kdv.KDV_ERR_ALIGN
     assert call(status=A + 1) == kdv.KDV_ERR_ALIGN
     assert call() == kdv.KDV_ERR_WORKSPACE  # workspace_bytes = 0: rejected before any launch
+
+
+def test_mfma_probe_argument_errors():
+    assert kdv.kdv_mfma_probe(10, None, 4, None) == kdv.KDV_ERR_NULL
+    assert kdv.kdv_mfma_probe(0, A, 4, None) == kdv.KDV_ERR_SHAPE
+    assert kdv.kdv_mfma_probe(10, A, 0, None) == kdv.KDV_ERR_SHAPE
+    assert kdv.kdv_mfma_probe(10, A + 2, 4, None) == kdv.KDV_ERR_ALIGN
