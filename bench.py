@@ -827,7 +827,49 @@ def summarize_profile(d, workload):
               "", "```json", json.dumps(rec), "```", ""]
     with open(os.path.join(out_dir, f"splitkv_{workload}_hbm_traffic.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
+    if os.path.isdir(os.path.join(d, "mfma")):
+        _summarize_mfma(d, workload, cmds, bench, durs, out_dir)
     print(out_dir)
+
+
+def _summarize_mfma(d, workload, cmds, trace_bench, durs, out_dir):
+    """MFMA instructions and busy cycles per dispatch (counter run) against the traced durations."""
+    mb = json.loads(open(os.path.join(d, "mfma_bench.json")).read().strip().splitlines()[-1])
+    insts = _counter_per_dispatch(os.path.join(d, "mfma"), "SQ_INSTS_MFMA", _kernel_key)
+    busy = _counter_per_dispatch(os.path.join(d, "mfma"), "SQ_VALU_MFMA_BUSY_CYCLES", _kernel_key)
+    agent = [r for r in _read_csv(os.path.join(d, "mfma", "run_agent_info.csv")) if r.get("Name", "").startswith("gfx")]
+    simds = int(agent[0]["Simd_Count"]) if agent else 1024
+    mhz = float(agent[0]["Max_Engine_Clk_Fcompute"]) if agent else 2400.0
+    lines = [f"# MFMA use per dispatch: tree-verify MLA attention, workload `{workload}`", "",
+             "Commands (from the repository root on the GPU machine; `bash profile_bench.sh` runs them):", "",
+             "```", cmds, "```", "",
+             f"Counters from `rocprofv3 --pmc SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES` over the eager cold launches "
+             f"of the counted run (`--steps {mb['steps']} --warmup {mb['warmup']}`); durations from the kernel "
+             f"trace of the same phase.  Every MFMA here is a 32x32x16 bf16 (32768 flop, 32 busy cycles).  "
+             f"Busy fraction = SQ_VALU_MFMA_BUSY_CYCLES / ({simds} SIMDs x duration x {mhz:.0f} MHz, the "
+             "agent's maximum engine clock): the share of the kernel's time the matrix cores were busy, "
+             "against the clock the vendor peak assumes.", "",
+             "| kernel | MFMA instructions | MFMA GFLOP | traced us | TFLOP/s from counters | MFMA busy fraction |",
+             "|---|---|---|---|---|---|"]
+    for k in KERNELS:
+        if k not in insts or k not in busy or k not in durs:
+            continue
+        ph, total = _phases(mb, k)
+        a, b = ph["eager cold, kernel events"]
+        iv, bv = insts[k][a:b], busy[k][a:b]
+        if len(insts[k]) != total or not iv:
+            continue
+        tph, _ = _phases(trace_bench, k)
+        ta, tb = tph["eager cold, kernel events"]
+        seg = sorted(durs[k])[ta:tb]
+        us = sum(e - s_ for _, s_, e in seg) / len(seg) / 1e3
+        n = sum(iv) / len(iv)
+        cyc = sum(bv) / len(bv)
+        gflop = n * 32768 / 1e9
+        frac = cyc / (simds * us * 1e-6 * mhz * 1e6)
+        lines.append(f"| {k} | {n:.0f} | {gflop:.3f} | {us:.2f} | {gflop / (us * 1e-6) / 1e3:.1f} | {frac:.3f} |")
+    with open(os.path.join(out_dir, f"verify_{workload}_mfma.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
 
 
 if __name__ == "__main__":

@@ -2,7 +2,8 @@
 # rocprofv3 evidence behind bench.py's roofline object, for one workload (default kimi5553):
 #   1. a bench run without the profiler, then the same run under a kernel trace (per-kernel durations,
 #      compared with bench.py's own event timings from the run without the profiler);
-#   2. FETCH_SIZE, then WRITE_SIZE, each in a counter run of its own, on a shorter bench run;
+#   2. FETCH_SIZE, then WRITE_SIZE, then the MFMA instruction and busy-cycle counts, each in a counter run of
+#      its own, on a shorter bench run;
 #   3. the same two counters on a plain 256 MiB device copy, the calibration of counter units to bytes.
 # Raw output goes to gpurun_out/profile_<workload>/; the markdown summaries to .../summaries/.
 # Run from anywhere on the GPU machine: bash profile_bench.sh [workload]
@@ -33,6 +34,8 @@ run 300 "$O/trace_bench.json" rocprofv3 --kernel-trace --stats -f csv -d "$O/tra
 run 120 "$O/fetch_bench.json" rocprofv3 --pmc FETCH_SIZE -f csv -d "$O/fetch" -o run -- \
   python3 "$R/bench.py" --workload "$W" --steps 10 --warmup 2 --no-cpu-baseline
 run 120 "$O/write_bench.json" rocprofv3 --pmc WRITE_SIZE -f csv -d "$O/write" -o run -- \
+  python3 "$R/bench.py" --workload "$W" --steps 10 --warmup 2 --no-cpu-baseline
+run 120 "$O/mfma_bench.json" rocprofv3 --pmc SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES -f csv -d "$O/mfma" -o run -- \
   python3 "$R/bench.py" --workload "$W" --steps 10 --warmup 2 --no-cpu-baseline
 run 120 "$O/copy_fetch.json" rocprofv3 --pmc FETCH_SIZE -f csv -d "$O/copy_fetch" -o run -- \
   python3 "$R/bench.py" --copy-calibration
