@@ -43,7 +43,8 @@ extern "C" {
 /* Model dimensions of one MLA attention layer.  Supported shapes:
  *   Kimi/DeepSeek shape: qk_nope 128, qk_rope 64, kv_lora_rank 512, v_head 128;
  *   tiny test shape:     qk_nope 32,  qk_rope 16, kv_lora_rank 64,  v_head 32;
- * with 1 <= num_heads <= 128.  sm_scale multiplies q.k (1/sqrt(qk_nope+qk_rope) for Kimi). */
+ * with 1 <= num_heads <= 128.  sm_scale multiplies q.k (1/sqrt(qk_nope+qk_rope) for Kimi); it must be finite and
+ * > 0 (KDV_ERR_SHAPE otherwise). */
 typedef struct kdv_mla_dims {
   int32_t num_heads;
   int32_t qk_nope_dim;

@@ -260,7 +260,7 @@ __device__ __forceinline__ void tile_compute(const char* tile, const bf16x8 (&q)
   }
   float s[16];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) s[r] = (acc0[r] + acc1[r]) * scale_log2;
+  for (int r = 0; r < 16; ++r) s[r] = acc0[r] + acc1[r];  // unscaled: the scale (> 0) goes into the exp2's fma
   if (n0 + KV_TILE > L) {  // tile reaches the tree rows (or past N): apply the ancestor mask
     const uint64_t mw = (uint64_t)mw0 | ((uint64_t)mw1 << 32);
     const int T = N - L;
@@ -275,7 +275,7 @@ __device__ __forceinline__ void tile_compute(const char* tile, const bf16x8 (&q)
   float tmax = -INFINITY;
 #pragma unroll
   for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[r]);
-  tmax = pair_max(tmax);
+  tmax = pair_max(tmax) * scale_log2;  // max of the scaled scores (scale > 0; -inf stays -inf)
   // ---- proposed reference for row (wi, c): keep the current one unless this half-tile exceeds it by more
   // than 2^8.  P of this half-tile is taken relative to the proposal.
   const float mref = (wi == 0) ? st.m_ref[0] : st.m_ref[1];  // (no dynamic index: st stays in registers)
@@ -285,7 +285,7 @@ __device__ __forceinline__ void tile_compute(const char* tile, const bf16x8 (&q)
   float ps = 0.f;  // unrounded row sum of this half-tile
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const float p0 = fast_exp2(s[e] - puse), p1 = fast_exp2(s[8 + e] - puse);
+    const float p0 = fast_exp2(fmaf(s[e], scale_log2, -puse)), p1 = fast_exp2(fmaf(s[8 + e], scale_log2, -puse));
     ps += p0 + p1;
     pk[0][e] = (__bf16)p0;
     pk[1][e] = (__bf16)p1;
@@ -868,6 +868,7 @@ enum ShapeId { SHAPE_NONE = 0, SHAPE_KIMI = 1, SHAPE_TINY = 2 };
 
 static ShapeId shape_of(const kdv_mla_dims* d) {
   if (d->num_heads < 1 || d->num_heads > 128) return SHAPE_NONE;
+  if (!(d->sm_scale > 0.f) || !(d->sm_scale < INFINITY)) return SHAPE_NONE;  // (NaN fails both)
   if (d->qk_nope_dim == 128 && d->qk_rope_dim == 64 && d->kv_lora_rank == 512 && d->v_head_dim == 128)
     return SHAPE_KIMI;
   if (d->qk_nope_dim == 32 && d->qk_rope_dim == 16 && d->kv_lora_rank == 64 && d->v_head_dim == 32)

@@ -298,3 +298,10 @@ def test_mfma_probe_argument_errors():
     assert kdv.kdv_mfma_probe(0, A, 4, None) == kdv.KDV_ERR_SHAPE
     assert kdv.kdv_mfma_probe(10, A, 0, None) == kdv.KDV_ERR_SHAPE
     assert kdv.kdv_mfma_probe(10, A + 2, 4, None) == kdv.KDV_ERR_ALIGN
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.1, float("inf"), float("nan")])
+def test_bad_softmax_scale_rejected(scale, fixed_splits):
+    d = kdv.make_dims(**dict(KIMI, sm_scale=scale))
+    assert _call(d) == kdv.KDV_ERR_SHAPE
+    assert kdv.kdv_verify_workspace_bytes(d, 15, 100) == 0
