@@ -266,9 +266,9 @@ __device__ __forceinline__ void tile_compute(const char* tile, const bf16x8 (&q)
     const int T = N - L;
     const int jb = n0 + wj * 32 + g * 4 - L;  // tree index of register 0's row
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
+    for (int r = 0; r < 16; ++r) {  // (bitwise, not short-circuit: selects in place, no per-element branches)
       const int jn = jb + (r >> 2) * 8 + (r & 3);
-      const bool vis = (jn < 0) || (jn < T && ((mw >> (jn & 63)) & 1u));
+      const bool vis = (jn < 0) | ((jn < T) & (((uint32_t)(mw >> (jn & 63)) & 1u) != 0u));
       s[r] = vis ? s[r] : -INFINITY;
     }
   }
@@ -282,11 +282,11 @@ __device__ __forceinline__ void tile_compute(const char* tile, const bf16x8 (&q)
   const float prop = (tmax > mref + 8.f) ? ceilf(tmax) : mref;
   const float puse = (prop == -INFINITY) ? 0.f : prop;
   bf16x8 pk[2];
-  float ps = 0.f;  // unrounded row sum of this half-tile
+  float ps;  // unrounded row sum of this half-tile
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const float p0 = fast_exp2(fmaf(s[e], scale_log2, -puse)), p1 = fast_exp2(fmaf(s[8 + e], scale_log2, -puse));
-    ps += p0 + p1;
+    ps = (e == 0) ? p0 + p1 : ps + (p0 + p1);
     pk[0][e] = (__bf16)p0;
     pk[1][e] = (__bf16)p1;
   }
