@@ -118,3 +118,17 @@ def test_merge_matches_oracle(rows, dv, seed):
     assert np.all(np.abs(glse[fin] - rlse[fin]) <= 2e-6 * np.maximum(1.0, np.abs(rlse[fin])))
     empty = ~fin
     assert np.all(got[empty] == 0.0)
+
+
+def test_merge_without_lse_output():
+    rng = np.random.default_rng(11)
+    oa, ob = _bf16(rng.normal(0, 1, (64, 128))).cuda(), _bf16(rng.normal(0, 1, (64, 128))).cuda()
+    la = torch.from_numpy(rng.normal(0, 3, 64).astype(np.float32)).cuda()
+    lb = torch.from_numpy(rng.normal(0, 3, 64).astype(np.float32)).cuda()
+    out = torch.empty_like(oa)
+    rc = kdv.kdv_merge_attn_states(oa.data_ptr(), la.data_ptr(), ob.data_ptr(), lb.data_ptr(), 64, 128,
+                                   out.data_ptr(), None, None)
+    assert rc == kdv.KDV_OK
+    ref_out, _ = kdv.merge_attn_states(oa, la, ob, lb)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref_out)

@@ -67,3 +67,24 @@ def test_tree_call_reports_malformed_tree():
     assert int(s1.item()) == int(s2.item()) == ref_status
     assert np.array_equal(m1.cpu().numpy().view(np.uint32), ref_mask)
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_tree_call_without_status():
+    inp = si.kimi(L=300, T=15, seed=7)
+    dev = si.to_device(inp)
+    dims = kdv.make_dims(**inp.dims())
+    T, H = inp.T, inp.H
+    mask = torch.empty((T, 1), dtype=torch.int32, device="cuda")
+    out = torch.empty((T, H, inp.Dv), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty((kdv.verify_workspace_bytes(dims, T, inp.L),), dtype=torch.uint8, device="cuda")
+    rc = kdv.kdv_verify_mla_attn_tree(dims, *[dev[k].data_ptr() for k in ("q_nope", "q_rope", "w_uk", "w_uv", "c_kv",
+                                                                         "k_pe")],
+                                      inp.pool_slots, dev["page_table"].data_ptr(), inp.L, T,
+                                      dev["parent"].data_ptr(), mask.data_ptr(), None, out.data_ptr(), None,
+                                      ws.data_ptr(), ws.numel(), None)
+    assert rc == kdv.KDV_OK
+    torch.cuda.synchronize()
+    ref_mask, _ = oracle.tree_mask(inp.parent)
+    assert np.array_equal(mask.cpu().numpy().view(np.uint32), ref_mask)
+    (o2, _, _, _), _, _ = both(inp)
+    assert torch.equal(out, o2)
