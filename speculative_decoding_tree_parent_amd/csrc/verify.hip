@@ -561,7 +561,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void splitkv_kernel(
 }
 
 // ------------------------------------------------------------------------------------------------ q_absorb
-// grid (H, ceil(R/128)); each wave produces 32 latent columns for all T nodes of head h.
+// grid (H, ceil(R/128), ceil(T/32)); each wave produces 32 latent columns of head h for the workgroup's 32 nodes.
 // MFMA D[r][t] = sum_k W_UK[h][k][r] q_nope[t,h][k]: the A operand W^T is read from LDS with transposed
 // reads (W_UK is stored k-major), the B operand straight from global memory.
 // The W_UK block arrives by LDS DMA (an LDS-DMA gather moves about 2.5 times the bytes per CU that loads into
@@ -577,9 +577,10 @@ __global__ __launch_bounds__(NTHREADS) void q_absorb_kernel(const uint16_t* __re
                                                             uint32_t* __restrict__ mask,
                                                             int32_t* __restrict__ status) {
   if (blockIdx.x == H) {  // a call that builds its own tree mask has one extra column of blocks (uniform exit)
-    if (blockIdx.y == 0 && threadIdx.x < 64) build_ancestor_mask(parent, T, mask, status, threadIdx.x);
+    if (blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x < 64) build_ancestor_mask(parent, T, mask, status, threadIdx.x);
     return;
   }
+  const int t_base = blockIdx.z * 32;  // this workgroup's 32 nodes (grid z covers all nodes of the call)
   constexpr int DQ = R + DR;
   constexpr int RB = 128;                    // latent columns per workgroup
   constexpr int WINS = DN * RB * 2 / 1024;   // DMA instructions for the W_UK block
@@ -600,16 +601,17 @@ __global__ __launch_bounds__(NTHREADS) void q_absorb_kernel(const uint16_t* __re
       if (col < R) dma16_lane_addr(wh + ((size_t)k * R + col) * 2, wl + ins * 1024);  // (columns past R: never read)
     }
   }
-  // query fragments of the first 32 nodes; rows past T load node T-1 (their results are never stored)
+  // query fragments of this workgroup's 32 nodes; rows past T load node T-1 (their results are never stored)
   bf16x8 qb[DN / 16];
   {
-    const int tq = min(c, T - 1);
+    const int tq = min(t_base + c, T - 1);
 #pragma unroll
     for (int kb = 0; kb < DN / 16; ++kb) qb[kb] = load_bf16x8(q_nope + ((size_t)tq * H + h) * DN + kb * 16 + g * 8);
   }
   if (blockIdx.y == 0) {
-    for (int ci = tid; ci < T * (DR / 8); ci += NTHREADS) {
-      const int t = ci / (DR / 8), col = (ci % (DR / 8)) * 8;
+    const int nt = min(32, T - t_base);
+    for (int ci = tid; ci < nt * (DR / 8); ci += NTHREADS) {
+      const int t = t_base + ci / (DR / 8), col = (ci % (DR / 8)) * 8;
       *reinterpret_cast<uint4*>(q_cat + (size_t)(t * H + h) * DQ + R + col) =
           *reinterpret_cast<const uint4*>(q_rope + ((size_t)t * H + h) * DR + col);
     }
@@ -623,15 +625,14 @@ __global__ __launch_bounds__(NTHREADS) void q_absorb_kernel(const uint16_t* __re
   auto wread = [&](int krow) -> i16x4 {
     return lds_read_tr16(w_s + krow * (RB * 2) + (((rs / 8 + cl) ^ (4 * (krow & 3))) << 4) + sub);
   };
-  for (int tb = 0; tb < T; tb += 32) {
+  {
     f32x16 acc = zero16();
-    const int t = tb + c;
+    const int t = t_base + c;
 #pragma unroll
     for (int kb = 0; kb < DN / 16; ++kb) {
       const int krow = kb * 16 + g * 8 + ((lane & 15) >> 2);
       const bf16x8 a = concat_tr(wread(krow), wread(krow + 4));
-      const bf16x8 b = (tb == 0) ? qb[kb] : load_bf16x8(q_nope + ((size_t)min(t, T - 1) * H + h) * DN + kb * 16 + g * 8);
-      acc = mfma32(a, b, acc);
+      acc = mfma32(a, qb[kb], acc);
     }
     if (t < T) {
       uint16_t* dst = q_cat + (size_t)(t * H + h) * DQ + r0 + rs + g * 4;
@@ -990,7 +991,7 @@ static void launch_all(const Plan& pl, float sm_scale, const uint16_t* q_nope, c
   float2* part_ml = reinterpret_cast<float2*>(ws + pl.off_pml);
   // The query absorption is per node: the packed nodes of all requests in one grid.  With `parent` (one
   // request) an extra block builds the tree mask the split-KV kernel then reads.
-  launch(q_absorb_kernel<DN, R, DR>, dim3(pl.H + (parent != nullptr ? 1 : 0), (R + 127) / 128), st,
+  launch(q_absorb_kernel<DN, R, DR>, dim3(pl.H + (parent != nullptr ? 1 : 0), (R + 127) / 128, (pl.nodes + 31) / 32), st,
          ev ? ev + 0 : nullptr, q_nope, q_rope, w_uk, q_cat, pl.nodes, pl.H, parent, const_cast<uint32_t*>(mask),
          status);
   const float scale_log2 = sm_scale * 1.44269504088896340736f;
