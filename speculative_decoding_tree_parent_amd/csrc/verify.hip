@@ -733,6 +733,8 @@ __global__ __launch_bounds__(NTHREADS) void combine_up_kernel(const uint16_t* __
     for (int u = 0; u < CPT; ++u)
 #pragma unroll
       for (int e = 0; e < 8; ++e) num[u][e] = 0.f;
+    // Splits are taken CH at a time.  Within a group the reference is the group's largest m_s, so each
+    // split costs one fused multiply-add per element; the running sums are rescaled once per further group.
     for (int s0 = 0; s0 < S; s0 += CH) {
       float2 ml[CH];
       bf16x8 v[CH][CPT];
@@ -743,19 +745,30 @@ __global__ __launch_bounds__(NTHREADS) void combine_up_kernel(const uint16_t* __
 #pragma unroll
         for (int u = 0; u < CPT; ++u) v[q][u] = src[sq * stride + u];
       }
+      float gm = -INFINITY;
 #pragma unroll
-      for (int q = 0; q < CH; ++q) {
-        if (s0 + q >= S || ml[q].x == -INFINITY) continue;  // nothing visible in that split
-        const float mn = fmaxf(mx, ml[q].x);
-        const float a = fast_exp2(mx - mn);  // mx = -inf -> 0
-        const float wgt = fast_exp2(ml[q].x - mn) * ml[q].y;
-        den = den * a + wgt;
+      for (int q = 0; q < CH; ++q) gm = (s0 + q < S) ? fmaxf(gm, ml[q].x) : gm;
+      const float mn = fmaxf(mx, gm);
+      if (mn == -INFINITY) continue;  // nothing visible in any split so far
+      if (s0 > 0) {
+        const float a = fast_exp2(mx - mn);  // mx = -inf -> 0 (the sums are still 0)
+        den *= a;
 #pragma unroll
         for (int u = 0; u < CPT; ++u)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) num[u][e] = num[u][e] * a + wgt * (float)v[q][u][e];
-        mx = mn;
+          for (int e = 0; e < 8; ++e) num[u][e] *= a;
       }
+#pragma unroll
+      for (int q = 0; q < CH; ++q) {
+        // weight 0 for a split past S (its loads repeat split S - 1) or one in which row m saw nothing
+        const float wq = (s0 + q < S && ml[q].x != -INFINITY) ? fast_exp2(ml[q].x - mn) * ml[q].y : 0.f;
+        den += wq;
+#pragma unroll
+        for (int u = 0; u < CPT; ++u)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) num[u][e] = fmaf(wq, (float)v[q][u][e], num[u][e]);
+      }
+      mx = mn;
     }
     const float inv = 1.f / den;
 #pragma unroll
