@@ -608,16 +608,17 @@ __global__ __launch_bounds__(NTHREADS) void q_absorb_kernel(const uint16_t* __re
 #pragma unroll
     for (int kb = 0; kb < DN / 16; ++kb) qb[kb] = load_bf16x8(q_nope + ((size_t)tq * H + h) * DN + kb * 16 + g * 8);
   }
-  if (blockIdx.y == 0) {
-    const int nt = min(32, T - t_base);
-    for (int ci = tid; ci < nt * (DR / 8); ci += NTHREADS) {
-      const int t = t_base + ci / (DR / 8), col = (ci % (DR / 8)) * 8;
-      *reinterpret_cast<uint4*>(q_cat + (size_t)(t * H + h) * DQ + R + col) =
-          *reinterpret_cast<const uint4*>(q_rope + ((size_t)t * H + h) * DR + col);
-    }
-  }
+  // The rotary part of q_cat is a copy (first column of workgroups, one 16-byte chunk per thread): loaded here
+  // with the other loads, stored after the product, so that no store acknowledgement is waited for before it.
+  constexpr int RCH = 32 * (DR / 8);  // rotary chunks of 32 nodes
+  static_assert(RCH <= NTHREADS, "one rotary chunk per thread");
+  const int rt = t_base + tid / (DR / 8), rcol = (tid % (DR / 8)) * 8;
+  const bool rcopy = blockIdx.y == 0 && tid < RCH && rt < T;
+  uint4 rv = make_uint4(0u, 0u, 0u, 0u);
+  if (rcopy) rv = *reinterpret_cast<const uint4*>(q_rope + ((size_t)rt * H + h) * DR + rcol);
   wait_vmem_all();
   __syncthreads();
+  if (rcopy) *reinterpret_cast<uint4*>(q_cat + (size_t)(rt * H + h) * DQ + R + rcol) = rv;
   const int rs = wave * 32;
   if (r0 + rs >= R) return;  // wave-uniform; no barrier follows
   // lane's transposed-read position: rows kb*16 + g*8 + (lane%16)/4 (+4), chunk rs/8 + cl, byte sub
@@ -656,18 +657,20 @@ __global__ __launch_bounds__(NTHREADS) void q_absorb_kernel(const uint16_t* __re
 // The merged latent row, rounded to bf16, goes through the value up-projection right away:
 // out[t,h][v] = sum_r W_UV[h][v][r] o[t,h][r].
 //
-// One workgroup per (head, block of RT nodes).  Workgroups are dealt to the XCDs round-robin, and the node
-// blocks of one head are kept on one XCD, so W_UV[h] is fetched into that XCD's L2 once.  The waves split
-// the fetching so that none waits for the other's loads (a wave's load counter is in order):
-//   - waves 0 and 1 load the partials of the RT rows into registers and merge them (two 16-byte chunks of a
-//     row per thread);
-//   - waves 2 and 3 gather all of W_UV[h] into LDS by DMA (an LDS-DMA gather moves about 2.5 times the
-//     bytes per CU that loads into registers do).  Chunk ch of W row r sits at position ch ^ (r % WSW) of
-//     the row, so the MFMA's quarter-wave reads (16 rows, one chunk) hit 16 distinct bank groups.
-// After one barrier, wave w computes D[v][t] = sum_r W_UV[h][v][r] o[t][r] for its 32 columns v, both
+// One workgroup of 8 waves per (head, block of RT nodes).  Workgroups are dealt to the XCDs round-robin, and
+// the node blocks of one head are kept on one XCD, so W_UV[h] is fetched into that XCD's L2 once.  The waves
+// split the fetching so that none waits for the other's loads (a wave's load counter is in order):
+//   - waves 0..3 load the partials of the RT rows into registers and merge them (one 16-byte chunk of a row
+//     per thread for the 512-wide latent);
+//   - waves 4..7 gather all of W_UV[h] into LDS by DMA (an LDS-DMA gather moves about 2.5 times the
+//     bytes per CU that loads into registers do; the issue cost of a DMA instruction is per wave, so four
+//     waves share it).  Chunk ch of W row r sits at position ch ^ (r % WSW) of the row, so the MFMA's
+//     quarter-wave reads (16 rows, one chunk) hit 16 distinct bank groups.
+// After one barrier, wave w < DV/32 computes D[v][t] = sum_r W_UV[h][v][r] o[t][r] for its 32 columns v, both
 // operands read from LDS (r-contiguous); columns t >= RT of the product repeat the last row, never stored.
+constexpr int COMB_THREADS = 512;
 template <int R, int DV, int NB>
-__global__ __launch_bounds__(NTHREADS) void combine_up_kernel(const uint16_t* __restrict__ part_o_all,
+__global__ __launch_bounds__(COMB_THREADS) void combine_up_kernel(const uint16_t* __restrict__ part_o_all,
                                                               const float2* __restrict__ part_ml_all,
                                                               const BatchArgs<NB> ba,
                                                               const uint16_t* __restrict__ w_uv,
@@ -678,14 +681,15 @@ __global__ __launch_bounds__(NTHREADS) void combine_up_kernel(const uint16_t* __
   constexpr int KS = R / 16;                 // MFMA k-steps
   constexpr int OP = R + 8;                  // LDS pitch of a merged row (elements)
   constexpr int CH = 16;                     // splits whose loads are in flight together
-  constexpr int MT = RT * CPR < 128 ? RT * CPR : 128;  // merging threads (in waves 0 and 1)
+  constexpr int NFW = 4;                     // fetching waves (4..7); waves 0..3 merge
+  constexpr int MT = RT * CPR < 256 ? RT * CPR : 256;  // merging threads (in waves 0..3)
   constexpr int CPT = RT * CPR / MT;         // chunks per merging thread
   constexpr int WSW = CPR < 16 ? CPR : 16;   // W_UV staging swizzle width (chunks)
   constexpr int WBYTES = DV * R * 2;         // all of W_UV[h]
-  constexpr int WINS = WBYTES / 1024 / 2;    // DMA instructions per fetching wave (waves 2 and 3)
+  constexpr int WINS = WBYTES / 1024 / NFW;  // DMA instructions per fetching wave
   static_assert(CPT >= 1 && RT * CPR % MT == 0, "chunks must split evenly over the merging threads");
-  static_assert(DV % 32 == 0 && DV / 32 <= NTHREADS / 64, "one wave per 32 output columns");
-  static_assert(WBYTES % 2048 == 0, "W_UV must split evenly over two fetching waves");
+  static_assert(DV % 32 == 0 && DV / 32 <= 4, "one merging wave per 32 output columns");
+  static_assert(WBYTES % (1024 * NFW) == 0, "W_UV must split evenly over the fetching waves");
   __shared__ __attribute__((aligned(16))) uint16_t o_s[RT * OP];
   __shared__ __attribute__((aligned(1024))) char w_s[WBYTES];
   const int rqi = NB > 1 ? request_of(ba.blk_comb, ba.n, blockIdx.x) : 0;
@@ -709,13 +713,13 @@ __global__ __launch_bounds__(NTHREADS) void combine_up_kernel(const uint16_t* __
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, c = lane & 31;
 
-  if (wave >= 2) {
+  if (wave >= 8 - NFW) {
     // ---- W_UV[h] -> LDS: lane l of instruction i fills position (i*64 + l) of the swizzled rows
     const char* wsrc = reinterpret_cast<const char*>(w_uv + (size_t)h * DV * R);
     const uint32_t wl = lds_address(w_s);
 #pragma unroll
     for (int k = 0; k < WINS; ++k) {
-      const int ins = (wave - 2) + 2 * k;
+      const int ins = (wave - (8 - NFW)) + NFW * k;
       const int pos = ins * 64 + lane, r = pos / CPR, p = pos % CPR;
       dma16_lane_addr(wsrc + (size_t)r * (R * 2) + ((p ^ (r & (WSW - 1))) << 4), wl + ins * 1024);
     }
@@ -987,11 +991,15 @@ static int make_plan(const kdv_mla_dims* d, int C, const int32_t* Ls, const int3
 
 // Launch one kernel; with `ev` (start, stop) the events take the kernel's own start and end timestamps.
 template <typename... KArgs, typename... Args>
-static void launch(void (*k)(KArgs...), dim3 grid, hipStream_t st, hipEvent_t const* ev, Args... args) {
+static void launch_n(void (*k)(KArgs...), dim3 grid, int threads, hipStream_t st, hipEvent_t const* ev, Args... args) {
   if (ev)
-    hipExtLaunchKernelGGL(k, grid, dim3(NTHREADS), 0, st, ev[0], ev[1], 0, args...);
+    hipExtLaunchKernelGGL(k, grid, dim3(threads), 0, st, ev[0], ev[1], 0, args...);
   else
-    hipLaunchKernelGGL(k, grid, dim3(NTHREADS), 0, st, args...);
+    hipLaunchKernelGGL(k, grid, dim3(threads), 0, st, args...);
+}
+template <typename... KArgs, typename... Args>
+static void launch(void (*k)(KArgs...), dim3 grid, hipStream_t st, hipEvent_t const* ev, Args... args) {
+  launch_n(k, grid, NTHREADS, st, ev, args...);
 }
 
 template <int DN, int R, int DR, int DV>
@@ -1018,13 +1026,13 @@ static void launch_all(const Plan& pl, float sm_scale, const uint16_t* q_nope, c
     one.r[0] = pl.ba.r[0];
     launch(splitkv_kernel<R, DR, 1>, dim3(pl.split_blocks), st, ev ? ev + 2 : nullptr, (const uint16_t*)q_cat, c_kv,
            k_pe, page_table, mask, one, scale_log2, part_o, part_ml);
-    launch(combine_up_kernel<R, DV, 1>, dim3(pl.comb_blocks), st, ev ? ev + 4 : nullptr, (const uint16_t*)part_o,
-           (const float2*)part_ml, one, w_uv, out, lse);
+    launch_n(combine_up_kernel<R, DV, 1>, dim3(pl.comb_blocks), COMB_THREADS, st, ev ? ev + 4 : nullptr,
+             (const uint16_t*)part_o, (const float2*)part_ml, one, w_uv, out, lse);
   } else {
     launch(splitkv_kernel<R, DR, MAX_BATCH>, dim3(pl.split_blocks), st, ev ? ev + 2 : nullptr,
            (const uint16_t*)q_cat, c_kv, k_pe, page_table, mask, pl.ba, scale_log2, part_o, part_ml);
-    launch(combine_up_kernel<R, DV, MAX_BATCH>, dim3(pl.comb_blocks), st, ev ? ev + 4 : nullptr,
-           (const uint16_t*)part_o, (const float2*)part_ml, pl.ba, w_uv, out, lse);
+    launch_n(combine_up_kernel<R, DV, MAX_BATCH>, dim3(pl.comb_blocks), COMB_THREADS, st, ev ? ev + 4 : nullptr,
+             (const uint16_t*)part_o, (const float2*)part_ml, pl.ba, w_uv, out, lse);
   }
 }
 
