@@ -53,6 +53,19 @@ __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Vector global stores with the SC1 bit (agent scope, the form an agent-scope atomic store takes): the data is
+// written through to memory as it is stored rather than left dirty in this XCD's L2 for the end-of-kernel
+// writeback, which the next kernel's workgroups (on any XCD) would otherwise wait for.  For results a kernel
+// writes in bulk at its end and the next kernel reads.
+typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(unsigned)))) unsigned u32x2;
+__device__ __forceinline__ void store_agent16(void* p, u32x4 v) {
+  asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
+}
+__device__ __forceinline__ void store_agent8(void* p, u32x2 v) {
+  asm volatile("global_store_dwordx2 %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
+}
+
 // Combine a value across the lane pair (l, l ^ 32) with one VALU swap (v_permlane32_swap) instead of an LDS
 // permute.  Swapping a register with itself leaves lane l holding v[l & 31] in the first result and
 // v[(l & 31) + 32] in the second; both lanes of a pair combine the two in the same order, so they get the same bits.

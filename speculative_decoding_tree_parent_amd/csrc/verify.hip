@@ -523,7 +523,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void splitkv_kernel(
 
   // Partial of this split: O / l rounded to bf16, row-major [split][row][R] so that a row is one contiguous
   // 1 KB line for the combine, plus fp32 (max, sum) per row, [split][row].  The register fragments go to
-  // LDS first (the KV buffers are free once every wave has left the loop), then out as whole rows.
+  // LDS first (the KV buffers are free once every wave has left the loop), then out as whole rows, written
+  // through at agent scope (all workgroups store their partials at about the same time, at the end).
   constexpr int OP = R + 8;  // staging pitch (elements): rows 16 B apart in the bank space
   static_assert(M_TILE * OP * 2 <= 2 * TL::BYTES, "O staging must fit in the KV buffers");
   uint16_t* o_s = reinterpret_cast<uint16_t*>(kvbuf);
@@ -548,7 +549,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void splitkv_kernel(
   if (wave == 0 && g == 0) {
 #pragma unroll
     for (int b = 0; b < 2; ++b)
-      part_ml[(size_t)split * Mp + mt * M_TILE + b * 32 + c] = make_float2(st.m_ref[b], st.l[b]);
+      store_agent8(&part_ml[(size_t)split * Mp + mt * M_TILE + b * 32 + c],
+                   u32x2{__float_as_uint(st.m_ref[b]), __float_as_uint(st.l[b])});
   }
   __syncthreads();
   uint16_t* dst = part_o + ((size_t)split * Mp + mt * M_TILE) * R;
@@ -556,7 +558,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void splitkv_kernel(
 #pragma unroll 4
   for (int idx = tid; idx < M_TILE * CPR; idx += NTHREADS) {
     const int row = idx / CPR, ch = idx % CPR;
-    *reinterpret_cast<uint4*>(dst + (size_t)row * R + ch * 8) = *reinterpret_cast<const uint4*>(o_s + row * OP + ch * 8);
+    store_agent16(dst + (size_t)row * R + ch * 8, *reinterpret_cast<const u32x4*>(o_s + row * OP + ch * 8));
   }
 }
 
