@@ -57,13 +57,17 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // written through to memory as it is stored rather than left dirty in this XCD's L2 for the end-of-kernel
 // writeback, which the next kernel's workgroups (on any XCD) would otherwise wait for.  For results a kernel
 // writes in bulk at its end and the next kernel reads.
+// The compiler treats an asm block's inputs as read once the block is issued and may overwrite them with the
+// next instruction, but a vector store reads more than 8 bytes of data over several cycles: on gfx940 and later
+// a VALU write to such a store's data registers must wait 2 states.  The compiler inserts that wait after its
+// own stores only, so these blocks end with it (s_nop 1 = 2 wait states).
 typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
 typedef __attribute__((__vector_size__(2 * sizeof(unsigned)))) unsigned u32x2;
 __device__ __forceinline__ void store_agent16(void* p, u32x4 v) {
-  asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
+  asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 1" ::"v"(p), "v"(v) : "memory");
 }
 __device__ __forceinline__ void store_agent8(void* p, u32x2 v) {
-  asm volatile("global_store_dwordx2 %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
+  asm volatile("global_store_dwordx2 %0, %1, off sc1\n\ts_nop 1" ::"v"(p), "v"(v) : "memory");
 }
 
 // Combine a value across the lane pair (l, l ^ 32) with one VALU swap (v_permlane32_swap) instead of an LDS

@@ -555,9 +555,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void splitkv_kernel(
   __syncthreads();
   uint16_t* dst = part_o + ((size_t)split * Mp + mt * M_TILE) * R;
   constexpr int CPR = R / 8;  // 16-byte chunks per row
+  static_assert(M_TILE * CPR % NTHREADS == 0, "partial rows split evenly over the threads");
 #pragma unroll 4
-  for (int idx = tid; idx < M_TILE * CPR; idx += NTHREADS) {
-    const int row = idx / CPR, ch = idx % CPR;
+  for (int k = 0; k < M_TILE * CPR / NTHREADS; ++k) {
+    const int idx = tid + k * NTHREADS, row = idx / CPR, ch = idx % CPR;
     store_agent16(dst + (size_t)row * R + ch * 8, *reinterpret_cast<const u32x4*>(o_s + row * OP + ch * 8));
   }
 }
