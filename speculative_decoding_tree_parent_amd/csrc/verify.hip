@@ -672,29 +672,34 @@ __global__ __launch_bounds__(NTHREADS) void q_absorb_kernel(const uint16_t* __re
 // After one barrier, wave w < DV/32 computes D[v][t] = sum_r W_UV[h][v][r] o[t][r] for its 32 columns v, both
 // operands read from LDS (r-contiguous); columns t >= RT of the product repeat the last row, never stored.
 constexpr int COMB_THREADS = 512;
-template <int R, int DV, int NB>
+// RT = tree nodes per workgroup (4, or 2 or 1 when a call has few heads and nodes, so that the grid still fills
+// the device).  The merging threads are split into SP groups that take every SP-th split of the same chunks
+// (SP > 1 when the RT rows have fewer chunks than there are merging threads); the groups' running (max, sum,
+// numerator) meet in LDS and are combined in a fixed order.
+template <int R, int DV, int NB, int RT>
 __global__ __launch_bounds__(COMB_THREADS) void combine_up_kernel(const uint16_t* __restrict__ part_o_all,
                                                               const float2* __restrict__ part_ml_all,
                                                               const BatchArgs<NB> ba,
                                                               const uint16_t* __restrict__ w_uv,
                                                               uint16_t* __restrict__ out_all,
                                                               float* __restrict__ lse_all) {
-  constexpr int RT = 4;                      // tree nodes per workgroup
   constexpr int CPR = R / 8;                 // 16-byte chunks per latent row
   constexpr int KS = R / 16;                 // MFMA k-steps
   constexpr int OP = R + 8;                  // LDS pitch of a merged row (elements)
   constexpr int CH = 16;                     // splits whose loads are in flight together
   constexpr int NFW = 4;                     // fetching waves (4..7); waves 0..3 merge
-  constexpr int MT = RT * CPR < 256 ? RT * CPR : 256;  // merging threads (in waves 0..3)
-  constexpr int CPT = RT * CPR / MT;         // chunks per merging thread
+  constexpr int RC = RT * CPR;               // chunks of the workgroup's rows, one per merging thread
+  constexpr int SP = 256 / RC >= 4 ? 4 : (256 / RC >= 2 ? 2 : 1);  // split groups merged side by side
+  constexpr int MT = RC * SP;                // merging threads (in waves 0..3)
   constexpr int WSW = CPR < 16 ? CPR : 16;   // W_UV staging swizzle width (chunks)
   constexpr int WBYTES = DV * R * 2;         // all of W_UV[h]
   constexpr int WINS = WBYTES / 1024 / NFW;  // DMA instructions per fetching wave
-  static_assert(CPT >= 1 && RT * CPR % MT == 0, "chunks must split evenly over the merging threads");
+  static_assert(RC <= 256 && MT <= 256, "one chunk per merging thread");
   static_assert(DV % 32 == 0 && DV / 32 <= 4, "one merging wave per 32 output columns");
   static_assert(WBYTES % (1024 * NFW) == 0, "W_UV must split evenly over the fetching waves");
   __shared__ __attribute__((aligned(16))) uint16_t o_s[RT * OP];
   __shared__ __attribute__((aligned(1024))) char w_s[WBYTES];
+  __shared__ float gx[SP > 1 ? SP : 1][SP > 1 ? RC : 1][10];  // per split group: max, sum, 8 numerators
   const int rqi = NB > 1 ? request_of(ba.blk_comb, ba.n, blockIdx.x) : 0;
   const ReqArgs& rq = ba.r[rqi];
   const int T = rq.T, H = ba.H;
@@ -715,6 +720,7 @@ __global__ __launch_bounds__(COMB_THREADS) void combine_up_kernel(const uint16_t
   const int nrow = min(RT, T - t0);
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, c = lane & 31;
+  constexpr float LN2 = 0.69314718055994530942f;
 
   if (wave >= 8 - NFW) {
     // ---- W_UV[h] -> LDS: lane l of instruction i fills position (i*64 + l) of the swizzled rows
@@ -728,64 +734,92 @@ __global__ __launch_bounds__(COMB_THREADS) void combine_up_kernel(const uint16_t
     }
     wait_vmem_all();
   } else if (tid < MT) {
-    // ---- merge: thread handles chunks k0 .. k0 + CPT - 1 of row i
-    const int i = tid / (CPR / CPT), k0 = (tid % (CPR / CPT)) * CPT;
+    // ---- merge: thread handles chunk k0 of row i over splits sp, sp + SP, sp + 2 SP, ... (all splits if SP = 1)
+    const int col = SP == 1 ? tid : tid % RC, sp = SP == 1 ? 0 : tid / RC;
+    const int i = col / CPR, k0 = col % CPR;
     const int t = t0 + min(i, nrow - 1);  // rows past the last node repeat it (never stored)
     const int m = t * H + h;
     const bf16x8* src = reinterpret_cast<const bf16x8*>(part_o + (size_t)m * R) + k0;
     const size_t stride = (size_t)Mp * CPR;  // bf16x8 per split
     float mx = -INFINITY, den = 0.f;
-    float num[CPT][8];
+    float num[8];
 #pragma unroll
-    for (int u = 0; u < CPT; ++u)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) num[u][e] = 0.f;
-    // Splits are taken CH at a time.  Within a group the reference is the group's largest m_s, so each
-    // split costs one fused multiply-add per element; the running sums are rescaled once per further group.
-    for (int s0 = 0; s0 < S; s0 += CH) {
+    for (int e = 0; e < 8; ++e) num[e] = 0.f;
+    // This group's splits are taken CH at a time.  Within a batch the reference is the batch's largest m_s, so
+    // each split costs one fused multiply-add per element; the running sums are rescaled once per further batch.
+    for (int s0 = 0; sp + s0 * SP < S; s0 += CH) {  // split of batch slot q: sp + (s0 + q) * SP
       float2 ml[CH];
-      bf16x8 v[CH][CPT];
+      bf16x8 v[CH];
 #pragma unroll
       for (int q = 0; q < CH; ++q) {
-        const int sq = min(s0 + q, S - 1);
+        const int sq = min(sp + (s0 + q) * SP, S - 1);  // past S: repeat split S - 1 (weight 0 below)
         ml[q] = part_ml[(size_t)sq * Mp + m];
-#pragma unroll
-        for (int u = 0; u < CPT; ++u) v[q][u] = src[sq * stride + u];
+        v[q] = src[sq * stride];
       }
       float gm = -INFINITY;
 #pragma unroll
-      for (int q = 0; q < CH; ++q) gm = (s0 + q < S) ? fmaxf(gm, ml[q].x) : gm;
+      for (int q = 0; q < CH; ++q) gm = (sp + (s0 + q) * SP < S) ? fmaxf(gm, ml[q].x) : gm;
       const float mn = fmaxf(mx, gm);
       if (mn == -INFINITY) continue;  // nothing visible in any split so far
       if (s0 > 0) {
         const float a = fast_exp2(mx - mn);  // mx = -inf -> 0 (the sums are still 0)
         den *= a;
 #pragma unroll
-        for (int u = 0; u < CPT; ++u)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) num[u][e] *= a;
+        for (int e = 0; e < 8; ++e) num[e] *= a;
       }
 #pragma unroll
       for (int q = 0; q < CH; ++q) {
-        // weight 0 for a split past S (its loads repeat split S - 1) or one in which row m saw nothing
-        const float wq = (s0 + q < S && ml[q].x != -INFINITY) ? fast_exp2(ml[q].x - mn) * ml[q].y : 0.f;
+        // weight 0 for a split past S or one in which row m saw nothing
+        const float wq =
+            (sp + (s0 + q) * SP < S && ml[q].x != -INFINITY) ? fast_exp2(ml[q].x - mn) * ml[q].y : 0.f;
         den += wq;
 #pragma unroll
-        for (int u = 0; u < CPT; ++u)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) num[u][e] = fmaf(wq, (float)v[q][u][e], num[u][e]);
+        for (int e = 0; e < 8; ++e) num[e] = fmaf(wq, (float)v[q][e], num[e]);
       }
       mx = mn;
     }
-    const float inv = 1.f / den;
-#pragma unroll
-    for (int u = 0; u < CPT; ++u) {
+    if constexpr (SP == 1) {
+      const float inv = 1.f / den;
       bf16x8 ov;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ov[e] = (__bf16)(num[u][e] * inv);
-      *reinterpret_cast<bf16x8*>(&o_s[i * OP + (k0 + u) * 8]) = ov;
+      for (int e = 0; e < 8; ++e) ov[e] = (__bf16)(num[e] * inv);
+      *reinterpret_cast<bf16x8*>(&o_s[i * OP + k0 * 8]) = ov;
+      if (lse != nullptr && k0 == 0 && i < nrow) lse[m] = (mx + log2f(den)) * LN2;
+    } else {
+      float* x = gx[sp][col];
+      x[0] = mx;
+      x[1] = den;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[2 + e] = num[e];
     }
-    if (lse != nullptr && k0 == 0 && i < nrow) lse[m] = (mx + log2f(den)) * 0.69314718055994530942f;
+  }
+  if constexpr (SP > 1) {
+    __syncthreads();  // every group's running sums are in LDS
+    if (tid < RC) {
+      // groups in a fixed order; a group that saw nothing (max -inf, sums 0) gets weight 0
+      const int i = tid / CPR, k0 = tid % CPR;
+      float M = -INFINITY;
+#pragma unroll
+      for (int q = 0; q < SP; ++q) M = fmaxf(M, gx[q][tid][0]);
+      float den = 0.f, num[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) num[e] = 0.f;
+#pragma unroll
+      for (int q = 0; q < SP; ++q) {
+        const float* x = gx[q][tid];
+        const float a = (x[0] == -INFINITY) ? 0.f : fast_exp2(x[0] - M);
+        den = fmaf(a, x[1], den);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) num[e] = fmaf(a, x[2 + e], num[e]);
+      }
+      const float inv = 1.f / den;
+      bf16x8 ov;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ov[e] = (__bf16)(num[e] * inv);
+      *reinterpret_cast<bf16x8*>(&o_s[i * OP + k0 * 8]) = ov;
+      const int t = t0 + min(i, nrow - 1);
+      if (lse != nullptr && k0 == 0 && i < nrow) lse[t * H + h] = (M + log2f(den)) * LN2;
+    }
   }
   __syncthreads();  // merged rows and W_UV are in LDS
   if (wave * 32 >= DV) return;  // wave-uniform; no barrier follows
@@ -881,6 +915,7 @@ __global__ __launch_bounds__(NTHREADS) void mfma_probe_kernel(int iters, float* 
 struct Plan {
   int H, nodes;           // heads, nodes of all requests
   int split_blocks, comb_blocks;
+  int comb_rt;            // tree nodes per combine workgroup (4; 2 or 1 for a single request with few heads)
   BatchArgs<MAX_BATCH> ba;
   size_t off_qcat, off_po, off_pml, total;
 };
@@ -948,6 +983,16 @@ static int make_plan(const kdv_mla_dims* d, int C, const int32_t* Ls, const int3
   const int cus = env_splits > 0 ? 0 : device_cu_count();
   if (env_splits <= 0 && cus <= 0) return KDV_ERR_HIP;
   const int R = d->kv_lora_rank, DQ = R + d->qk_rope_dim;
+  // Combine: 4 nodes per workgroup, fewer when a single request's (head, node-block) grid would otherwise leave
+  // CUs idle (8 heads x 32 nodes: 64 workgroups of 4 nodes, 256 of one node).
+  const int cus_rt = cus > 0 ? cus : 256;
+  p->comb_rt = 4;
+  if (C == 1)
+    for (int rt = 1; rt < 4; rt *= 2)
+      if ((int64_t)NUM_XCD * ((H + NUM_XCD - 1) / NUM_XCD) * ((Ts[0] + rt - 1) / rt) <= cus_rt) {
+        p->comb_rt = rt;
+        break;
+      }
   p->H = H;
   p->nodes = (int)nodes;
   p->ba.n = C;
@@ -974,7 +1019,7 @@ static int make_plan(const kdv_mla_dims* d, int C, const int32_t* Ls, const int3
     po += (int64_t)r.splits * r.Mp * R;
     pml += (int64_t)r.splits * r.Mp;
     blk_s += (int64_t)NUM_XCD * r.m_tiles * ((r.splits + NUM_XCD - 1) / NUM_XCD);
-    blk_c += (int64_t)NUM_XCD * ((H + NUM_XCD - 1) / NUM_XCD) * ((r.T + 3) / 4);
+    blk_c += (int64_t)NUM_XCD * ((H + NUM_XCD - 1) / NUM_XCD) * ((r.T + p->comb_rt - 1) / p->comb_rt);
     if (blk_s > 0x7fffffff || blk_c > 0x7fffffff) return KDV_ERR_SHAPE;
     p->ba.blk_split[c + 1] = (int)blk_s;
     p->ba.blk_comb[c + 1] = (int)blk_c;
@@ -1029,12 +1074,14 @@ static void launch_all(const Plan& pl, float sm_scale, const uint16_t* q_nope, c
     one.r[0] = pl.ba.r[0];
     launch(splitkv_kernel<R, DR, 1>, dim3(pl.split_blocks), st, ev ? ev + 2 : nullptr, (const uint16_t*)q_cat, c_kv,
            k_pe, page_table, mask, one, scale_log2, part_o, part_ml);
-    launch_n(combine_up_kernel<R, DV, 1>, dim3(pl.comb_blocks), COMB_THREADS, st, ev ? ev + 4 : nullptr,
-             (const uint16_t*)part_o, (const float2*)part_ml, one, w_uv, out, lse);
+    auto comb = pl.comb_rt == 1 ? combine_up_kernel<R, DV, 1, 1>
+                : pl.comb_rt == 2 ? combine_up_kernel<R, DV, 1, 2> : combine_up_kernel<R, DV, 1, 4>;
+    launch_n(comb, dim3(pl.comb_blocks), COMB_THREADS, st, ev ? ev + 4 : nullptr, (const uint16_t*)part_o,
+             (const float2*)part_ml, one, w_uv, out, lse);
   } else {
     launch(splitkv_kernel<R, DR, MAX_BATCH>, dim3(pl.split_blocks), st, ev ? ev + 2 : nullptr,
            (const uint16_t*)q_cat, c_kv, k_pe, page_table, mask, pl.ba, scale_log2, part_o, part_ml);
-    launch_n(combine_up_kernel<R, DV, MAX_BATCH>, dim3(pl.comb_blocks), COMB_THREADS, st, ev ? ev + 4 : nullptr,
+    launch_n(combine_up_kernel<R, DV, MAX_BATCH, 4>, dim3(pl.comb_blocks), COMB_THREADS, st, ev ? ev + 4 : nullptr,
              (const uint16_t*)part_o, (const float2*)part_ml, pl.ba, w_uv, out, lse);
   }
 }

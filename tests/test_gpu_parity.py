@@ -153,10 +153,20 @@ def test_kimi_tree_sizes(T):
     check(si.kimi(L=300, T=T, seed=100 + T, dist="unit"))
 
 
-@pytest.mark.parametrize("H,T", [(1, 15), (3, 9), (8, 32), (100, 15), (128, 64)])
+@pytest.mark.parametrize("H,T", [(1, 15), (3, 9), (8, 32), (16, 32), (32, 15), (100, 15), (128, 64)])
 def test_kimi_head_counts(H, T):
+    """Also covers each node-block size of the combine: 1 node per workgroup (8 heads x 32 nodes), 2 (16 x 32,
+    32 x 15) and 4 (100 x 15, 128 x 64)."""
     inp = si.make_inputs(**dict(si.KIMI_DIMS, num_heads=H), L=700, T=T, seed=H, dist="unit")
-    check(inp, heads=None if H <= 8 else [0, H // 2, H - 1])
+    check(inp, heads=None if H <= 8 else [0, 1, H // 2, H - 1])
+
+
+@pytest.mark.parametrize("T,splits", [(7, None), (33, None), (33, 5), (64, 9)])
+def test_tiny_combine_node_blocks(T, splits):
+    """64-wide shape, 4 heads: 7 nodes -> 1 node per combine workgroup, 33 and 64 -> 2 (the batched tests cover
+    4); forced split counts give the combine's split groups unequal numbers of splits."""
+    inp = si.make_inputs(**si.TINY_DIMS, L=300, T=T, seed=T, dist="unit")
+    check(inp, splits=splits)
 
 
 @pytest.mark.parametrize("shape", ["chain", "star"])
