@@ -664,13 +664,14 @@ __global__ __launch_bounds__(NTHREADS) void q_absorb_kernel(const uint16_t* __re
 // the node blocks of one head are kept on one XCD, so W_UV[h] is fetched into that XCD's L2 once.  The waves
 // split the fetching so that none waits for the other's loads (a wave's load counter is in order):
 //   - waves 0..3 load the partials of the RT rows into registers and merge them (one 16-byte chunk of a row
-//     per thread for the 512-wide latent);
+//     per thread, over every SP-th split; see below);
 //   - waves 4..7 gather all of W_UV[h] into LDS by DMA (an LDS-DMA gather moves about 2.5 times the
 //     bytes per CU that loads into registers do; the issue cost of a DMA instruction is per wave, so four
 //     waves share it).  Chunk ch of W row r sits at position ch ^ (r % WSW) of the row, so the MFMA's
 //     quarter-wave reads (16 rows, one chunk) hit 16 distinct bank groups.
-// After one barrier, wave w < DV/32 computes D[v][t] = sum_r W_UV[h][v][r] o[t][r] for its 32 columns v, both
-// operands read from LDS (r-contiguous); columns t >= RT of the product repeat the last row, never stored.
+// Once the merged rows and W_UV are in LDS (one barrier; two when the split groups' sums meet in LDS first),
+// wave w < DV/32 computes D[v][t] = sum_r W_UV[h][v][r] o[t][r] for its 32 columns v, both operands read from
+// LDS (r-contiguous); columns t >= RT of the product repeat the last row, never stored.
 constexpr int COMB_THREADS = 512;
 // RT = tree nodes per workgroup (4, or 2 or 1 when a call has few heads and nodes, so that the grid still fills
 // the device).  The merging threads are split into SP groups that take every SP-th split of the same chunks
