@@ -37,6 +37,7 @@ struct ReqArgs {
   int m_tiles, Mp;              // 64-row query tiles of the request's T*H rows, and their padded row count
   int tiles_per_split, splits;  // KV split plan
   int xoff;                     // the request's splits start at this XCD (spreads small requests over the dies)
+  int lin;                      // > 0: contiguous placement, lin workgroup slots per XCD (see splitkv_kernel)
   long long po, pml;            // element offsets of the request's partials in part_o and part_ml
 };
 // NB = capacity: 1 for the single-request entry points (a small kernel-argument block), MAX_BATCH for batches.
@@ -427,11 +428,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void splitkv_kernel(
   float2* part_ml = part_ml_all + pml;
   // Workgroups are dealt to the XCDs round-robin (block b -> XCD b % NUM_XCD; a request's first block is a
   // multiple of NUM_XCD).  Every query tile of one KV split is kept on one XCD so that split's rows are fetched
-  // into that XCD's L2 once and then shared; the request's splits start at XCD xoff.
+  // into that XCD's L2 once and then shared; the request's splits start at XCD xoff.  With the contiguous
+  // placement (lin > 0) XCD x instead takes the (split, query tile) pairs lin*x .. lin*x + lin - 1 in split-major
+  // order: a split straddles at most two XCDs, and the grid can use every CU when the query tiles do not
+  // divide an XCD's CUs.
   const int bid = blockIdx.x - ba.blk_split[rqi];
   const int xcd = bid % NUM_XCD, j = bid / NUM_XCD;
-  const int split = (xcd - rq.xoff + NUM_XCD) % NUM_XCD + NUM_XCD * (j / m_tiles);
-  const int mt = j % m_tiles;
+  const int kl = xcd * rq.lin + j;
+  const int split = rq.lin > 0 ? kl / m_tiles : (xcd - rq.xoff + NUM_XCD) % NUM_XCD + NUM_XCD * (j / m_tiles);
+  const int mt = rq.lin > 0 ? kl % m_tiles : j % m_tiles;
   if (split >= num_splits) return;  // padding block (uniform; before any barrier)
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -687,7 +692,8 @@ __global__ __launch_bounds__(COMB_THREADS) void combine_up_kernel(const uint16_t
   constexpr int CPR = R / 8;                 // 16-byte chunks per latent row
   constexpr int KS = R / 16;                 // MFMA k-steps
   constexpr int OP = R + 8;                  // LDS pitch of a merged row (elements)
-  constexpr int CH = 16;                     // splits whose loads are in flight together
+  constexpr int CH = 17;                     // splits whose loads are in flight together (17: the most the
+                                             // plan gives 15 query tiles on 256 CUs)
   constexpr int NFW = 4;                     // fetching waves (4..7); waves 0..3 merge
   constexpr int RC = RT * CPR;               // chunks of the workgroup's rows, one per merging thread
   constexpr int SP = 256 / RC >= 4 ? 4 : (256 / RC >= 2 ? 2 : 1);  // split groups merged side by side
@@ -1012,6 +1018,19 @@ static int make_plan(const kdv_mla_dims* d, int C, const int32_t* Ls, const int3
     const int nt_plan = (r.L + r.T + KV_TILE - 1) / KV_TILE;  // tiles of the full verify (see above)
     if (want > nt_plan) want = nt_plan;
     r.tiles_per_split = (nt_plan + want - 1) / want;
+    r.lin = 0;
+    if (C == 1 && env_splits <= 0) {
+      // contiguous placement when it gives every workgroup fewer tiles (e.g. 15 query tiles: 17 splits on
+      // 255 CUs instead of 16 on 240)
+      const int lin = cus / NUM_XCD, s_lin = std::min(NUM_XCD * lin / r.m_tiles, nt_plan);
+      if (s_lin >= 1) {
+        const int tps = (nt_plan + s_lin - 1) / s_lin;
+        if (tps < r.tiles_per_split) {
+          r.tiles_per_split = tps;
+          r.lin = lin;
+        }
+      }
+    }
     r.splits = (ntiles[c] + r.tiles_per_split - 1) / r.tiles_per_split;
     r.xoff = (int)(xoff % NUM_XCD);
     xoff += r.splits;
@@ -1019,7 +1038,7 @@ static int make_plan(const kdv_mla_dims* d, int C, const int32_t* Ls, const int3
     r.pml = pml;
     po += (int64_t)r.splits * r.Mp * R;
     pml += (int64_t)r.splits * r.Mp;
-    blk_s += (int64_t)NUM_XCD * r.m_tiles * ((r.splits + NUM_XCD - 1) / NUM_XCD);
+    blk_s += r.lin > 0 ? (int64_t)NUM_XCD * r.lin : (int64_t)NUM_XCD * r.m_tiles * ((r.splits + NUM_XCD - 1) / NUM_XCD);
     blk_c += (int64_t)NUM_XCD * ((H + NUM_XCD - 1) / NUM_XCD) * ((r.T + p->comb_rt - 1) / p->comb_rt);
     if (blk_s > 0x7fffffff || blk_c > 0x7fffffff) return KDV_ERR_SHAPE;
     p->ba.blk_split[c + 1] = (int)blk_s;
