@@ -39,6 +39,7 @@ struct ReqArgs {
   int xoff;                     // the request's splits start at this XCD (spreads small requests over the dies)
   int lin;                      // > 0: contiguous placement, lin workgroup slots per XCD (see splitkv_kernel)
   long long po, pml;            // element offsets of the request's partials in part_o and part_ml
+  long long sk_base;            // stream-K plan: the request's first unit (query tile x KV tile, tile-major)
 };
 // NB = capacity: 1 for the single-request entry points (a small kernel-argument block), MAX_BATCH for batches.
 template <int NB>
@@ -47,6 +48,7 @@ struct BatchArgs {
   int blk_split[NB + 1];  // first split-KV workgroup of each request (multiples of NUM_XCD)
   int blk_comb[NB + 1];   // first combine workgroup of each request (multiples of NUM_XCD)
   ReqArgs r[NB];
+  long long sk_w, sk_u;   // stream-K plan of a batch (sk_w > 0): units per workgroup, units in all
 };
 // Request owning workgroup b (uniform): the last one whose first workgroup is <= b.
 __device__ __forceinline__ int request_of(const int* first, int n, int b) {
@@ -400,23 +402,22 @@ __device__ __forceinline__ void tile_compute(const char* tile, const bf16x8 (&q)
 // Workgroup = 4 waves over 64 query rows (m = t*H + h).  Wave (wi, wj) = (w / 2, w % 2): scores of rows wi*32..+31
 // against KV rows wj*32..+31 of each tile; values for latent columns w*CPW..+CPW of all 64 rows.
 // Two LDS tiles: while one is computed, the next is gathered by DMA (spread over the score MFMAs).
-template <int R, int DR, int NB>
-__global__ __launch_bounds__(NTHREADS, 1) void splitkv_kernel(
-    const uint16_t* __restrict__ q_cat_all, const uint16_t* __restrict__ c_kv, const uint16_t* __restrict__ k_pe,
-    const int32_t* __restrict__ page_table_all, const uint32_t* __restrict__ mask_all, const BatchArgs<NB> ba,
-    float scale_log2, uint16_t* __restrict__ part_o_all, float2* __restrict__ part_ml_all) {
+// One segment of the split-KV pass: query tile mt of request rq against its KV tiles [tile_begin, tile_end),
+// ending with the partial (O / l, max, sum) of those tiles in partial slot `split` of the request.  All threads
+// of the workgroup call it together (it has barriers); it leaves the LDS buffers free for another segment only
+// after the caller's next barrier.
+template <int R, int DR>
+__device__ __forceinline__ void splitkv_segment(const uint16_t* __restrict__ q_cat_all, const uint16_t* __restrict__ c_kv,
+                                                const uint16_t* __restrict__ k_pe,
+                                                const int32_t* __restrict__ page_table_all,
+                                                const uint32_t* __restrict__ mask_all, const ReqArgs& rq, int H,
+                                                int mt, int tile_begin, int tile_end, int split, float scale_log2,
+                                                uint16_t* __restrict__ part_o_all, float2* __restrict__ part_ml_all,
+                                                char* kvbuf, uint4 (*pbuf)[2][2][64], float (*mxch)[2][32],
+                                                float (*psum)[2][32]) {
   using TL = TileLayout<R, DR>;
   constexpr int DQ = R + DR, KB = DQ / 16;
-  __shared__ __attribute__((aligned(1024))) char kvbuf[2 * TL::BYTES];
-  __shared__ uint4 pbuf[2][2][2][64];  // [row block][kv half][16-row k-step][lane]: P^T fragments (bf16)
-  __shared__ float mxch[2][2][32];     // [row block][kv half][row]: proposed reference
-  __shared__ float psum[2][2][32];     // [row block][kv half][row]: half-tile row sum
-
-  // This workgroup's request; its arrays start at the request's offsets.
-  const int rqi = NB > 1 ? request_of(ba.blk_split, ba.n, blockIdx.x) : 0;  // (a constant index for one request)
-  const ReqArgs& rq = ba.r[rqi];
-  const int L = rq.L, T = rq.T, H = ba.H, M = rq.T * ba.H, N = rq.N, m_tiles = rq.m_tiles, Mp = rq.Mp;
-  const int tiles_per_split = rq.tiles_per_split, num_splits = rq.splits;
+  const int L = rq.L, T = rq.T, M = rq.T * H, N = rq.N, Mp = rq.Mp;
   const uint16_t* q_cat = q_cat_all + (size_t)rq.node0 * H * DQ;
   const int32_t* page_table = page_table_all + rq.pt0;
   const uint32_t* mask = (N > L) ? mask_all + rq.mask0 : nullptr;
@@ -426,27 +427,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void splitkv_kernel(
   asm volatile("" : "+s"(po), "+s"(pml));
   uint16_t* part_o = part_o_all + po;
   float2* part_ml = part_ml_all + pml;
-  // Workgroups are dealt to the XCDs round-robin (block b -> XCD b % NUM_XCD; a request's first block is a
-  // multiple of NUM_XCD).  Every query tile of one KV split is kept on one XCD so that split's rows are fetched
-  // into that XCD's L2 once and then shared; the request's splits start at XCD xoff.  With the contiguous
-  // placement (lin > 0) XCD x instead takes the (split, query tile) pairs lin*x .. lin*x + lin - 1 in split-major
-  // order: a split straddles at most two XCDs, and the grid can use every CU when the query tiles do not
-  // divide an XCD's CUs.
-  const int bid = blockIdx.x - ba.blk_split[rqi];
-  const int xcd = bid % NUM_XCD, j = bid / NUM_XCD;
-  const int kl = xcd * rq.lin + j;
-  const int split = rq.lin > 0 ? kl / m_tiles : (xcd - rq.xoff + NUM_XCD) % NUM_XCD + NUM_XCD * (j / m_tiles);
-  const int mt = rq.lin > 0 ? kl % m_tiles : j % m_tiles;
-  if (split >= num_splits) return;  // padding block (uniform; before any barrier)
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wi = wave >> 1, wj = wave & 1;
   const int g = lane >> 5, c = lane & 31;
   const int m = mt * M_TILE + wi * 32 + c;
 
-  const int ntiles = (N + KV_TILE - 1) / KV_TILE;
-  const int tile_begin = split * tiles_per_split;
-  const int tile_end = min(tile_begin + tiles_per_split, ntiles);
 
   // Prologue.  Each wave first gathers the first tile's page-table slice by DMA into its own 256 bytes of the
   // (still idle) exchange buffer; the mask words load; then the query tile (64 rows of q_cat) is gathered by
@@ -566,6 +552,64 @@ __global__ __launch_bounds__(NTHREADS, 1) void splitkv_kernel(
     const int idx = tid + k * NTHREADS, row = idx / CPR, ch = idx % CPR;
     store_agent16(dst + (size_t)row * R + ch * 8, *reinterpret_cast<const u32x4*>(o_s + row * OP + ch * 8));
   }
+}
+
+template <int R, int DR, int NB>
+__global__ __launch_bounds__(NTHREADS, 1) void splitkv_kernel(
+    const uint16_t* __restrict__ q_cat_all, const uint16_t* __restrict__ c_kv, const uint16_t* __restrict__ k_pe,
+    const int32_t* __restrict__ page_table_all, const uint32_t* __restrict__ mask_all, const BatchArgs<NB> ba,
+    float scale_log2, uint16_t* __restrict__ part_o_all, float2* __restrict__ part_ml_all) {
+  using TL = TileLayout<R, DR>;
+  __shared__ __attribute__((aligned(1024))) char kvbuf[2 * TL::BYTES];
+  __shared__ uint4 pbuf[2][2][2][64];  // [row block][kv half][16-row k-step][lane]: P^T fragments (bf16)
+  __shared__ float mxch[2][2][32];     // [row block][kv half][row]: proposed reference
+  __shared__ float psum[2][2][32];     // [row block][kv half][row]: half-tile row sum
+
+  if (NB > 1 && ba.sk_w > 0) {
+    // Stream-K plan of a batch: the (request, query tile, KV tile) units, query-tile-major within a request,
+    // are dealt out in contiguous runs of sk_w; a run that crosses the end of a query tile is one segment per
+    // query tile it touches.  Segment slot = this workgroup's index minus that of the first workgroup that
+    // touches the query tile, so a query tile's slots are 0 .. (its workgroups - 1).
+    const long long u1 = min((long long)(blockIdx.x + 1) * ba.sk_w, ba.sk_u);
+    for (long long u = (long long)blockIdx.x * ba.sk_w; u < u1;) {
+      int rqi = 0;
+      while (rqi + 1 < ba.n && u >= ba.r[rqi + 1].sk_base) ++rqi;  // (uniform scalar search)
+      const ReqArgs& rq = ba.r[rqi];
+      const int nt = (rq.N + KV_TILE - 1) / KV_TILE;
+      const long long off = u - rq.sk_base, first = rq.sk_base + (off / nt) * nt;
+      const int mt = (int)(off / nt), t0 = (int)(off % nt);
+      const long long seg_end = min(u1, first + nt);
+      const int slot = (int)(blockIdx.x - first / ba.sk_w);
+      splitkv_segment<R, DR>(q_cat_all, c_kv, k_pe, page_table_all, mask_all, rq, ba.H, mt, t0,
+                             t0 + (int)(seg_end - u), slot, scale_log2, part_o_all, part_ml_all, kvbuf, pbuf, mxch,
+                             psum);
+      u = seg_end;
+      __syncthreads();  // the next segment's DMAs reuse the LDS the epilogue read
+    }
+    return;
+  }
+
+  // This workgroup's request; its arrays start at the request's offsets.
+  const int rqi = NB > 1 ? request_of(ba.blk_split, ba.n, blockIdx.x) : 0;  // (a constant index for one request)
+  const ReqArgs& rq = ba.r[rqi];
+  const int m_tiles = rq.m_tiles;
+  // Workgroups are dealt to the XCDs round-robin (block b -> XCD b % NUM_XCD; a request's first block is a
+  // multiple of NUM_XCD).  Every query tile of one KV split is kept on one XCD so that split's rows are fetched
+  // into that XCD's L2 once and then shared; the request's splits start at XCD xoff.  With the contiguous
+  // placement (lin > 0) XCD x instead takes the (split, query tile) pairs lin*x .. lin*x + lin - 1 in split-major
+  // order: a split straddles at most two XCDs, and the grid can use every CU when the query tiles do not
+  // divide an XCD's CUs.
+  const int bid = blockIdx.x - ba.blk_split[rqi];
+  const int xcd = bid % NUM_XCD, j = bid / NUM_XCD;
+  const int kl = xcd * rq.lin + j;
+  const int split = rq.lin > 0 ? kl / m_tiles : (xcd - rq.xoff + NUM_XCD) % NUM_XCD + NUM_XCD * (j / m_tiles);
+  const int mt = rq.lin > 0 ? kl % m_tiles : j % m_tiles;
+  if (split >= rq.splits) return;  // padding block (uniform; before any barrier)
+  const int ntiles = (rq.N + KV_TILE - 1) / KV_TILE;
+  const int tile_begin = split * rq.tiles_per_split;
+  const int tile_end = min(tile_begin + rq.tiles_per_split, ntiles);
+  splitkv_segment<R, DR>(q_cat_all, c_kv, k_pe, page_table_all, mask_all, rq, ba.H, mt, tile_begin, tile_end, split,
+                         scale_log2, part_o_all, part_ml_all, kvbuf, pbuf, mxch, psum);
 }
 
 // ------------------------------------------------------------------------------------------------ q_absorb
@@ -746,6 +790,13 @@ __global__ __launch_bounds__(COMB_THREADS) void combine_up_kernel(const uint16_t
     const int i = col / CPR, k0 = col % CPR;
     const int t = t0 + min(i, nrow - 1);  // rows past the last node repeat it (never stored)
     const int m = t * H + h;
+    // partial slots of this row: all S splits, or under a batch's stream-K plan the runs that touched its
+    // query tile (the first run's slot is 0)
+    int Sr = S;
+    if (NB > 1 && ba.sk_w > 0) {
+      const long long nt = (rq.N + KV_TILE - 1) / KV_TILE, a = rq.sk_base + (long long)(m / M_TILE) * nt;
+      Sr = (int)((a + nt - 1) / ba.sk_w - a / ba.sk_w + 1);
+    }
     const bf16x8* src = reinterpret_cast<const bf16x8*>(part_o + (size_t)m * R) + k0;
     const size_t stride = (size_t)Mp * CPR;  // bf16x8 per split
     float mx = -INFINITY, den = 0.f;
@@ -754,18 +805,18 @@ __global__ __launch_bounds__(COMB_THREADS) void combine_up_kernel(const uint16_t
     for (int e = 0; e < 8; ++e) num[e] = 0.f;
     // This group's splits are taken CH at a time.  Within a batch the reference is the batch's largest m_s, so
     // each split costs one fused multiply-add per element; the running sums are rescaled once per further batch.
-    for (int s0 = 0; sp + s0 * SP < S; s0 += CH) {  // split of batch slot q: sp + (s0 + q) * SP
+    for (int s0 = 0; sp + s0 * SP < Sr; s0 += CH) {  // split of batch slot q: sp + (s0 + q) * SP
       float2 ml[CH];
       bf16x8 v[CH];
 #pragma unroll
       for (int q = 0; q < CH; ++q) {
-        const int sq = min(sp + (s0 + q) * SP, S - 1);  // past S: repeat split S - 1 (weight 0 below)
+        const int sq = min(sp + (s0 + q) * SP, Sr - 1);  // past Sr: repeat split Sr - 1 (weight 0 below)
         ml[q] = part_ml[(size_t)sq * Mp + m];
         v[q] = src[sq * stride];
       }
       float gm = -INFINITY;
 #pragma unroll
-      for (int q = 0; q < CH; ++q) gm = (sp + (s0 + q) * SP < S) ? fmaxf(gm, ml[q].x) : gm;
+      for (int q = 0; q < CH; ++q) gm = (sp + (s0 + q) * SP < Sr) ? fmaxf(gm, ml[q].x) : gm;
       const float mn = fmaxf(mx, gm);
       if (mn == -INFINITY) continue;  // nothing visible in any split so far
       if (s0 > 0) {
@@ -778,7 +829,7 @@ __global__ __launch_bounds__(COMB_THREADS) void combine_up_kernel(const uint16_t
       for (int q = 0; q < CH; ++q) {
         // weight 0 for a split past S or one in which row m saw nothing
         const float wq =
-            (sp + (s0 + q) * SP < S && ml[q].x != -INFINITY) ? fast_exp2(ml[q].x - mn) * ml[q].y : 0.f;
+            (sp + (s0 + q) * SP < Sr && ml[q].x != -INFINITY) ? fast_exp2(ml[q].x - mn) * ml[q].y : 0.f;
         den += wq;
 #pragma unroll
         for (int e = 0; e < 8; ++e) num[e] = fmaf(wq, (float)v[q][e], num[e]);
@@ -1005,9 +1056,44 @@ static int make_plan(const kdv_mla_dims* d, int C, const int32_t* Ls, const int3
   p->ba.n = C;
   p->ba.H = H;
   p->ba.blk_split[0] = p->ba.blk_comb[0] = 0;
-  int64_t po = 0, pml = 0, blk_s = 0, blk_c = 0, xoff = 0;
+  // A batch (several requests, no fixed split count) takes the stream-K plan: every CU gets an equal
+  // contiguous run of the (request, query tile, KV tile) units, query-tile-major within a request.  A query
+  // tile's partial slots are the runs that touch it.
+  const bool streamk = C > 1 && env_splits <= 0 && with_tree;
+  p->ba.sk_w = p->ba.sk_u = 0;
+  int64_t sk_wgs = 0;
+  if (streamk) {
+    const int64_t units = work, wgs = std::min<int64_t>(cus, units);
+    p->ba.sk_w = (units + wgs - 1) / wgs;
+    p->ba.sk_u = units;
+    sk_wgs = (units + p->ba.sk_w - 1) / p->ba.sk_w;
+  }
+  int64_t po = 0, pml = 0, blk_s = 0, blk_c = 0, xoff = 0, sk_base = 0;
   for (int c = 0; c < C; ++c) {
     ReqArgs& r = p->ba.r[c];
+    r.sk_base = sk_base;
+    if (streamk) {
+      r.tiles_per_split = ntiles[c];
+      r.lin = 0;
+      r.xoff = 0;
+      int slots = 1;
+      for (int mt = 0; mt < r.m_tiles; ++mt) {
+        const int64_t a = sk_base + (int64_t)mt * ntiles[c], b = a + ntiles[c] - 1;
+        slots = std::max<int64_t>(slots, b / p->ba.sk_w - a / p->ba.sk_w + 1);
+      }
+      r.splits = slots;
+      sk_base += (int64_t)r.m_tiles * ntiles[c];
+      r.po = po;
+      r.pml = pml;
+      po += (int64_t)r.splits * r.Mp * R;
+      pml += (int64_t)r.splits * r.Mp;
+      blk_c += (int64_t)NUM_XCD * ((H + NUM_XCD - 1) / NUM_XCD) * ((r.T + p->comb_rt - 1) / p->comb_rt);
+      if (blk_c > 0x7fffffff) return KDV_ERR_SHAPE;
+      p->ba.blk_split[c + 1] = (int)sk_wgs;
+      p->ba.blk_comb[c + 1] = (int)blk_c;
+      blk_s = sk_wgs;
+      continue;
+    }
     int want = env_splits;
     if (want <= 0) {
       const int share = (C == 1) ? cus : (int)std::max<int64_t>(NUM_XCD, (int64_t)cus * m_tiles[c] * ntiles[c] / work);
@@ -1088,6 +1174,8 @@ static void launch_all(const Plan& pl, float sm_scale, const uint16_t* q_nope, c
     BatchArgs<1> one;
     one.n = 1;
     one.H = pl.ba.H;
+    one.sk_w = 0;
+    one.sk_u = 0;
     one.blk_split[0] = one.blk_comb[0] = 0;
     one.blk_split[1] = pl.ba.blk_split[1];
     one.blk_comb[1] = pl.ba.blk_comb[1];
