@@ -39,7 +39,7 @@ struct ReqArgs {
   int xoff;                     // the request's splits start at this XCD (spreads small requests over the dies)
   int lin;                      // > 0: contiguous placement, lin workgroup slots per XCD (see splitkv_kernel)
   long long po, pml;            // element offsets of the request's partials in part_o and part_ml
-  long long sk_base;            // stream-K plan: the request's first unit (query tile x KV tile, tile-major)
+  long long sk_base;            // stream-K plan: the request's first KV tile in the concatenation of all requests
 };
 // NB = capacity: 1 for the single-request entry points (a small kernel-argument block), MAX_BATCH for batches.
 template <int NB>
@@ -48,7 +48,10 @@ struct BatchArgs {
   int blk_split[NB + 1];  // first split-KV workgroup of each request (multiples of NUM_XCD)
   int blk_comb[NB + 1];   // first combine workgroup of each request (multiples of NUM_XCD)
   ReqArgs r[NB];
-  long long sk_w, sk_u;   // stream-K plan of a batch (sk_w > 0): units per workgroup, units in all
+  // stream-K plan of a batch (sk_w > 0): KV tiles per run, KV tiles of all requests, workgroups per group (one
+  // per query tile), workgroup slots per XCD, groups
+  long long sk_w, sk_u;
+  int sk_g, sk_lin, sk_groups;
 };
 // Request owning workgroup b (uniform): the last one whose first workgroup is <= b.
 __device__ __forceinline__ int request_of(const int* first, int n, int b) {
@@ -566,24 +569,25 @@ __global__ __launch_bounds__(NTHREADS, 1) void splitkv_kernel(
   __shared__ float psum[2][2][32];     // [row block][kv half][row]: half-tile row sum
 
   if (NB > 1 && ba.sk_w > 0) {
-    // Stream-K plan of a batch: the (request, query tile, KV tile) units, query-tile-major within a request,
-    // are dealt out in contiguous runs of sk_w; a run that crosses the end of a query tile is one segment per
-    // query tile it touches.  Segment slot = this workgroup's index minus that of the first workgroup that
-    // touches the query tile, so a query tile's slots are 0 .. (its workgroups - 1).
-    const long long u1 = min((long long)(blockIdx.x + 1) * ba.sk_w, ba.sk_u);
-    for (long long u = (long long)blockIdx.x * ba.sk_w; u < u1;) {
+    // Stream-K plan of a batch: the KV tiles of all requests, concatenated, are dealt out in equal contiguous
+    // runs, one per group of sk_g workgroups; member j of a group takes query tile j of every request its run
+    // touches (one segment per request), so a group's members read the same KV tiles at the same time, as the
+    // query tiles of one split do.  Groups are laid out contiguously over the XCDs (slots lin*x .. lin*x+lin-1
+    // on XCD x).  A request's partial slots are the runs that touch it: slot = group - (first such group).
+    const int k = (int)(blockIdx.x % NUM_XCD) * ba.sk_lin + (int)(blockIdx.x / NUM_XCD);
+    const int gi = k / ba.sk_g, mj = k % ba.sk_g;
+    if (gi >= ba.sk_groups) return;  // spare slot (uniform; before any barrier)
+    const long long p1 = min((long long)(gi + 1) * ba.sk_w, ba.sk_u);
+    for (long long p = (long long)gi * ba.sk_w; p < p1;) {
       int rqi = 0;
-      while (rqi + 1 < ba.n && u >= ba.r[rqi + 1].sk_base) ++rqi;  // (uniform scalar search)
+      while (rqi + 1 < ba.n && p >= ba.r[rqi + 1].sk_base) ++rqi;  // (uniform scalar search)
       const ReqArgs& rq = ba.r[rqi];
-      const int nt = (rq.N + KV_TILE - 1) / KV_TILE;
-      const long long off = u - rq.sk_base, first = rq.sk_base + (off / nt) * nt;
-      const int mt = (int)(off / nt), t0 = (int)(off % nt);
-      const long long seg_end = min(u1, first + nt);
-      const int slot = (int)(blockIdx.x - first / ba.sk_w);
-      splitkv_segment<R, DR>(q_cat_all, c_kv, k_pe, page_table_all, mask_all, rq, ba.H, mt, t0,
-                             t0 + (int)(seg_end - u), slot, scale_log2, part_o_all, part_ml_all, kvbuf, pbuf, mxch,
-                             psum);
-      u = seg_end;
+      const long long nt = (rq.N + KV_TILE - 1) / KV_TILE, seg_end = min(p1, rq.sk_base + nt);
+      if (mj < rq.m_tiles)  // (uniform)
+        splitkv_segment<R, DR>(q_cat_all, c_kv, k_pe, page_table_all, mask_all, rq, ba.H, mj, (int)(p - rq.sk_base),
+                               (int)(seg_end - rq.sk_base), (int)(gi - rq.sk_base / ba.sk_w), scale_log2,
+                               part_o_all, part_ml_all, kvbuf, pbuf, mxch, psum);
+      p = seg_end;
       __syncthreads();  // the next segment's DMAs reuse the LDS the epilogue read
     }
     return;
@@ -790,13 +794,7 @@ __global__ __launch_bounds__(COMB_THREADS) void combine_up_kernel(const uint16_t
     const int i = col / CPR, k0 = col % CPR;
     const int t = t0 + min(i, nrow - 1);  // rows past the last node repeat it (never stored)
     const int m = t * H + h;
-    // partial slots of this row: all S splits, or under a batch's stream-K plan the runs that touched its
-    // query tile (the first run's slot is 0)
-    int Sr = S;
-    if (NB > 1 && ba.sk_w > 0) {
-      const long long nt = (rq.N + KV_TILE - 1) / KV_TILE, a = rq.sk_base + (long long)(m / M_TILE) * nt;
-      Sr = (int)((a + nt - 1) / ba.sk_w - a / ba.sk_w + 1);
-    }
+    const int Sr = S;  // partial slots of this row (under a batch's stream-K plan: the runs that touched it)
     const bf16x8* src = reinterpret_cast<const bf16x8*>(part_o + (size_t)m * R) + k0;
     const size_t stride = (size_t)Mp * CPR;  // bf16x8 per split
     float mx = -INFINITY, den = 0.f;
@@ -1056,17 +1054,26 @@ static int make_plan(const kdv_mla_dims* d, int C, const int32_t* Ls, const int3
   p->ba.n = C;
   p->ba.H = H;
   p->ba.blk_split[0] = p->ba.blk_comb[0] = 0;
-  // A batch (several requests, no fixed split count) takes the stream-K plan: every CU gets an equal
-  // contiguous run of the (request, query tile, KV tile) units, query-tile-major within a request.  A query
-  // tile's partial slots are the runs that touch it.
-  const bool streamk = C > 1 && env_splits <= 0 && with_tree;
+  // A batch (several requests, no fixed split count) takes the stream-K plan: groups of G workgroups (G = the
+  // most query tiles of any request), laid out contiguously over the XCDs; the KV tiles of all requests,
+  // concatenated, are dealt out in equal contiguous runs, one per group.  A request's partial slots are the
+  // runs that touch its KV tiles, the same for each of its query tiles.
+  int64_t G = 1, kv_all = 0;
+  for (int c = 0; c < C; ++c) {
+    G = std::max<int64_t>(G, m_tiles[c]);
+    kv_all += ntiles[c];
+  }
+  const int lin_sk = cus / NUM_XCD;
+  const bool streamk = C > 1 && env_splits <= 0 && with_tree && (int64_t)NUM_XCD * lin_sk >= G;
   p->ba.sk_w = p->ba.sk_u = 0;
-  int64_t sk_wgs = 0;
+  p->ba.sk_g = p->ba.sk_lin = p->ba.sk_groups = 0;
   if (streamk) {
-    const int64_t units = work, wgs = std::min<int64_t>(cus, units);
-    p->ba.sk_w = (units + wgs - 1) / wgs;
-    p->ba.sk_u = units;
-    sk_wgs = (units + p->ba.sk_w - 1) / p->ba.sk_w;
+    const int64_t groups = std::min<int64_t>((int64_t)NUM_XCD * lin_sk / G, kv_all);
+    p->ba.sk_w = (kv_all + groups - 1) / groups;
+    p->ba.sk_u = kv_all;
+    p->ba.sk_g = (int)G;
+    p->ba.sk_lin = lin_sk;
+    p->ba.sk_groups = (int)((kv_all + p->ba.sk_w - 1) / p->ba.sk_w);
   }
   int64_t po = 0, pml = 0, blk_s = 0, blk_c = 0, xoff = 0, sk_base = 0;
   for (int c = 0; c < C; ++c) {
@@ -1076,22 +1083,17 @@ static int make_plan(const kdv_mla_dims* d, int C, const int32_t* Ls, const int3
       r.tiles_per_split = ntiles[c];
       r.lin = 0;
       r.xoff = 0;
-      int slots = 1;
-      for (int mt = 0; mt < r.m_tiles; ++mt) {
-        const int64_t a = sk_base + (int64_t)mt * ntiles[c], b = a + ntiles[c] - 1;
-        slots = std::max<int64_t>(slots, b / p->ba.sk_w - a / p->ba.sk_w + 1);
-      }
-      r.splits = slots;
-      sk_base += (int64_t)r.m_tiles * ntiles[c];
+      r.splits = (int)((sk_base + ntiles[c] - 1) / p->ba.sk_w - sk_base / p->ba.sk_w + 1);
+      sk_base += ntiles[c];
       r.po = po;
       r.pml = pml;
       po += (int64_t)r.splits * r.Mp * R;
       pml += (int64_t)r.splits * r.Mp;
       blk_c += (int64_t)NUM_XCD * ((H + NUM_XCD - 1) / NUM_XCD) * ((r.T + p->comb_rt - 1) / p->comb_rt);
       if (blk_c > 0x7fffffff) return KDV_ERR_SHAPE;
-      p->ba.blk_split[c + 1] = (int)sk_wgs;
+      blk_s = (int64_t)NUM_XCD * lin_sk;
+      p->ba.blk_split[c + 1] = (int)blk_s;
       p->ba.blk_comb[c + 1] = (int)blk_c;
-      blk_s = sk_wgs;
       continue;
     }
     int want = env_splits;
