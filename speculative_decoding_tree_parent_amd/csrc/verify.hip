@@ -740,21 +740,24 @@ __global__ __launch_bounds__(COMB_THREADS) void combine_up_kernel(const uint16_t
   constexpr int CPR = R / 8;                 // 16-byte chunks per latent row
   constexpr int KS = R / 16;                 // MFMA k-steps
   constexpr int OP = R + 8;                  // LDS pitch of a merged row (elements)
-  constexpr int CH = 17;                     // splits whose loads are in flight together (17: the most the
-                                             // plan gives 15 query tiles on 256 CUs)
   constexpr int NFW = 4;                     // fetching waves (4..7); waves 0..3 merge
-  constexpr int RC = RT * CPR;               // chunks of the workgroup's rows, one per merging thread
-  constexpr int SP = 256 / RC >= 4 ? 4 : (256 / RC >= 2 ? 2 : 1);  // split groups merged side by side
-  constexpr int MT = RC * SP;                // merging threads (in waves 0..3)
+  constexpr int RC = RT * CPR;               // chunks of the workgroup's rows
+  constexpr int CPT = RC > 256 ? RC / 256 : 1;  // chunks per merging thread (16 nodes: 4)
+  constexpr int RCT = RC / CPT;              // merging threads per split group
+  constexpr int SP = 256 / RCT >= 4 ? 4 : (256 / RCT >= 2 ? 2 : 1);  // split groups merged side by side
+  constexpr int MT = RCT * SP;               // merging threads (in waves 0..3)
+  // splits whose loads are in flight together (17: the most the plan gives 15 query tiles on 256 CUs; fewer
+  // when a thread merges several chunks, to bound its registers)
+  constexpr int CH = CPT == 1 ? 17 : 16 / CPT;
   constexpr int WSW = CPR < 16 ? CPR : 16;   // W_UV staging swizzle width (chunks)
   constexpr int WBYTES = DV * R * 2;         // all of W_UV[h]
   constexpr int WINS = WBYTES / 1024 / NFW;  // DMA instructions per fetching wave
-  static_assert(RC <= 256 && MT <= 256, "one chunk per merging thread");
+  static_assert(RC % CPT == 0 && CPR % CPT == 0 && MT <= 256 && (CPT == 1 || SP == 1), "merging threads");
   static_assert(DV % 32 == 0 && DV / 32 <= 4, "one merging wave per 32 output columns");
   static_assert(WBYTES % (1024 * NFW) == 0, "W_UV must split evenly over the fetching waves");
   __shared__ __attribute__((aligned(16))) uint16_t o_s[RT * OP];
   __shared__ __attribute__((aligned(1024))) char w_s[WBYTES];
-  __shared__ float gx[SP > 1 ? SP : 1][SP > 1 ? RC : 1][10];  // per split group: max, sum, 8 numerators
+  __shared__ float gx[SP > 1 ? SP : 1][SP > 1 ? RCT : 1][10];  // per split group: max, sum, 8 numerators
   const int rqi = NB > 1 ? request_of(ba.blk_comb, ba.n, blockIdx.x) : 0;
   const ReqArgs& rq = ba.r[rqi];
   const int T = rq.T, H = ba.H;
@@ -789,28 +792,31 @@ __global__ __launch_bounds__(COMB_THREADS) void combine_up_kernel(const uint16_t
     }
     wait_vmem_all();
   } else if (tid < MT) {
-    // ---- merge: thread handles chunk k0 of row i over splits sp, sp + SP, sp + 2 SP, ... (all splits if SP = 1)
-    const int col = SP == 1 ? tid : tid % RC, sp = SP == 1 ? 0 : tid / RC;
-    const int i = col / CPR, k0 = col % CPR;
+    // ---- merge: thread handles chunks k0 .. k0 + CPT - 1 of row i over splits sp, sp + SP, ... (all if SP = 1)
+    const int col = SP == 1 ? tid : tid % RCT, sp = SP == 1 ? 0 : tid / RCT;
+    const int i = col * CPT / CPR, k0 = col * CPT % CPR;
     const int t = t0 + min(i, nrow - 1);  // rows past the last node repeat it (never stored)
     const int m = t * H + h;
     const int Sr = S;  // partial slots of this row (under a batch's stream-K plan: the runs that touched it)
     const bf16x8* src = reinterpret_cast<const bf16x8*>(part_o + (size_t)m * R) + k0;
     const size_t stride = (size_t)Mp * CPR;  // bf16x8 per split
     float mx = -INFINITY, den = 0.f;
-    float num[8];
+    float num[CPT][8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) num[e] = 0.f;
+    for (int u = 0; u < CPT; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) num[u][e] = 0.f;
     // This group's splits are taken CH at a time.  Within a batch the reference is the batch's largest m_s, so
     // each split costs one fused multiply-add per element; the running sums are rescaled once per further batch.
     for (int s0 = 0; sp + s0 * SP < Sr; s0 += CH) {  // split of batch slot q: sp + (s0 + q) * SP
       float2 ml[CH];
-      bf16x8 v[CH];
+      bf16x8 v[CH][CPT];
 #pragma unroll
       for (int q = 0; q < CH; ++q) {
         const int sq = min(sp + (s0 + q) * SP, Sr - 1);  // past Sr: repeat split Sr - 1 (weight 0 below)
         ml[q] = part_ml[(size_t)sq * Mp + m];
-        v[q] = src[sq * stride];
+#pragma unroll
+        for (int u = 0; u < CPT; ++u) v[q][u] = src[sq * stride + u];
       }
       float gm = -INFINITY;
 #pragma unroll
@@ -821,7 +827,9 @@ __global__ __launch_bounds__(COMB_THREADS) void combine_up_kernel(const uint16_t
         const float a = fast_exp2(mx - mn);  // mx = -inf -> 0 (the sums are still 0)
         den *= a;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) num[e] *= a;
+        for (int u = 0; u < CPT; ++u)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) num[u][e] *= a;
       }
 #pragma unroll
       for (int q = 0; q < CH; ++q) {
@@ -830,28 +838,33 @@ __global__ __launch_bounds__(COMB_THREADS) void combine_up_kernel(const uint16_t
             (sp + (s0 + q) * SP < Sr && ml[q].x != -INFINITY) ? fast_exp2(ml[q].x - mn) * ml[q].y : 0.f;
         den += wq;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) num[e] = fmaf(wq, (float)v[q][e], num[e]);
+        for (int u = 0; u < CPT; ++u)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) num[u][e] = fmaf(wq, (float)v[q][u][e], num[u][e]);
       }
       mx = mn;
     }
     if constexpr (SP == 1) {
       const float inv = 1.f / den;
-      bf16x8 ov;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ov[e] = (__bf16)(num[e] * inv);
-      *reinterpret_cast<bf16x8*>(&o_s[i * OP + k0 * 8]) = ov;
+      for (int u = 0; u < CPT; ++u) {
+        bf16x8 ov;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ov[e] = (__bf16)(num[u][e] * inv);
+        *reinterpret_cast<bf16x8*>(&o_s[i * OP + (k0 + u) * 8]) = ov;
+      }
       if (lse != nullptr && k0 == 0 && i < nrow) lse[m] = (mx + log2f(den)) * LN2;
     } else {
       float* x = gx[sp][col];
       x[0] = mx;
       x[1] = den;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[2 + e] = num[e];
+      for (int e = 0; e < 8; ++e) x[2 + e] = num[0][e];
     }
   }
   if constexpr (SP > 1) {
     __syncthreads();  // every group's running sums are in LDS
-    if (tid < RC) {
+    if (tid < RCT) {
       // groups in a fixed order; a group that saw nothing (max -inf, sums 0) gets weight 0
       const int i = tid / CPR, k0 = tid % CPR;
       float M = -INFINITY;
@@ -1041,14 +1054,21 @@ static int make_plan(const kdv_mla_dims* d, int C, const int32_t* Ls, const int3
   const int R = d->kv_lora_rank, DQ = R + d->qk_rope_dim;
   // Combine: 4 nodes per workgroup, fewer when a single request's (head, node-block) grid would otherwise leave
   // CUs idle (8 heads x 32 nodes: 64 workgroups of 4 nodes, 256 of one node).
+  // A batch takes 16 nodes per workgroup when 4 would need more workgroups than CUs: every workgroup gathers
+  // all of W_UV[h] (128 KB), so ten 15-node requests at 4 nodes cost 2560 gathers, at 16 nodes 640.
   const int cus_rt = cus > 0 ? cus : 256;
   p->comb_rt = 4;
-  if (C == 1)
+  if (C == 1) {
     for (int rt = 1; rt < 4; rt *= 2)
       if ((int64_t)NUM_XCD * ((H + NUM_XCD - 1) / NUM_XCD) * ((Ts[0] + rt - 1) / rt) <= cus_rt) {
         p->comb_rt = rt;
         break;
       }
+  } else {
+    int64_t wgs4 = 0;
+    for (int c = 0; c < C; ++c) wgs4 += (int64_t)NUM_XCD * ((H + NUM_XCD - 1) / NUM_XCD) * ((Ts[c] + 3) / 4);
+    if (wgs4 > cus_rt) p->comb_rt = 16;
+  }
   p->H = H;
   p->nodes = (int)nodes;
   p->ba.n = C;
@@ -1191,7 +1211,8 @@ static void launch_all(const Plan& pl, float sm_scale, const uint16_t* q_nope, c
   } else {
     launch(splitkv_kernel<R, DR, MAX_BATCH>, dim3(pl.split_blocks), st, ev ? ev + 2 : nullptr,
            (const uint16_t*)q_cat, c_kv, k_pe, page_table, mask, pl.ba, scale_log2, part_o, part_ml);
-    launch_n(combine_up_kernel<R, DV, MAX_BATCH, 4>, dim3(pl.comb_blocks), COMB_THREADS, st, ev ? ev + 4 : nullptr,
+    launch_n(pl.comb_rt == 16 ? combine_up_kernel<R, DV, MAX_BATCH, 16> : combine_up_kernel<R, DV, MAX_BATCH, 4>,
+             dim3(pl.comb_blocks), COMB_THREADS, st, ev ? ev + 4 : nullptr,
              (const uint16_t*)part_o, (const float2*)part_ml, pl.ba, w_uv, out, lse);
   }
 }
