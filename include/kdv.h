@@ -191,8 +191,9 @@ int kdv_verify_mla_attn_profiled(const kdv_mla_dims* d, const uint16_t* q_nope, 
  * beside one ("The Three Acts of Engineering: Diagnosis, Extension, and Analytical Pivot in a Speculative
  * Decoding Stack", section "References", item [3]) and list batching among the throughput levers ("From
  * Diagnosis to Deployment: Three Threads of Inference Engineering for Kimi K2.6", section "The Diagnostic
- * Infrastructure").  Request c's result is what kdv_verify_mla_attn computes for it alone; the requests only
- * share the launches, so that small trees fill the device together.
+ * Infrastructure").  Request c's result is what kdv_verify_mla_attn computes for it alone, up to the rounding
+ * of a different division of its KV rows into splits: the requests share the launches, and unless a split
+ * count is forced (KDV_SPLITS) the KV tiles of all requests are dealt out in equal runs over the CUs.
  *   C          : 1 <= C <= KDV_MAX_BATCH.
  *   L, T       : host int32 [C]: prefix length (>= 0) and tree size (1..64) of each request.
  *   Requests are packed in order.  With n_c = T[0] + ... + T[c-1]:
