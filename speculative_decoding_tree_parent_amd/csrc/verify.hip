@@ -716,7 +716,7 @@ __global__ __launch_bounds__(NTHREADS) void q_absorb_kernel(const uint16_t* __re
 // One workgroup of 8 waves per (head, block of RT nodes).  Workgroups are dealt to the XCDs round-robin, and
 // the node blocks of one head are kept on one XCD, so W_UV[h] is fetched into that XCD's L2 once.  The waves
 // split the fetching so that none waits for the other's loads (a wave's load counter is in order):
-//   - waves 0..3 load the partials of the RT rows into registers and merge them (one 16-byte chunk of a row
+//   - waves 0..3 load the partials of the RT rows into registers and merge them (CPT 16-byte chunks of a row
 //     per thread, over every SP-th split; see below);
 //   - waves 4..7 gather all of W_UV[h] into LDS by DMA (an LDS-DMA gather moves about 2.5 times the
 //     bytes per CU that loads into registers do; the issue cost of a DMA instruction is per wave, so four
@@ -726,10 +726,11 @@ __global__ __launch_bounds__(NTHREADS) void q_absorb_kernel(const uint16_t* __re
 // wave w < DV/32 computes D[v][t] = sum_r W_UV[h][v][r] o[t][r] for its 32 columns v, both operands read from
 // LDS (r-contiguous); columns t >= RT of the product repeat the last row, never stored.
 constexpr int COMB_THREADS = 512;
-// RT = tree nodes per workgroup (4, or 2 or 1 when a call has few heads and nodes, so that the grid still fills
-// the device).  The merging threads are split into SP groups that take every SP-th split of the same chunks
-// (SP > 1 when the RT rows have fewer chunks than there are merging threads); the groups' running (max, sum,
-// numerator) meet in LDS and are combined in a fixed order.
+// RT = tree nodes per workgroup: 4; 2 or 1 when a call has few heads and nodes, so that the grid still fills the
+// device; 16 for a batch whose 4-node grid would exceed the CUs (fewer W_UV gathers).  A merging thread takes
+// CPT chunks (1, or 4 for 16 nodes).  When the rows have fewer chunks than there are merging threads, the
+// threads are split into SP groups that take every SP-th split of the same chunks; the groups' running (max,
+// sum, numerators) meet in LDS and are combined in a fixed order.
 template <int R, int DV, int NB, int RT>
 __global__ __launch_bounds__(COMB_THREADS) void combine_up_kernel(const uint16_t* __restrict__ part_o_all,
                                                               const float2* __restrict__ part_ml_all,
@@ -797,7 +798,6 @@ __global__ __launch_bounds__(COMB_THREADS) void combine_up_kernel(const uint16_t
     const int i = col * CPT / CPR, k0 = col * CPT % CPR;
     const int t = t0 + min(i, nrow - 1);  // rows past the last node repeat it (never stored)
     const int m = t * H + h;
-    const int Sr = S;  // partial slots of this row (under a batch's stream-K plan: the runs that touched it)
     const bf16x8* src = reinterpret_cast<const bf16x8*>(part_o + (size_t)m * R) + k0;
     const size_t stride = (size_t)Mp * CPR;  // bf16x8 per split
     float mx = -INFINITY, den = 0.f;
@@ -808,19 +808,19 @@ __global__ __launch_bounds__(COMB_THREADS) void combine_up_kernel(const uint16_t
       for (int e = 0; e < 8; ++e) num[u][e] = 0.f;
     // This group's splits are taken CH at a time.  Within a batch the reference is the batch's largest m_s, so
     // each split costs one fused multiply-add per element; the running sums are rescaled once per further batch.
-    for (int s0 = 0; sp + s0 * SP < Sr; s0 += CH) {  // split of batch slot q: sp + (s0 + q) * SP
+    for (int s0 = 0; sp + s0 * SP < S; s0 += CH) {  // split of batch slot q: sp + (s0 + q) * SP
       float2 ml[CH];
       bf16x8 v[CH][CPT];
 #pragma unroll
       for (int q = 0; q < CH; ++q) {
-        const int sq = min(sp + (s0 + q) * SP, Sr - 1);  // past Sr: repeat split Sr - 1 (weight 0 below)
+        const int sq = min(sp + (s0 + q) * SP, S - 1);  // past S: repeat split S - 1 (weight 0 below)
         ml[q] = part_ml[(size_t)sq * Mp + m];
 #pragma unroll
         for (int u = 0; u < CPT; ++u) v[q][u] = src[sq * stride + u];
       }
       float gm = -INFINITY;
 #pragma unroll
-      for (int q = 0; q < CH; ++q) gm = (sp + (s0 + q) * SP < Sr) ? fmaxf(gm, ml[q].x) : gm;
+      for (int q = 0; q < CH; ++q) gm = (sp + (s0 + q) * SP < S) ? fmaxf(gm, ml[q].x) : gm;
       const float mn = fmaxf(mx, gm);
       if (mn == -INFINITY) continue;  // nothing visible in any split so far
       if (s0 > 0) {
@@ -835,7 +835,7 @@ __global__ __launch_bounds__(COMB_THREADS) void combine_up_kernel(const uint16_t
       for (int q = 0; q < CH; ++q) {
         // weight 0 for a split past S or one in which row m saw nothing
         const float wq =
-            (sp + (s0 + q) * SP < Sr && ml[q].x != -INFINITY) ? fast_exp2(ml[q].x - mn) * ml[q].y : 0.f;
+            (sp + (s0 + q) * SP < S && ml[q].x != -INFINITY) ? fast_exp2(ml[q].x - mn) * ml[q].y : 0.f;
         den += wq;
 #pragma unroll
         for (int u = 0; u < CPT; ++u)
@@ -984,7 +984,7 @@ __global__ __launch_bounds__(NTHREADS) void mfma_probe_kernel(int iters, float* 
 struct Plan {
   int H, nodes;           // heads, nodes of all requests
   int split_blocks, comb_blocks;
-  int comb_rt;            // tree nodes per combine workgroup (4; 2 or 1 for a single request with few heads)
+  int comb_rt;            // tree nodes per combine workgroup (4; 2 or 1 for a small single request, 16 for a batch)
   BatchArgs<MAX_BATCH> ba;
   size_t off_qcat, off_po, off_pml, total;
 };
