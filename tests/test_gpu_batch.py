@@ -94,6 +94,14 @@ def test_kimi_two_requests():
     check_batch(si.batch_inputs(si.KIMI_DIMS, [5553, 100], [15, 9], seed=4), heads=[0, 33, 63])
 
 
+def test_kimi_uneven_requests():
+    """Requests of 1, 15, 64 and 9 nodes over prefixes of 0, 4000, 13 and 700 tokens: under the batch plan the
+    groups have 64 workgroups (one per query tile of the 64-node request), the runs are 20 KV tiles, the last
+    run touches three requests, most members skip the smaller requests, and the combine takes 16-node blocks."""
+    check_batch(si.batch_inputs(si.KIMI_DIMS, [0, 4000, 13, 700], [1, 15, 64, 9], seed=8, dist="unit"),
+                heads=[0, 31, 63])
+
+
 def test_kimi_ten_streams():
     """Ten concurrent 15-node trees over 1000-token prefixes (the pages' C = 10 serving level)."""
     check_batch(si.batch_inputs(si.KIMI_DIMS, [1000] * 10, [15] * 10, seed=5), heads=[0, 63])
