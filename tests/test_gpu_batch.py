@@ -107,6 +107,23 @@ def test_kimi_ten_streams():
     check_batch(si.batch_inputs(si.KIMI_DIMS, [1000] * 10, [15] * 10, seed=5), heads=[0, 63])
 
 
+def test_kimi_ten_requests_timed_workload():
+    """The ten-request workload the benchmark times: ten 15-node trees over 5553-token prefixes.  The batch plan
+    takes 17 groups of 15 workgroups and runs of 52 of the 870 KV tiles, so every request is split over 2 or 3
+    runs, and the combine takes 16-node blocks."""
+    check_batch(si.batch_inputs(si.KIMI_DIMS, [5553] * 10, [15] * 10, seed=10, dist="unit"), heads=[0, 37, 63])
+
+
+def test_kimi_sixteen_requests():
+    """The largest batch (16 requests) at full Kimi dims: ten 15-node trees over 5553-token prefixes, as in the
+    timed ten-request workload, plus six more requests of 64, 1, 33, 9, 15 and 2 nodes over 0 to 3333 tokens.
+    Under the batch plan the groups have 64 workgroups (one per query tile of the 64-node request), four runs
+    of 239 of the 955 KV tiles, each touching 3 to 8 requests; members past a request's query tiles skip it."""
+    Ls = [5553] * 10 + [0, 1, 64, 3333, 1663, 13]
+    Ts = [15] * 10 + [64, 1, 33, 9, 15, 2]
+    check_batch(si.batch_inputs(si.KIMI_DIMS, Ls, Ts, seed=9, dist="unit"), heads=[0, 63])
+
+
 def test_batch_of_one_is_the_single_call():
     reqs = si.batch_inputs(si.KIMI_DIMS, [777], [15], seed=6)
     got, glse, dev, mask = run_batch(reqs)
