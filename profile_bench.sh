@@ -5,7 +5,7 @@
 #   2. FETCH_SIZE, then WRITE_SIZE, then the MFMA instruction and busy-cycle counts, each in a counter run of
 #      its own, on a shorter bench run;
 #   3. the same two counters on a plain 256 MiB device copy, the calibration of counter units to bytes.
-# Raw output goes to gpurun_out/profile_<workload>/; the markdown summaries to .../summaries/.
+# Raw output goes to $O (profile_<workload>/ under the output folder); the markdown summaries to $O/summaries/.
 # Run from anywhere on the GPU machine: bash profile_bench.sh [workload]
 R=$(cd "$(dirname "$0")" && pwd)
 W=${1:-kimi5553}
