@@ -10,6 +10,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import synth_inputs as si
 
 pytestmark = pytest.mark.gpu
@@ -116,3 +117,53 @@ def test_batched_verify_graph_replays():
     refs = [(n_, b, b.clone()) for n_, b in (("out", out), ("lse", lse))]
     g = _capture(call)
     _replay_and_check(g, [out, lse, ws], refs, clobber=[0, 3, 255], other_call=other_call)
+
+
+def test_verify_step_graph_replays():
+    """The whole verify step in one graph, device arrays only: best-first tree builder -> verify with its own
+    ancestor mask -> greedy acceptance, with the built tree feeding the other two calls on the device."""
+    T = 15
+    logp, tok = si.draft_topk(7, 16, 4)
+    rng = np.random.default_rng(9)
+    inp = si.kimi(L=300, T=T, seed=5, dist="unit")
+    d = si.to_device(inp)
+    dims = kdv.make_dims(**inp.dims())
+    lp, tk = torch.from_numpy(logp).cuda(), torch.from_numpy(tok).cuda()
+    root = torch.tensor([42], dtype=torch.int32, device="cuda")
+    # target predictions that mostly follow a drafted child (tree from the oracle's builder), so that acceptance
+    # walks several levels
+    b_parent, b_tokens, _ = oracle.build_draft_tree(logp, tok, T, 42)
+    pr = rng.integers(0, 1 << 16, size=T).astype(np.int32)
+    for p in range(T):
+        kids = [c for c in range(T) if b_parent[c] == p]
+        if kids and rng.random() < 0.9:
+            pr[p] = b_tokens[kids[int(rng.integers(0, len(kids)))]]
+    pred = torch.from_numpy(pr).cuda()
+    res = {}
+
+    def call():
+        parent, tokens, n_nodes = kdv.build_draft_tree(lp, tk, T, root)
+        out, _, mask, mstatus = kdv.verify_mla_attn_tree(dims, d["q_nope"], d["q_rope"], d["w_uk"], d["w_uv"],
+                                                         d["c_kv"], d["k_pe"], d["page_table"], inp.L, parent)
+        path, n_path, nxt, astatus = kdv.tree_accept(parent, tokens, pred)
+        res.update(parent=parent, tokens=tokens, n_nodes=n_nodes, out=out, mask=mask, mstatus=mstatus, path=path,
+                   n_path=n_path, next_token=nxt, astatus=astatus)
+
+    call()
+    torch.cuda.synchronize()
+    ref = {k: v.clone() for k, v in res.items()}
+    assert int(ref["n_nodes"].item()) == T and int(ref["mstatus"].item()) == 0 and int(ref["astatus"].item()) == 0
+    g = _capture(call)
+    n = int(ref["n_path"].item())
+    for rep in range(REPLAYS):
+        for v in res.values():
+            v.fill_([0, 255, 7][rep % 3])
+        kdv.build_tree_mask(d["parent"])  # other eager work of the library between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k, v in res.items():
+            if k == "path":  # entries past n_path are not part of the result
+                assert torch.equal(v[:n], ref[k][:n]), f"replay {rep}: path differs from the eager call"
+            else:
+                assert torch.equal(v, ref[k]), f"replay {rep}: {k} differs from the eager call"
