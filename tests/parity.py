@@ -6,6 +6,11 @@ relative to max(1, max|ref|), so for outputs of magnitude <= 1 it is exactly an
 absolute 2e-2; a second term requires max|diff| <= 1% of max|ref| so that an
 all-zero answer cannot pass when the outputs are small.  The mask is compared
 bit for bit elsewhere.
+
+The lse bound is the exact first-order effect of the one rounding the device
+applies to a score operand that is not already a bf16 input: the absorbed query
+q_lat = W_UK^T q_nope is an fp32 MFMA result rounded to bf16 before the score
+product.  Everything else on the lse path is fp32 (LSE_SLACK).
 """
 from __future__ import annotations
 
@@ -13,8 +18,8 @@ import numpy as np
 
 ABS_TOL = 2e-2
 REL_TOL = 1e-2
-BF16_U = 2.0 ** -8          # unit roundoff of bfloat16 (8 significant bits)
-LSE_SLACK = 1e-3            # fp32 accumulation, exp2/log2 and split-merge rounding
+LSE_SLACK = 1e-3            # fp32 score accumulation, exp2/log2 and the split merge
+FP32_U = 2.0 ** -24         # unit roundoff of float32
 
 
 def out_errors(got, ref) -> dict:
@@ -35,21 +40,47 @@ def out_passes(got, ref) -> tuple[bool, dict]:
     return ok, e
 
 
+def bf16_round_f64(x: np.ndarray) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Round float64 values to bfloat16 (8 significant bits, nearest even) without an intermediate float32.
+
+    Returns (rounded, ulp, distance to the nearest rounding boundary), all float64.  The boundary is the
+    midpoint between the two bfloat16 neighbours that bracket x."""
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)                       # x = m 2^e, 0.5 <= |m| < 1: m * 256 has 8 integer bits
+    s = m * 256.0
+    ulp = np.ldexp(1.0, e - 8)
+    r = np.rint(s)                           # ties to even
+    mid = np.floor(s) + 0.5
+    return r * ulp, ulp, np.abs(s - mid) * ulp
+
+
 def lse_tolerance(inp, heads=None) -> np.ndarray:
     """Per (node, head) bound on |lse_gpu - lse_ref| [T][H].
 
-    The device rounds the absorbed query q_lat = W_UK^T q_nope to bfloat16 before the score MFMA (the other
-    score operands are exact bf16 inputs).  That moves each score s_n by at most
-    u * scale * sum_i |q_lat_i| |c_n,i| with u = 2^-8, and lse = ln sum exp(s) is 1-Lipschitz in the
-    max-norm of s, so the same quantity, maximised over n, bounds the lse error; LSE_SLACK covers the fp32
-    parts.  Rows over all cached positions bound the visible ones."""
+    The device computes q_lat = W_UK[h]^T q_nope[t,h] with fp32 accumulation and rounds it to bfloat16
+    before the score product; the other score operands (c_kv, q_rope, k_pe) are bf16 inputs already.  With
+    d = bf16(q_lat) - q_lat, every score s_n moves by scale * d . c_n, and to first order lse moves by the
+    softmax-weighted mean of those shifts, which is at most max_n |scale * d . c_n|: the first term below,
+    computed exactly from the fp64 q_lat.  The device's q_lat is its fp32 sum, which differs from the fp64
+    one by at most Dn * u32 * sum_k |q_k W_ki|; where that could carry q_lat_i across a rounding boundary the
+    device may round it to the other neighbour, one ulp away, and the second term adds that ulp for those
+    elements.  LSE_SLACK covers the fp32 score accumulation, exp2/log2 and the split merge.  Rows over all
+    cached positions bound the visible ones."""
     T, H = inp.T, inp.H
     heads = range(H) if heads is None else heads
-    C = np.abs(inp.f32("c_kv")[inp.page_table].astype(np.float64))
+    C = inp.f32("c_kv")[inp.page_table].astype(np.float64)
+    absC = np.abs(C)
     tol = np.full((T, H), np.nan)
     for h in heads:
-        qlat = np.abs(inp.f32("q_nope")[:, h].astype(np.float64) @ inp.f32("w_uk")[h].astype(np.float64))
-        tol[:, h] = BF16_U * inp.sm_scale * (qlat @ C.T).max(axis=1) + LSE_SLACK
+        qn = inp.f32("q_nope")[:, h].astype(np.float64)
+        W = inp.f32("w_uk")[h].astype(np.float64)
+        qlat = qn @ W
+        qb, ulp, to_boundary = bf16_round_f64(qlat)
+        first = np.abs((qb - qlat) @ C.T).max(axis=1)
+        acc_err = inp.Dn * FP32_U * (np.abs(qn) @ np.abs(W))
+        flip = np.where(to_boundary <= acc_err, ulp, 0.0)
+        second = (flip @ absC.T).max(axis=1) if flip.any() else np.zeros(T)
+        tol[:, h] = inp.sm_scale * (first + second) + LSE_SLACK
     return tol
 
 
