@@ -44,7 +44,9 @@ PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, vendor figure
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, vendor figure
 COLD_BYTES = 576 << 20
 KERNEL_SOURCES = ("speculative_decoding_tree_parent_amd/csrc/verify.hip",
-                  "speculative_decoding_tree_parent_amd/csrc/common.h")
+                  "speculative_decoding_tree_parent_amd/csrc/common.h",
+                  "speculative_decoding_tree_parent_amd/csrc/tree_mask.h",
+                  "speculative_decoding_tree_parent_amd/csrc/tree.hip")
 KERNELS = ("tree_mask_kernel", "q_absorb_kernel", "splitkv_kernel", "combine_up_kernel", "tree_accept_kernel",
            "draft_tree_kernel", "merge_states_kernel")
 

@@ -61,12 +61,14 @@ typedef enum kdv_status {
   KDV_ERR_TREE = -3,      /* parent array is not a rooted tree in topological order (device side) */
   KDV_ERR_ALIGN = -4,     /* a bf16/fp32 array or the workspace is not 16-byte aligned            */
   KDV_ERR_WORKSPACE = -5, /* workspace smaller than kdv_verify_workspace_bytes()                  */
-  KDV_ERR_HIP = -6        /* a HIP launch or query failed                                         */
+  KDV_ERR_HIP = -6,       /* a HIP launch or query failed                                         */
+  KDV_ERR_PAGE = -7       /* a page-table entry outside [0, pool_slots) (device side, KDV_DEBUG)  */
 } kdv_status;
 
 #define KDV_MAX_TREE_NODES 64
 #define KDV_MAX_BATCH 16           /* requests per kdv_verify_mla_attn_batch call */
 #define KDV_MAX_DRAFT_ENTRIES 4096 /* block x K entries of the drafter's top-K table */
+#define KDV_WS_HEADER 256          /* bytes at the start of every verify workspace: the debug status below */
 
 /* Best-first construction of the draft tree on the device ("The Architecture of Diagnosis...", section
  * "Phase 1: Custom CUDA Kernels", item 1).
@@ -146,7 +148,12 @@ size_t kdv_verify_workspace_bytes(const kdv_mla_dims* d, int32_t T, int32_t L);
  *   c_kv       : device bf16 pool [P][R] of latent rows.
  *   k_pe       : device bf16 pool [P][Dr] of rotary key rows (post-RoPE).
  *   pool_slots : P.  Every page_table entry must be in [0, P); this is the caller's contract and is not
- *                checked on the hot path.
+ *                checked on the hot path.  With KDV_DEBUG set (to anything but "0") in the environment when
+ *                the call is made, a one-workgroup kernel first checks every entry of the call's page table
+ *                (pages are one token each: "The Architecture of Diagnosis...", section "The Discrepancy That
+ *                Revealed the Truth") and writes KDV_OK or KDV_ERR_PAGE to the int32 at offset 0 of the
+ *                workspace; on KDV_ERR_PAGE the verify kernels gather nothing and `out` (and `lse`, if given)
+ *                are filled with NaN.  Also for the batched and prefix-only calls (their whole page table).
  *   page_table : device int32 [L+T]; logical position n -> pool slot.  Positions 0..L-1 are the prefix;
  *                position L+i holds tree node i's own latent row (already appended by the caller).
  *   L, T       : prefix length (>= 0) and tree size (1..64).
@@ -155,8 +162,8 @@ size_t kdv_verify_workspace_bytes(const kdv_mla_dims* d, int32_t T, int32_t L);
  *   lse        : device fp32 [T][H], nullable; natural-log sum of exp of the scaled visible scores,
  *                for merging with attention computed elsewhere.
  *   workspace  : device scratch of workspace_bytes >= kdv_verify_workspace_bytes(d, T, L); 16-byte
- *                aligned; its contents are undefined after the call.  Calls that share a workspace
- *                must be ordered on one stream.
+ *                aligned; its contents are undefined after the call (except the KDV_DEBUG status word
+ *                above).  Calls that share a workspace must be ordered on one stream.
  * Returns KDV_OK or a negative kdv_status (nothing enqueued on error). */
 int kdv_verify_mla_attn(const kdv_mla_dims* d, const uint16_t* q_nope, const uint16_t* q_rope,
                         const uint16_t* w_uk, const uint16_t* w_uv, const uint16_t* c_kv, const uint16_t* k_pe,
@@ -253,7 +260,7 @@ int kdv_merge_attn_states(const uint16_t* out_a, const float* lse_a, const uint1
  * (diagnostic; 0 if unsupported). */
 int32_t kdv_verify_num_splits(const kdv_mla_dims* d, int32_t T, int32_t L);
 
-/* Diagnostic, for measurement: launches `blocks` workgroups of 256 threads in which every wave issues `iters`
+/* DIAGNOSTIC ONLY, not part of the attention path: a measurement aid for the benchmark.  Launches `blocks` workgroups of 256 threads in which every wave issues `iters`
  * rounds of four independent 32x32x16 bf16 MFMA chains (4 * iters * 32768 flop per wave), the issue-rate
  * ceiling the verify kernels are compared with.  sink: device float [blocks * 256], written (zeros).  Time
  * it with events on `stream`.  Returns KDV_OK, KDV_ERR_NULL, KDV_ERR_SHAPE (iters < 1, blocks outside

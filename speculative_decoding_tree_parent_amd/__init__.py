@@ -24,6 +24,8 @@ KDV_ERR_TREE = -3
 KDV_ERR_ALIGN = -4
 KDV_ERR_WORKSPACE = -5
 KDV_ERR_HIP = -6
+KDV_ERR_PAGE = -7
+KDV_WS_HEADER = 256
 KDV_MAX_TREE_NODES = 64
 KDV_MAX_DRAFT_ENTRIES = 4096
 KDV_MAX_BATCH = 16
@@ -214,6 +216,19 @@ def _ptr(t, dtype, what: str) -> int:
     return t.data_ptr()
 
 
+def _bf16_ptr(t, what: str) -> int:
+    """Device address of a bf16 tensor given as torch.bfloat16 or as int16 bit patterns."""
+    import torch
+    return _ptr(t, torch.bfloat16 if t.dtype == torch.bfloat16 else torch.int16, what)
+
+
+def debug_status(workspace) -> int:
+    """The page-table status a call made with KDV_DEBUG set wrote into its workspace (KDV_OK or KDV_ERR_PAGE).
+    Reads the device (synchronising with it)."""
+    import torch
+    return int(workspace[:4].view(torch.int32).item())
+
+
 def build_tree_mask(parent, mask=None, status=None, stream=None):
     """parent: int32 [T] device tensor -> (mask uint32-as-int32 [T][W], status int32 [1])."""
     import torch
@@ -274,18 +289,16 @@ def verify_workspace_bytes(dims: KdvMlaDims, T: int, L: int) -> int:
 
 
 def verify_mla_attn(dims: KdvMlaDims, q_nope, q_rope, w_uk, w_uv, c_kv, k_pe, page_table, L: int, mask, out=None,
-                    lse=None, workspace=None, stream=None):
-    """All tensors on the device; bf16 tensors may be torch.bfloat16 or int16 bit patterns.
+                    lse=None, workspace=None, stream=None, pool_slots=None):
+    """All tensors on the device; bf16 tensors may be torch.bfloat16 or int16 bit patterns.  pool_slots defaults
+    to the pool's row count.
 
     Returns (out [T][H][Dv] bf16, lse [T][H] fp32 or None)."""
     import torch
     T = q_nope.shape[0]
     H = dims.num_heads
 
-    def bf(t, what):
-        if t.dtype == torch.bfloat16:
-            return _ptr(t, torch.bfloat16, what)
-        return _ptr(t, torch.int16, what)
+    bf = _bf16_ptr
 
     if out is None:
         out = torch.empty((T, H, dims.v_head_dim), dtype=torch.bfloat16, device=q_nope.device)
@@ -293,7 +306,8 @@ def verify_mla_attn(dims: KdvMlaDims, q_nope, q_rope, w_uk, w_uv, c_kv, k_pe, pa
         workspace = torch.empty((verify_workspace_bytes(dims, T, L),), dtype=torch.uint8, device=q_nope.device)
     lse_ptr = None if lse is None else _ptr(lse, torch.float32, "lse")
     rc = kdv_verify_mla_attn(dims, bf(q_nope, "q_nope"), bf(q_rope, "q_rope"), bf(w_uk, "w_uk"), bf(w_uv, "w_uv"),
-                             bf(c_kv, "c_kv"), bf(k_pe, "k_pe"), c_kv.shape[0], _ptr(page_table, torch.int32, "page_table"),
+                             bf(c_kv, "c_kv"), bf(k_pe, "k_pe"), c_kv.shape[0] if pool_slots is None else pool_slots,
+                             _ptr(page_table, torch.int32, "page_table"),
                              L, T, _ptr(mask, torch.int32, "mask"), bf(out, "out"), lse_ptr,
                              _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream_handle(stream))
     if rc != KDV_OK:
@@ -302,7 +316,7 @@ def verify_mla_attn(dims: KdvMlaDims, q_nope, q_rope, w_uk, w_uv, c_kv, k_pe, pa
 
 
 def prefix_mla_attn(dims: KdvMlaDims, q_nope, q_rope, w_uk, w_uv, c_kv, k_pe, page_table, L: int, out=None,
-                    lse=None, workspace=None, stream=None):
+                    lse=None, workspace=None, stream=None, pool_slots=None):
     """Prefix part of a split verify step: every (node, head) row over the L prefix positions only.
 
     page_table: int32 [L] device tensor.  Returns (out [T][H][Dv] bf16, lse [T][H] fp32)."""
@@ -310,10 +324,7 @@ def prefix_mla_attn(dims: KdvMlaDims, q_nope, q_rope, w_uk, w_uv, c_kv, k_pe, pa
     T = q_nope.shape[0]
     H = dims.num_heads
 
-    def bf(t, what):
-        if t.dtype == torch.bfloat16:
-            return _ptr(t, torch.bfloat16, what)
-        return _ptr(t, torch.int16, what)
+    bf = _bf16_ptr
 
     if out is None:
         out = torch.empty((T, H, dims.v_head_dim), dtype=torch.bfloat16, device=q_nope.device)
@@ -325,7 +336,7 @@ def prefix_mla_attn(dims: KdvMlaDims, q_nope, q_rope, w_uk, w_uv, c_kv, k_pe, pa
             raise KdvError(KDV_ERR_SHAPE, "kdv_prefix_workspace_bytes")
         workspace = torch.empty((n,), dtype=torch.uint8, device=q_nope.device)
     rc = kdv_prefix_mla_attn(dims, bf(q_nope, "q_nope"), bf(q_rope, "q_rope"), bf(w_uk, "w_uk"), bf(w_uv, "w_uv"),
-                             bf(c_kv, "c_kv"), bf(k_pe, "k_pe"), c_kv.shape[0],
+                             bf(c_kv, "c_kv"), bf(k_pe, "k_pe"), c_kv.shape[0] if pool_slots is None else pool_slots,
                              _ptr(page_table, torch.int32, "page_table"), L, T, bf(out, "out"),
                              _ptr(lse, torch.float32, "lse"), _ptr(workspace, torch.uint8, "workspace"),
                              workspace.numel(), _stream_handle(stream))
@@ -385,17 +396,14 @@ def verify_batch_workspace_bytes(dims: KdvMlaDims, Ls, Ts) -> int:
 
 
 def verify_mla_attn_batch(dims: KdvMlaDims, q_nope, q_rope, w_uk, w_uv, c_kv, k_pe, page_table, Ls, Ts, mask,
-                          out=None, lse=None, workspace=None, stream=None):
+                          out=None, lse=None, workspace=None, stream=None, pool_slots=None):
     """Batched verify over packed requests (include/kdv.h): q_nope [sum T][H][Dn], page_table [sum (L+T)],
     mask from build_tree_masks.  Returns (out [sum T][H][Dv] bf16, lse [sum T][H] fp32 or None)."""
     import torch
     n_nodes = int(sum(Ts))
     H = dims.num_heads
 
-    def bf(t, what):
-        if t.dtype == torch.bfloat16:
-            return _ptr(t, torch.bfloat16, what)
-        return _ptr(t, torch.int16, what)
+    bf = _bf16_ptr
 
     if out is None:
         out = torch.empty((n_nodes, H, dims.v_head_dim), dtype=torch.bfloat16, device=q_nope.device)
@@ -407,7 +415,8 @@ def verify_mla_attn_batch(dims: KdvMlaDims, q_nope, q_rope, w_uk, w_uv, c_kv, k_
     lse_ptr = None if lse is None else _ptr(lse, torch.float32, "lse")
     rc = kdv_verify_mla_attn_batch(dims, len(Ls), lp, tp, bf(q_nope, "q_nope"), bf(q_rope, "q_rope"),
                                    bf(w_uk, "w_uk"), bf(w_uv, "w_uv"), bf(c_kv, "c_kv"), bf(k_pe, "k_pe"),
-                                   c_kv.shape[0], _ptr(page_table, torch.int32, "page_table"),
+                                   c_kv.shape[0] if pool_slots is None else pool_slots,
+                                   _ptr(page_table, torch.int32, "page_table"),
                                    _ptr(mask, torch.int32, "mask"), bf(out, "out"), lse_ptr,
                                    _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
                                    _stream_handle(stream))
@@ -426,10 +435,7 @@ def verify_mla_attn_tree(dims: KdvMlaDims, q_nope, q_rope, w_uk, w_uv, c_kv, k_p
     H = dims.num_heads
     dev = q_nope.device
 
-    def bf(t, what):
-        if t.dtype == torch.bfloat16:
-            return _ptr(t, torch.bfloat16, what)
-        return _ptr(t, torch.int16, what)
+    bf = _bf16_ptr
 
     if mask is None:
         mask = torch.empty((T, (T + 31) // 32), dtype=torch.int32, device=dev)

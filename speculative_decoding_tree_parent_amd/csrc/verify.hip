@@ -561,8 +561,10 @@ template <int R, int DR, int NB>
 __global__ __launch_bounds__(NTHREADS, 1) void splitkv_kernel(
     const uint16_t* __restrict__ q_cat_all, const uint16_t* __restrict__ c_kv, const uint16_t* __restrict__ k_pe,
     const int32_t* __restrict__ page_table_all, const uint32_t* __restrict__ mask_all, const BatchArgs<NB> ba,
-    float scale_log2, uint16_t* __restrict__ part_o_all, float2* __restrict__ part_ml_all) {
+    float scale_log2, uint16_t* __restrict__ part_o_all, float2* __restrict__ part_ml_all,
+    const int32_t* __restrict__ dbg) {
   using TL = TileLayout<R, DR>;
+  if (dbg != nullptr && *dbg != KDV_OK) return;  // page table failed its check: no gather (uniform)
   __shared__ __attribute__((aligned(1024))) char kvbuf[2 * TL::BYTES];
   __shared__ uint4 pbuf[2][2][2][64];  // [row block][kv half][16-row k-step][lane]: P^T fragments (bf16)
   __shared__ float mxch[2][2][32];     // [row block][kv half][row]: proposed reference
@@ -631,7 +633,9 @@ __global__ __launch_bounds__(NTHREADS) void q_absorb_kernel(const uint16_t* __re
                                                             uint16_t* __restrict__ q_cat, int T, int H,
                                                             const int32_t* __restrict__ parent,
                                                             uint32_t* __restrict__ mask,
-                                                            int32_t* __restrict__ status) {
+                                                            int32_t* __restrict__ status,
+                                                            const int32_t* __restrict__ dbg) {
+  if (dbg != nullptr && *dbg != KDV_OK && blockIdx.x != H) return;  // page table failed its check (uniform)
   if (blockIdx.x == H) {  // a call that builds its own tree mask has one extra column of blocks (uniform exit)
     if (blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x < 64) build_ancestor_mask(parent, T, mask, status, threadIdx.x);
     return;
@@ -737,7 +741,8 @@ __global__ __launch_bounds__(COMB_THREADS) void combine_up_kernel(const uint16_t
                                                               const BatchArgs<NB> ba,
                                                               const uint16_t* __restrict__ w_uv,
                                                               uint16_t* __restrict__ out_all,
-                                                              float* __restrict__ lse_all) {
+                                                              float* __restrict__ lse_all,
+                                                              const int32_t* __restrict__ dbg) {
   constexpr int CPR = R / 8;                 // 16-byte chunks per latent row
   constexpr int KS = R / 16;                 // MFMA k-steps
   constexpr int OP = R + 8;                  // LDS pitch of a merged row (elements)
@@ -780,6 +785,11 @@ __global__ __launch_bounds__(COMB_THREADS) void combine_up_kernel(const uint16_t
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, c = lane & 31;
   constexpr float LN2 = 0.69314718055994530942f;
+  if (dbg != nullptr && *dbg != KDV_OK) {  // page table failed its check: NaN results, nothing gathered (uniform)
+    for (int k = tid; k < nrow * DV; k += COMB_THREADS) out[((size_t)(t0 + k / DV) * H + h) * DV + k % DV] = 0x7FC0;
+    if (lse != nullptr && tid < nrow) lse[(t0 + tid) * H + h] = __builtin_nanf("");
+    return;
+  }
 
   if (wave >= 8 - NFW) {
     // ---- W_UV[h] -> LDS: lane l of instruction i fills position (i*64 + l) of the swizzled rows
@@ -955,6 +965,21 @@ __global__ __launch_bounds__(NTHREADS) void merge_states_kernel(const uint16_t* 
   if (lse != nullptr && idx % cpr == 0) lse[r] = lo;
 }
 
+// ------------------------------------------------------------------------------------------------ page-table check
+// Debug builds of a call (KDV_DEBUG=1 in the environment): one workgroup reads every page-table entry of the call
+// and writes KDV_OK, or KDV_ERR_PAGE if some entry is outside [0, pool_slots), to `status`.  The verify kernels
+// that follow read it first and gather nothing when it is not KDV_OK.
+__global__ __launch_bounds__(1024) void page_check_kernel(const int32_t* __restrict__ page_table, int64_t n,
+                                                          int64_t pool_slots, int32_t* __restrict__ status) {
+  int bad = 0;
+  for (int64_t i = threadIdx.x; i < n; i += 1024) {
+    const int32_t v = page_table[i];
+    bad |= (v < 0) | ((int64_t)v >= pool_slots);
+  }
+  bad = __syncthreads_or(bad);
+  if (threadIdx.x == 0) *status = bad ? KDV_ERR_PAGE : KDV_OK;
+}
+
 // ------------------------------------------------------------------------------------------------ MFMA ceiling probe
 // Diagnostic: every wave runs `iters` rounds of four independent 32x32x16 bf16 MFMA chains (the issue rate of
 // back-to-back independent MFMAs, the ceiling the verify kernels are measured against).  Operands are zero, so
@@ -986,7 +1011,7 @@ struct Plan {
   int split_blocks, comb_blocks;
   int comb_rt;            // tree nodes per combine workgroup (4; 2 or 1 for a small single request, 16 for a batch)
   BatchArgs<MAX_BATCH> ba;
-  size_t off_qcat, off_po, off_pml, total;
+  size_t off_qcat, off_po, off_pml, total;   // workspace regions (after a KDV_WS_HEADER-byte header)
 };
 
 enum ShapeId { SHAPE_NONE = 0, SHAPE_KIMI = 1, SHAPE_TINY = 2 };
@@ -1154,7 +1179,7 @@ static int make_plan(const kdv_mla_dims* d, int C, const int32_t* Ls, const int3
   }
   p->split_blocks = (int)blk_s;
   p->comb_blocks = (int)blk_c;
-  size_t off = 0;
+  size_t off = KDV_WS_HEADER;  // header: the debug page-table status (int32 at offset 0)
   p->off_qcat = off;
   off += align256((size_t)nodes * H * DQ * 2);
   p->off_po = off;
@@ -1182,7 +1207,8 @@ template <int DN, int R, int DR, int DV>
 static void launch_all(const Plan& pl, float sm_scale, const uint16_t* q_nope, const uint16_t* q_rope,
                        const uint16_t* w_uk, const uint16_t* w_uv, const uint16_t* c_kv, const uint16_t* k_pe,
                        const int32_t* page_table, const uint32_t* mask, uint16_t* out, float* lse, char* ws,
-                       hipStream_t st, hipEvent_t const* ev, const int32_t* parent, int32_t* status) {
+                       hipStream_t st, hipEvent_t const* ev, const int32_t* parent, int32_t* status,
+                       const int32_t* dbg) {
   uint16_t* q_cat = reinterpret_cast<uint16_t*>(ws + pl.off_qcat);
   uint16_t* part_o = reinterpret_cast<uint16_t*>(ws + pl.off_po);
   float2* part_ml = reinterpret_cast<float2*>(ws + pl.off_pml);
@@ -1190,7 +1216,7 @@ static void launch_all(const Plan& pl, float sm_scale, const uint16_t* q_nope, c
   // request) an extra block builds the tree mask the split-KV kernel then reads.
   launch(q_absorb_kernel<DN, R, DR>, dim3(pl.H + (parent != nullptr ? 1 : 0), (R + 127) / 128, (pl.nodes + 31) / 32), st,
          ev ? ev + 0 : nullptr, q_nope, q_rope, w_uk, q_cat, pl.nodes, pl.H, parent, const_cast<uint32_t*>(mask),
-         status);
+         status, dbg);
   const float scale_log2 = sm_scale * 1.44269504088896340736f;
   if (pl.ba.n == 1) {
     BatchArgs<1> one;
@@ -1203,21 +1229,27 @@ static void launch_all(const Plan& pl, float sm_scale, const uint16_t* q_nope, c
     one.blk_comb[1] = pl.ba.blk_comb[1];
     one.r[0] = pl.ba.r[0];
     launch(splitkv_kernel<R, DR, 1>, dim3(pl.split_blocks), st, ev ? ev + 2 : nullptr, (const uint16_t*)q_cat, c_kv,
-           k_pe, page_table, mask, one, scale_log2, part_o, part_ml);
+           k_pe, page_table, mask, one, scale_log2, part_o, part_ml, dbg);
     auto comb = pl.comb_rt == 1 ? combine_up_kernel<R, DV, 1, 1>
                 : pl.comb_rt == 2 ? combine_up_kernel<R, DV, 1, 2> : combine_up_kernel<R, DV, 1, 4>;
     launch_n(comb, dim3(pl.comb_blocks), COMB_THREADS, st, ev ? ev + 4 : nullptr, (const uint16_t*)part_o,
-             (const float2*)part_ml, one, w_uv, out, lse);
+             (const float2*)part_ml, one, w_uv, out, lse, dbg);
   } else {
     launch(splitkv_kernel<R, DR, MAX_BATCH>, dim3(pl.split_blocks), st, ev ? ev + 2 : nullptr,
-           (const uint16_t*)q_cat, c_kv, k_pe, page_table, mask, pl.ba, scale_log2, part_o, part_ml);
+           (const uint16_t*)q_cat, c_kv, k_pe, page_table, mask, pl.ba, scale_log2, part_o, part_ml, dbg);
     launch_n(pl.comb_rt == 16 ? combine_up_kernel<R, DV, MAX_BATCH, 16> : combine_up_kernel<R, DV, MAX_BATCH, 4>,
              dim3(pl.comb_blocks), COMB_THREADS, st, ev ? ev + 4 : nullptr,
-             (const uint16_t*)part_o, (const float2*)part_ml, pl.ba, w_uv, out, lse);
+             (const uint16_t*)part_o, (const float2*)part_ml, pl.ba, w_uv, out, lse, dbg);
   }
 }
 
 static bool misaligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
+
+// KDV_DEBUG set to a value other than "0" in the environment at the time of a call turns on the page-table check.
+static bool debug_checks() {
+  const char* v = getenv("KDV_DEBUG");
+  return v != nullptr && v[0] != '\0' && !(v[0] == '0' && v[1] == '\0');
+}
 
 }  // namespace kdv
 
@@ -1273,12 +1305,21 @@ static int verify_impl(const kdv_mla_dims* d, int32_t C, const int32_t* Ls, cons
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   (void)hipGetLastError();
+  // KDV_DEBUG=1: check every page-table entry of the call against pool_slots first (status in the workspace header)
+  const int32_t* dbg = nullptr;
+  if (debug_checks()) {
+    int64_t entries = 0;
+    for (int c = 0; c < C; ++c) entries += (int64_t)Ls[c] + (with_tree ? Ts[c] : 0);
+    int32_t* dst = reinterpret_cast<int32_t*>(ws);
+    hipLaunchKernelGGL(page_check_kernel, dim3(1), dim3(1024), 0, s, page_table, entries, pool_slots, dst);
+    dbg = dst;
+  }
   if (sid == SHAPE_KIMI)
     launch_all<128, 512, 64, 128>(pl, d->sm_scale, q_nope, q_rope, w_uk, w_uv, c_kv, k_pe, page_table, mask, out,
-                                  lse, ws, s, ev, parent, status);
+                                  lse, ws, s, ev, parent, status, dbg);
   else
     launch_all<32, 64, 16, 32>(pl, d->sm_scale, q_nope, q_rope, w_uk, w_uv, c_kv, k_pe, page_table, mask, out, lse,
-                               ws, s, ev, parent, status);
+                               ws, s, ev, parent, status, dbg);
   return hipGetLastError() == hipSuccess ? KDV_OK : KDV_ERR_HIP;
 }
 
@@ -1370,6 +1411,7 @@ extern "C" const char* kdv_status_string(int status) {
     case KDV_ERR_ALIGN: return "an array or the workspace is not suitably aligned (16 B for bf16 data)";
     case KDV_ERR_WORKSPACE: return "workspace smaller than kdv_verify_workspace_bytes()";
     case KDV_ERR_HIP: return "HIP launch or query failed";
+    case KDV_ERR_PAGE: return "a page-table entry is outside [0, pool_slots) (KDV_DEBUG check)";
     default: return "unknown kdv status";
   }
 }

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in range(-6, 1):
+    for code in range(-7, 1):
         s = kdv.kdv_status_string(code)
         assert s and "unknown" not in s
     assert "unknown" in kdv.kdv_status_string(-99)
@@ -95,14 +95,14 @@ def test_workspace_too_small_rejected(dims, fixed_splits):
 
 
 def test_workspace_formula(fixed_splits):
-    # q_cat (bf16) + split partials (bf16 O / l + fp32 (max, sum)), each region 256-byte aligned
+    # header + q_cat (bf16) + split partials (bf16 O / l + fp32 (max, sum)), each region 256-byte aligned
     d = kdv.make_dims(**KIMI)
     T, L = 15, 5553
     S = kdv.kdv_verify_num_splits(d, T, L)
     assert S == 4
     M, Mp = T * 64, ((T * 64 + 63) // 64) * 64
     up = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    expect = up(M * 576 * 2) + up(S * Mp * 512 * 2) + up(S * Mp * 8)
+    expect = kdv.KDV_WS_HEADER + up(M * 576 * 2) + up(S * Mp * 512 * 2) + up(S * Mp * 8)
     assert kdv.kdv_verify_workspace_bytes(d, T, L) == expect
 
 
@@ -242,7 +242,7 @@ def test_batch_workspace_formula(fixed_splits):
         tps = (tiles + want - 1) // want
         S = (tiles + tps - 1) // tps
         rows += S * ((T * 64 + 63) // 64) * 64
-    expect = up(sum(Ts) * 64 * 576 * 2) + up(rows * 512 * 2) + up(rows * 8)
+    expect = kdv.KDV_WS_HEADER + up(sum(Ts) * 64 * 576 * 2) + up(rows * 512 * 2) + up(rows * 8)
     assert kdv.kdv_verify_batch_workspace_bytes(d, 3, lp, tp) == expect
 
 
