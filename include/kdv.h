@@ -69,6 +69,7 @@ typedef enum kdv_status {
 #define KDV_MAX_BATCH 16           /* requests per kdv_verify_mla_attn_batch call */
 #define KDV_MAX_DRAFT_ENTRIES 4096 /* block x K entries of the drafter's top-K table */
 #define KDV_WS_HEADER 256          /* bytes at the start of every verify workspace: the debug status below */
+#define KDV_NOALLOC_SCRATCH_BYTES (32u << 20) /* device array behind kdv_verify_mla_attn_noalloc (32 MiB) */
 
 /* Best-first construction of the draft tree on the device ("The Architecture of Diagnosis...", section
  * "Phase 1: Custom CUDA Kernels", item 1).
@@ -169,6 +170,20 @@ int kdv_verify_mla_attn(const kdv_mla_dims* d, const uint16_t* q_nope, const uin
                         const uint16_t* w_uk, const uint16_t* w_uv, const uint16_t* c_kv, const uint16_t* k_pe,
                         int64_t pool_slots, const int32_t* page_table, int32_t L, int32_t T, const uint32_t* mask,
                         uint16_t* out, float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/* kdv_verify_mla_attn for callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  It takes no workspace: it uses a fixed array of
+ * KDV_NOALLOC_SCRATCH_BYTES that the library holds on each device it runs on (reserved when the library is
+ * loaded there, kept until the process ends), and it calls no hipMalloc, hipFree or allocating routine.
+ * Arguments, results and errors as kdv_verify_mla_attn, plus KDV_ERR_WORKSPACE (nothing enqueued) when the
+ * call needs more than KDV_NOALLOC_SCRATCH_BYTES of workspace (kdv_verify_workspace_bytes(d, T, L) tells; every
+ * shape of the default split plan on a 256-CU device fits, a large KDV_SPLITS override may not).  All calls on
+ * one device share that device's array and it keeps the last call's contents: calls that overlap in time on
+ * one device (different streams, or different host threads) race and must not be issued. */
+int kdv_verify_mla_attn_noalloc(const kdv_mla_dims* d, const uint16_t* q_nope, const uint16_t* q_rope,
+                                const uint16_t* w_uk, const uint16_t* w_uv, const uint16_t* c_kv, const uint16_t* k_pe,
+                                int64_t pool_slots, const int32_t* page_table, int32_t L, int32_t T,
+                                const uint32_t* mask, uint16_t* out, float* lse, void* stream);
 
 /* kdv_verify_mla_attn that builds the tree's ancestor mask itself: the mask of kdv_build_tree_mask(parent, T)
  * is written to `mask` (device uint32 [T][(T+31)/32], written; the caller can pass it to kdv_verify_mla_attn

@@ -26,6 +26,7 @@ KDV_ERR_WORKSPACE = -5
 KDV_ERR_HIP = -6
 KDV_ERR_PAGE = -7
 KDV_WS_HEADER = 256
+KDV_NOALLOC_SCRATCH_BYTES = 32 << 20
 KDV_MAX_TREE_NODES = 64
 KDV_MAX_DRAFT_ENTRIES = 4096
 KDV_MAX_BATCH = 16
@@ -34,7 +35,7 @@ EXPORTED = ("kdv_build_draft_tree", "kdv_build_tree_mask", "kdv_merge_attn_state
             "kdv_prefix_workspace_bytes",
             "kdv_tree_accept", "kdv_verify_batch_workspace_bytes", "kdv_verify_mla_attn_batch",
             "kdv_verify_workspace_bytes", "kdv_verify_mla_attn", "kdv_verify_mla_attn_profiled",
-            "kdv_verify_mla_attn_tree",
+            "kdv_verify_mla_attn_tree", "kdv_verify_mla_attn_noalloc",
             "kdv_verify_num_splits", "kdv_mfma_probe", "kdv_status_string")
 
 
@@ -74,6 +75,8 @@ def _load() -> ctypes.CDLL:
     lib.kdv_verify_mla_attn_tree.argtypes = [dims_p, vp, vp, vp, vp, vp, vp, i64, vp, i32, i32, vp, vp, vp, vp, vp,
                                              vp, sz, vp]
     lib.kdv_verify_mla_attn_tree.restype = ctypes.c_int
+    lib.kdv_verify_mla_attn_noalloc.argtypes = [dims_p, vp, vp, vp, vp, vp, vp, i64, vp, i32, i32, vp, vp, vp, vp]
+    lib.kdv_verify_mla_attn_noalloc.restype = ctypes.c_int
     lib.kdv_verify_mla_attn_batch.argtypes = [dims_p, i32, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, vp,
                                               sz, vp]
     lib.kdv_verify_mla_attn_batch.restype = ctypes.c_int
@@ -142,6 +145,13 @@ def kdv_verify_mla_attn_tree(dims: KdvMlaDims, q_nope: int, q_rope: int, w_uk: i
     return _lib.kdv_verify_mla_attn_tree(ctypes.byref(dims), q_nope, q_rope, w_uk, w_uv, c_kv, k_pe, pool_slots,
                                          page_table, L, T, parent, mask, status, out, lse, workspace,
                                          workspace_bytes, stream)
+
+
+def kdv_verify_mla_attn_noalloc(dims: KdvMlaDims, q_nope: int, q_rope: int, w_uk: int, w_uv: int, c_kv: int,
+                                k_pe: int, pool_slots: int, page_table: int, L: int, T: int, mask: int, out: int,
+                                lse: int | None, stream: int | None) -> int:
+    return _lib.kdv_verify_mla_attn_noalloc(ctypes.byref(dims), q_nope, q_rope, w_uk, w_uv, c_kv, k_pe, pool_slots,
+                                            page_table, L, T, mask, out, lse, stream)
 
 
 def _host_i32(values):

@@ -15,6 +15,7 @@
 //              out[t,h] = W_UV[h] o[t,h]                                   (bf16 MFMA)
 #include <hip/hip_ext.h>
 #include <algorithm>
+#include <mutex>
 #include <math.h>
 #include <stdlib.h>
 
@@ -1330,6 +1331,55 @@ extern "C" int kdv_verify_mla_attn(const kdv_mla_dims* d, const uint16_t* q_nope
                                    size_t workspace_bytes, void* stream) {
   return verify_impl(d, 1, &L, &T, q_nope, q_rope, w_uk, w_uv, c_kv, k_pe, pool_slots, page_table, mask, out, lse,
                      workspace, workspace_bytes, stream, nullptr);
+}
+
+// ------------------------------------------------------------------------------------------------ no-allocation entry
+// The workspace of kdv_verify_mla_attn_noalloc: one array per device, in the library's code object, reserved when
+// the library is loaded on that device and held until the process ends.  Host code never passes the array's name to
+// a kernel (on the host it is only a stand-in for the symbol); it takes each device's address once, with that device
+// current, and uses that.  Nothing in it needs to start at zero: every region a call reads is first written by the
+// same call.  Calls on one device share it, so calls that overlap in time on one device race.
+namespace kdv {
+static __device__ __align__(256) char scratch[KDV_NOALLOC_SCRATCH_BYTES];
+constexpr int MAX_DEVICES = 64;
+static std::mutex scratch_mu;
+static void* scratch_ptr[MAX_DEVICES];
+
+static int scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return KDV_ERR_HIP;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return KDV_ERR_HIP;
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
+  return KDV_OK;
+}
+}  // namespace kdv
+
+extern "C" int kdv_verify_mla_attn_noalloc(const kdv_mla_dims* d, const uint16_t* q_nope, const uint16_t* q_rope,
+                                           const uint16_t* w_uk, const uint16_t* w_uv, const uint16_t* c_kv,
+                                           const uint16_t* k_pe, int64_t pool_slots, const int32_t* page_table,
+                                           int32_t L, int32_t T, const uint32_t* mask, uint16_t* out, float* lse,
+                                           void* stream) {
+  // argument errors and the scratch limit are reported before the device is touched (the plan needs no device
+  // when KDV_SPLITS is set)
+  if (d == nullptr || q_nope == nullptr || q_rope == nullptr || w_uk == nullptr || w_uv == nullptr ||
+      c_kv == nullptr || k_pe == nullptr || page_table == nullptr || mask == nullptr || out == nullptr)
+    return KDV_ERR_NULL;
+  if (kdv::shape_of(d) == kdv::SHAPE_NONE || pool_slots < 1 || T < 1 || T > KDV_MAX_TREE_NODES || L < 0)
+    return KDV_ERR_SHAPE;
+  kdv::Plan pl;
+  const int st = kdv::make_plan(d, 1, &L, &T, &pl);
+  if (st != KDV_OK) return st;
+  if (pl.total > KDV_NOALLOC_SCRATCH_BYTES) return KDV_ERR_WORKSPACE;
+  void* ws = nullptr;
+  const int sst = kdv::scratch_of_current_device(&ws);
+  if (sst != KDV_OK) return sst;
+  return verify_impl(d, 1, &L, &T, q_nope, q_rope, w_uk, w_uv, c_kv, k_pe, pool_slots, page_table, mask, out, lse,
+                     ws, KDV_NOALLOC_SCRATCH_BYTES, stream, nullptr);
 }
 
 extern "C" int kdv_verify_mla_attn_profiled(const kdv_mla_dims* d, const uint16_t* q_nope, const uint16_t* q_rope,
