@@ -1,22 +1,28 @@
 #!/usr/bin/env python3
 """Benchmark of DDTree tree-verify MLA attention on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload kimi5553|long200k|full61|sweep]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload kimi5553|long200k|full61|kimi:L:T] [--no-extra]
 
 A step is one pass of the whole hot path over one batch of synthetic input: the ancestor mask of the draft
-tree (kdv_build_tree_mask) and tree-verify attention for one layer (kdv_verify_mla_attn: q absorption,
-split-KV MFMA pass, split combine fused with the W_UV up-projection); for `full61` a step is one mask and 61 layers.
+tree and tree-verify attention for one layer (kdv_verify_mla_attn: q absorption, split-KV MFMA pass, split
+combine fused with the W_UV up-projection); for `full61` a step is one mask and 61 layers.
+
+The default run measures the headline workload (64 heads, 15 nodes, 5553-token prefix) for the line's `value`,
+then every other configuration of the metric with the same measurement, under `configs`: the context sweep
+(prefix 13 / 1663 / 3333 / 5553 / 16384 x trees of 9 / 15 nodes), the 200000-token prefix over a scattered
+262144-slot pool, and the 61-layer step (8 heads, 32 nodes, 131072 tokens).  `--no-extra` measures one workload.
 
 Timing: W eager warm-up steps, then the K timed steps are captured in one HIP graph (so host launch cost is
 not counted) and replayed once between two device synchronisations, timed with HIP events on the stream the
-kernels run on.  "Cold" rotates the steps over distinct copies of the layer's buffers totalling more than
-512 MiB (twice the 256 MiB Infinity Cache) as a real multi-layer model would; "hot" reuses one copy.
-Each kernel's own time comes from HIP events that the launch itself stamps with the kernel's start and end
-(hipExtLaunchKernelGGL, through kdv_verify_mla_attn_profiled), over eager launches of the same cold steps.
+kernels run on.  "Cold" rotates the steps over distinct copies of the layer's buffers (together more than
+512 MiB, twice the 256 MiB Infinity Cache, as a real multi-layer model would; `buffers` states how much the K
+timed steps touched); "hot" reuses one copy.  Each kernel's own time comes from HIP events that the launch itself
+stamps with the kernel's start and end (hipExtLaunchKernelGGL, through kdv_verify_mla_attn_profiled), over eager
+launches of the same cold steps; those also give the per-layer p10 / p50 / p90.
 Work counts are algorithmic: masked tree entries and padding are not counted.
 
-Profile evidence (bash profile_bench.sh) is summarised by `--summarize-profile DIR`; `roofline.traffic`
-is read from the committed counter summary only while its hash of the kernel source matches the source.
+Profile evidence (bash profile_bench.sh [workload]) is summarised by `--summarize-profile DIR`;
+`roofline.traffic` is read from the committed counter summary only while its hash of the kernel source matches.
 
 Prints ONE JSON line.  Inputs are seeded synthetic data with the shapes of the pages' workloads.
 """
@@ -113,40 +119,240 @@ class Hip:
 
 
 # ------------------------------------------------------------------------------------------------ workloads
-class Layer:
-    """Device buffers of one layer + the raw pointers the C ABI takes."""
-
-    def __init__(self, t, pool_slots):
-        self.t = t
-        self.pool_slots = pool_slots
-
-    def ptrs(self):
-        t = self.t
-        return [t["q_nope"].data_ptr(), t["q_rope"].data_ptr(), t["w_uk"].data_ptr(), t["w_uv"].data_ptr(),
-                t["c_kv"].data_ptr(), t["k_pe"].data_ptr()]
+SWEEP_L = (13, 1663, 3333, 5553, 16384)
+SWEEP_T = (9, 15)
 
 
 def clone_layer(t):
     return {k: v.clone() for k, v in t.items()}
 
 
-def build_workload(name, torch, si):
-    """Returns (description, dims, L, T, parent, page_table tensor, [layers], layers_per_step, numpy inputs)."""
-    if name == "kimi5553":
+def parse_workload(name):
+    """(kind, L, T, seed) for a workload name: kimi5553, long200k, full61, or kimi:L:T (64 heads, contiguous cache,
+    the sweep's seed for that point: 2 * index(L) + index(T) when (L, T) is a sweep point, else 0)."""
+    if name in ("kimi5553", "long200k", "full61"):
+        return name, None, None, None
+    parts = name.split(":")
+    if len(parts) == 3 and parts[0] == "kimi":
+        L, T = int(parts[1]), int(parts[2])
+        seed = 2 * SWEEP_L.index(L) + SWEEP_T.index(T) if (L in SWEEP_L and T in SWEEP_T) else 0
+        return "kimi", L, T, seed
+    raise SystemExit(f"unknown workload {name!r} (kimi5553, long200k, full61, sweep, or kimi:L:T)")
+
+
+def profile_tag(workload):
+    """File-name form of a workload name (profiles/<kernel>_<tag>_*.md)."""
+    return workload.replace(":", "_L", 1).replace(":", "_T", 1)
+
+
+class Setup:
+    """Device buffers of one workload: the layer buffer sets of the cold rotation, the hot set, and the shared
+    page table and tree."""
+
+
+def setup_workload(name, torch, si, dev):
+    kind, Lk, Tk, seed = parse_workload(name)
+    S = Setup()
+    S.name = name
+    if kind == "full61":
+        parent_np, table_np = si.full61_shared()
+        S.H, S.Dn, S.Dr, S.R, S.Dv = 8, 128, 64, 512, 128
+        S.L, S.T, P = 131072, 32, 262144
+        S.scale = 1.0 / math.sqrt(S.Dn + S.Dr)
+        S.desc = ("verify-step attention, 61 layers x 8 heads, 32-node tree (depth <= 16), 131072-token prefix "
+                  "scattered over a 262144-slot pool, per-layer buffers")
+        gen = torch.Generator(device=dev)
+        layers = []
+        for layer in range(61):
+            gen.manual_seed(1000 + layer)
+
+            def rnd(shape, std):
+                x = torch.randn(shape, generator=gen, device=dev, dtype=torch.float32) * std
+                return x.to(torch.bfloat16).view(torch.int16)
+            layers.append(dict(q_nope=rnd((S.T, S.H, S.Dn), S.Dn ** -0.5), q_rope=rnd((S.T, S.H, S.Dr), S.Dr ** -0.5),
+                               w_uk=rnd((S.H, S.Dn, S.R), S.R ** -0.5), w_uv=rnd((S.H, S.Dv, S.R), S.R ** -0.5),
+                               c_kv=rnd((P, S.R), S.R ** -0.5), k_pe=rnd((P, S.Dr), S.Dr ** -0.5)))
+        S.layers_per_step = 61
+        S.cold_sets, S.hot_sets = [layers], [layers[:1] * 61]
+        S.parent_t = torch.from_numpy(parent_np.astype(np.int32)).to(dev)
+        S.table_t = torch.from_numpy(table_np.astype(np.int32)).to(dev)
+        S.pool_slots, S.parent_np, S.inp = P, parent_np, None
+        per_layer = sum(v.numel() * v.element_size() for v in layers[0].values())
+        S.n_cold, S.set_bytes = 1, 61 * per_layer
+        return S
+    if kind == "kimi5553":
         inp = si.kimi(L=5553, T=15, seed=0, dist="literal")
-        desc = ("tree-verify MLA attention (absorbed), 64 heads, 15-node random tree, 5553-token prefix, "
-                "contiguous bf16 latent cache, dims nope/rope/rank/v = 128/64/512/128")
-        return desc, inp, 1
-    if name == "long200k":
+        S.desc = ("tree-verify MLA attention (absorbed), 64 heads, 15-node random tree, 5553-token prefix, "
+                  "contiguous bf16 latent cache, dims nope/rope/rank/v = 128/64/512/128")
+    elif kind == "long200k":
         inp = si.long_fragmented(seed=0, dist="literal")
-        desc = ("tree-verify MLA attention (absorbed), 64 heads, 15-node random tree, 200000-token prefix "
-                "scattered over a 262144-slot page_size=1 pool")
-        return desc, inp, 1
-    if name == "full61":
-        desc = ("verify-step attention, 61 layers x 8 heads, 32-node tree (depth <= 16), 131072-token prefix "
-                "scattered over a 262144-slot pool, per-layer buffers")
-        return desc, None, 61
-    raise SystemExit(f"unknown workload {name}")
+        S.desc = ("tree-verify MLA attention (absorbed), 64 heads, 15-node random tree, 200000-token prefix "
+                  "scattered over a 262144-slot page_size=1 pool")
+    else:
+        inp = si.kimi(L=Lk, T=Tk, seed=seed, dist="literal")
+        S.desc = (f"tree-verify MLA attention (absorbed), 64 heads, {Tk}-node random tree, {Lk}-token prefix, "
+                  f"contiguous bf16 latent cache (seed {seed})")
+    S.inp = inp
+    S.H, S.Dn, S.Dr, S.R, S.Dv, S.L, S.T = inp.H, inp.Dn, inp.Dr, inp.R, inp.Dv, inp.L, inp.T
+    S.parent_np, S.scale, S.pool_slots = inp.parent, inp.sm_scale, inp.pool_slots
+    d0 = si.to_device(inp, dev)
+    S.parent_t, S.table_t = d0.pop("parent"), d0.pop("page_table")
+    S.set_bytes = sum(v.numel() * v.element_size() for v in d0.values())
+    S.n_cold = max(2, math.ceil(COLD_BYTES / S.set_bytes))
+    cold = [d0] + [clone_layer(d0) for _ in range(S.n_cold - 1)]
+    S.cold_sets, S.hot_sets = [[c] for c in cold], [[d0]]
+    S.layers_per_step = 1
+    return S
+
+
+def measure(S, args, torch, kdv, dev, hip, stream, sh, note, K, Wm, full=True):
+    """Times one workload: K steps of the cold rotation and of one hot buffer set, each captured in one HIP graph,
+    and the kernels of each call over eager cold steps (kernel-stamped HIP events).  Returns (result dict, state for
+    the extra rows of the headline)."""
+    H, Dn, Dr, R, Dv, L, T = S.H, S.Dn, S.Dr, S.R, S.Dv, S.L, S.T
+    lps = S.layers_per_step
+    dims = kdv.make_dims(H, Dn, Dr, R, Dv, S.scale)
+    W = (T + 31) // 32
+    mask_t = torch.empty((T, W), dtype=torch.int32, device=dev)
+    status_t = torch.zeros((1,), dtype=torch.int32, device=dev)
+    out_t = torch.empty((T, H, Dv), dtype=torch.bfloat16, device=dev)
+    lse_t = torch.empty((T, H), dtype=torch.float32, device=dev)
+    ws_bytes = kdv.verify_workspace_bytes(dims, T, L)
+    ws_t = torch.zeros((ws_bytes,), dtype=torch.uint8, device=dev)
+    splits = kdv.kdv_verify_num_splits(dims, T, L)
+    wk = work(H, Dn, Dr, R, Dv, L, T, S.parent_np)
+
+    def ptrs(t):
+        return [t["q_nope"].data_ptr(), t["q_rope"].data_ptr(), t["w_uk"].data_ptr(), t["w_uv"].data_ptr(),
+                t["c_kv"].data_ptr(), t["k_pe"].data_ptr()]
+    cold_ptrs = [[ptrs(t) for t in s] for s in S.cold_sets]
+    hot_ptrs = [[ptrs(t) for t in s] for s in S.hot_sets]
+    fx = dict(pt=S.table_t.data_ptr(), mask=mask_t.data_ptr(), out=out_t.data_ptr(), lse=lse_t.data_ptr(),
+              ws=ws_t.data_ptr(), parent=S.parent_t.data_ptr(), status=status_t.data_ptr())
+    ps = S.pool_slots
+
+    def step(set_ptrs):
+        # The first layer's call builds the step's tree mask (one extra block of its first kernel); the other
+        # layers of the step reuse it.
+        for i, lp in enumerate(set_ptrs):
+            if i == 0:
+                rc = kdv.kdv_verify_mla_attn_tree(dims, *lp, ps, fx["pt"], L, T, fx["parent"], fx["mask"],
+                                                  fx["status"], fx["out"], fx["lse"], fx["ws"], ws_bytes, sh)
+            else:
+                rc = kdv.kdv_verify_mla_attn(dims, *lp, ps, fx["pt"], L, T, fx["mask"], fx["out"], fx["lse"],
+                                             fx["ws"], ws_bytes, sh)
+            if rc:
+                raise kdv.KdvError(rc, "kdv_verify_mla_attn")
+
+    def run_steps(sets, n, fn=step):
+        for i in range(n):
+            fn(sets[i % len(sets)])
+
+    def timed(sets, n, fn=step):
+        """Device time (ms) of n steps: graph-captured unless --no-graph."""
+        e0, e1 = hip.event(), hip.event()
+        if args.no_graph:
+            torch.cuda.synchronize()
+            hip.record(e0, sh)
+            run_steps(sets, n, fn)
+            hip.record(e1, sh)
+            return hip.elapsed_ms(e0, e1)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            run_steps(sets, n, fn)
+        g.replay()                       # untimed replay: graph upload, first-touch
+        torch.cuda.synchronize()
+        hip.record(e0, sh)
+        g.replay()
+        hip.record(e1, sh)
+        ms = hip.elapsed_ms(e0, e1)
+        torch.cuda.synchronize()
+        return ms
+
+    per_step = dict(q_absorb=lps, splitkv=lps, combine_up=lps)  # (the mask is built inside the first call)
+    per_step_eager = dict(tree_mask=1, q_absorb=lps, splitkv=lps, combine_up=lps)
+
+    def note_timed(what, counts, n):
+        if args.no_graph:
+            note(f"{S.name}: {what}, eager", counts, n)
+        else:
+            note(f"{S.name}: graph {what}, upload replay", counts, n)
+            note(f"{S.name}: graph {what}, timed replay", counts, n)
+
+    log(f"[bench] {S.name}: warmup {Wm} steps")
+    torch.cuda.synchronize()
+    run_steps(cold_ptrs, Wm)
+    torch.cuda.synchronize()
+    if int(status_t.item()) != 0:
+        raise SystemExit("tree status not OK")
+    note(f"{S.name}: warm-up", per_step, Wm)
+    log(f"[bench] {S.name}: timing {K} steps (cold)")
+    ms_cold = timed(cold_ptrs, K)
+    note_timed("cold", per_step, K)
+    log(f"[bench] {S.name}: timing {K} steps (hot)")
+    ms_hot = timed(hot_ptrs, K)
+    note_timed("hot", per_step, K)
+
+    # per-kernel device time and per-step spread: events stamped by each kernel's own dispatch, eager launches
+    # queued behind a spin kernel so that they run back to back as in the graph
+    log(f"[bench] {S.name}: per-kernel timing")
+    EvArr = ctypes.c_void_p * 6
+    Kp = min(K, max(1, 400 // lps))
+    ev_list = [EvArr(*[hip.event() for _ in range(6)]) for _ in range(Kp * lps)]
+
+    def step_ev(set_ptrs, evs):
+        rc = kdv.kdv_build_tree_mask(fx["parent"], T, fx["mask"], fx["status"], sh)
+        if rc:
+            raise kdv.KdvError(rc, "kdv_build_tree_mask")
+        for lp, ev in zip(set_ptrs, evs):
+            rc = kdv.kdv_verify_mla_attn_profiled(dims, *lp, ps, fx["pt"], L, T, fx["mask"], fx["out"], fx["lse"],
+                                                  fx["ws"], ws_bytes, sh, ctypes.addressof(ev))
+            if rc:
+                raise kdv.KdvError(rc, "kdv_verify_mla_attn_profiled")
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(2.4e9 * 0.05))
+    for i in range(Kp):
+        step_ev(cold_ptrs[i % len(cold_ptrs)], ev_list[i * lps:(i + 1) * lps])
+    torch.cuda.synchronize()
+    note(f"{S.name}: eager cold, kernel events", per_step_eager, Kp)
+    names = ["q_absorb", "splitkv", "combine_up"]
+    samples = {n: [] for n in names}
+    for ev in ev_list:
+        for k, n in enumerate(names):
+            samples[n].append(1e3 * hip.elapsed_ms(ev[2 * k], ev[2 * k + 1]))
+    # a layer's span: first kernel's start to last kernel's end (per layer of every eager step)
+    spans = [1e3 * hip.elapsed_ms(ev[0], ev[5]) for ev in ev_list]
+    kern_us = {n: float(np.mean(v)) for n, v in samples.items()}
+    kern_pct = {n: [round(float(np.percentile(v, 10)), 3), round(float(np.percentile(v, 90)), 3)]
+                for n, v in samples.items()}
+
+    us_cold = 1e3 * ms_cold / (K * lps)
+    us_hot = 1e3 * ms_hot / (K * lps)
+    tf_cold = wk["flops"] / (us_cold * 1e-6) / 1e12
+    tf_hot = wk["flops"] / (us_hot * 1e-6) / 1e12
+    gbs = wk["bytes"] / (us_cold * 1e-6) / 1e9
+    touched = min(K, S.n_cold) * S.set_bytes if lps == 1 else S.set_bytes
+    res = {
+        "workload": S.desc, "heads": H, "tree_nodes": T, "prefix_len": L, "layers_per_step": lps,
+        "kv_splits": splits,
+        "us_per_layer": round(us_cold, 3),
+        "tflops": round(tf_cold, 3), "frac_bf16_peak": round(tf_cold / PEAK_BF16_TFLOPS, 4),
+        "hbm_gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+        "us_per_layer_eager_p10_p50_p90": [round(float(np.percentile(spans, q)), 3) for q in (10, 50, 90)],
+        "hot": {"us_per_layer": round(us_hot, 3), "tflops": round(tf_hot, 3),
+                "frac_bf16_peak": round(tf_hot / PEAK_BF16_TFLOPS, 4)},
+        "kernels_us": {k: round(v, 3) for k, v in kern_us.items()},
+        "kernels_us_p10_p90": kern_pct,
+        "work_per_layer": {"gflop": round(wk["flops"] / 1e9, 4), "mbytes": round(wk["bytes"] / 1e6, 3)},
+        "buffers": (f"cold: {S.n_cold} distinct layer buffer sets of {S.set_bytes / 2**20:.1f} MiB in rotation, "
+                    f"{touched / 2**20:.0f} MiB touched by the {K} timed steps; hot: one set" if lps == 1 else
+                    f"cold: 61 distinct layers ({S.set_bytes / 2**30:.2f} GiB) per step; hot: layer 0 61 times"),
+        "timing": ("one HIP graph of K steps" if not args.no_graph else "eager") +
+                  "; eager p10/p50/p90: first kernel's start to last kernel's end of each layer, kernel-stamped events",
+    }
+    state = dict(dims=dims, fx=fx, ws_bytes=ws_bytes, cold_ptrs=cold_ptrs, out_t=out_t, lse_t=lse_t, wk=wk,
+                 kern_us=kern_us, timed=timed, step=step, note_timed=note_timed, run_steps=run_steps)
+    return res, state
 
 
 def main():
@@ -154,7 +360,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="kimi5553", choices=["kimi5553", "long200k", "full61"])
+    ap.add_argument("--workload", default="kimi5553",
+                    help="kimi5553 (default, with the other configurations as extra keys), long200k, full61, or "
+                         "kimi:L:T (64 heads, L-token contiguous prefix, T-node tree)")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="headline workload only: no context sweep, 200k and 61-layer rows, no batched row")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of one HIP graph")
@@ -163,6 +373,7 @@ def main():
     ap.add_argument("--summarize-profile", metavar="DIR",
                     help="print the markdown summaries of a profile_bench.sh run and exit (no GPU needed)")
     args = ap.parse_args()
+    parse_workload(args.workload)
     if args.summarize_profile:
         summarize_profile(args.summarize_profile, args.workload)
         return
@@ -194,127 +405,7 @@ def main():
 
 
 def run(args, torch, si, kdv, dev, hip, stream, sh):
-
-    desc, inp, layers_per_step = build_workload(args.workload, torch, si)
-    log(f"[bench] workload {args.workload}: building inputs")
-    if args.workload == "full61":
-        parent_np, table_np = si.full61_shared()
-        H, Dn, Dr, R, Dv = 8, 128, 64, 512, 128
-        L, T, P = 131072, 32, 262144
-        scale = 1.0 / math.sqrt(Dn + Dr)
-        gen = torch.Generator(device=dev)
-        layers = []
-        for layer in range(61):
-            gen.manual_seed(1000 + layer)
-
-            def rnd(shape, std):
-                x = torch.randn(shape, generator=gen, device=dev, dtype=torch.float32) * std
-                return x.to(torch.bfloat16).view(torch.int16)
-            layers.append(dict(q_nope=rnd((T, H, Dn), Dn ** -0.5), q_rope=rnd((T, H, Dr), Dr ** -0.5),
-                               w_uk=rnd((H, Dn, R), R ** -0.5), w_uv=rnd((H, Dv, R), R ** -0.5),
-                               c_kv=rnd((P, R), R ** -0.5), k_pe=rnd((P, Dr), Dr ** -0.5)))
-        hot_layers = layers[:1] * 61
-        cold_sets = [layers]
-        hot_sets = [hot_layers]
-        parent_t = torch.from_numpy(parent_np.astype(np.int32)).to(dev)
-        table_t = torch.from_numpy(table_np.astype(np.int32)).to(dev)
-        pool_slots = P
-    else:
-        H, Dn, Dr, R, Dv, L, T = inp.H, inp.Dn, inp.Dr, inp.R, inp.Dv, inp.L, inp.T
-        parent_np = inp.parent
-        scale = inp.sm_scale
-        d0 = si.to_device(inp, dev)
-        parent_t, table_t = d0.pop("parent"), d0.pop("page_table")
-        per_set = sum(v.numel() * v.element_size() for v in d0.values())
-        n_cold = max(2, math.ceil(COLD_BYTES / per_set))
-        cold = [d0] + [clone_layer(d0) for _ in range(n_cold - 1)]
-        cold_sets = [[c] for c in cold]
-        hot_sets = [[d0]]
-        pool_slots = inp.pool_slots
-        log(f"[bench] cold rotation: {n_cold} buffer sets x {per_set / 2**20:.1f} MiB")
-
-    dims = kdv.make_dims(H, Dn, Dr, R, Dv, scale)
-    W = (T + 31) // 32
-    mask_t = torch.empty((T, W), dtype=torch.int32, device=dev)
-    status_t = torch.zeros((1,), dtype=torch.int32, device=dev)
-    out_t = torch.empty((T, H, Dv), dtype=torch.bfloat16, device=dev)
-    lse_t = torch.empty((T, H), dtype=torch.float32, device=dev)
-    ws_bytes = kdv.verify_workspace_bytes(dims, T, L)
-    ws_t = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
-    splits = kdv.kdv_verify_num_splits(dims, T, L)
-    wk = work(H, Dn, Dr, R, Dv, L, T, parent_np)
-
-    cold_ptrs = [[(Layer(t, pool_slots).ptrs()) for t in s] for s in cold_sets]
-    hot_ptrs = [[(Layer(t, pool_slots).ptrs()) for t in s] for s in hot_sets]
-    fixed = dict(pt=table_t.data_ptr(), mask=mask_t.data_ptr(), out=out_t.data_ptr(), lse=lse_t.data_ptr(),
-                 ws=ws_t.data_ptr(), parent=parent_t.data_ptr(), status=status_t.data_ptr())
-
-    def step(set_ptrs):
-        # The first layer's call builds the step's tree mask (one extra block of its first kernel); the other
-        # layers of the step reuse it.
-        for i, lp in enumerate(set_ptrs):
-            if i == 0:
-                rc = kdv.kdv_verify_mla_attn_tree(dims, *lp, pool_slots, fixed["pt"], L, T, fixed["parent"],
-                                                  fixed["mask"], fixed["status"], fixed["out"], fixed["lse"],
-                                                  fixed["ws"], ws_bytes, sh)
-            else:
-                rc = kdv.kdv_verify_mla_attn(dims, *lp, pool_slots, fixed["pt"], L, T, fixed["mask"], fixed["out"],
-                                             fixed["lse"], fixed["ws"], ws_bytes, sh)
-            if rc:
-                raise kdv.KdvError(rc, "kdv_verify_mla_attn")
-
-    # The prefix/tail split of the same step: per layer, a prefix-only call over the L prefix rows, the tree
-    # call over the T tail rows (L = 0) and the LSE merge of the two (one stream, so they share a workspace).
-    split_bufs = [torch.empty_like(out_t), torch.empty_like(lse_t), torch.empty_like(out_t), torch.empty_like(lse_t)]
-    split_ptr = [t.data_ptr() for t in split_bufs]
-
-    def split_step(set_ptrs):
-        rc = kdv.kdv_build_tree_mask(fixed["parent"], T, fixed["mask"], fixed["status"], sh)
-        if rc:
-            raise kdv.KdvError(rc, "kdv_build_tree_mask")
-        for lp in set_ptrs:
-            rc = kdv.kdv_prefix_mla_attn(dims, *lp, pool_slots, fixed["pt"], L, T, split_ptr[0], split_ptr[1],
-                                         fixed["ws"], ws_bytes, sh)
-            if rc:
-                raise kdv.KdvError(rc, "kdv_prefix_mla_attn")
-            rc = kdv.kdv_verify_mla_attn(dims, *lp, pool_slots, fixed["pt"] + 4 * L, 0, T, fixed["mask"],
-                                         split_ptr[2], split_ptr[3], fixed["ws"], ws_bytes, sh)
-            if rc:
-                raise kdv.KdvError(rc, "kdv_verify_mla_attn")
-            rc = kdv.kdv_merge_attn_states(split_ptr[0], split_ptr[1], split_ptr[2], split_ptr[3], T * H, Dv,
-                                           fixed["out"], fixed["lse"], sh)
-            if rc:
-                raise kdv.KdvError(rc, "kdv_merge_attn_states")
-
-    def run_steps(sets, K, fn=step):
-        for i in range(K):
-            fn(sets[i % len(sets)])
-
-    def timed(sets, K, fn=step):
-        """Device time (ms) of K steps: graph-captured unless --no-graph."""
-        e0, e1 = hip.event(), hip.event()
-        if args.no_graph:
-            torch.cuda.synchronize()
-            hip.record(e0, sh)
-            run_steps(sets, K, fn)
-            hip.record(e1, sh)
-            return hip.elapsed_ms(e0, e1)
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
-            run_steps(sets, K, fn)
-        g.replay()                       # untimed replay: graph upload, first-touch
-        torch.cuda.synchronize()
-        hip.record(e0, sh)
-        g.replay()
-        hip.record(e1, sh)
-        ms = hip.elapsed_ms(e0, e1)
-        torch.cuda.synchronize()
-        return ms
-
-    # Dispatch ledger: (phase, {kernel: dispatches}) in launch order, so that the profile summaries can split a
-    # trace of this run by phase.
     ledger = []
-    lps = layers_per_step
 
     def note(phase, counts, n=1):
         names = {p for p, _ in ledger}
@@ -322,77 +413,47 @@ def run(args, torch, si, kdv, dev, hip, stream, sh):
         while name in names:  # phase names are unique keys
             name, i = f"{phase} #{i}", i + 1
         ledger.append([name, {f"{k}_kernel": v * n for k, v in counts.items() if v}])
-    per_step = dict(q_absorb=lps, splitkv=lps, combine_up=lps)  # (the mask is built inside the first call)
-    per_step_eager = dict(tree_mask=1, q_absorb=lps, splitkv=lps, combine_up=lps)
-    per_split_step = dict(tree_mask=1, q_absorb=2 * lps, splitkv=2 * lps, combine_up=2 * lps, merge_states=lps)
-
-    def note_timed(what, counts, K):
-        if args.no_graph:
-            note(f"{what}, eager", counts, K)
-        else:
-            note(f"graph {what}, upload replay", counts, K)
-            note(f"graph {what}, timed replay", counts, K)
 
     K, Wm = args.steps, args.warmup
-    log(f"[bench] warmup {Wm} steps")
-    torch.cuda.synchronize()
-    run_steps(cold_ptrs, Wm)
-    torch.cuda.synchronize()
-    if int(status_t.item()) != 0:
-        raise SystemExit("tree status not OK")
-    note("warm-up", per_step, Wm)
-    log(f"[bench] timing {K} steps (cold)")
-    ms_cold = timed(cold_ptrs, K)
-    note_timed("cold", per_step, K)
-    log(f"[bench] timing {K} steps (hot)")
-    ms_hot = timed(hot_ptrs, K)
-    note_timed("hot", per_step, K)
+    log(f"[bench] workload {args.workload}: building inputs")
+    S = setup_workload(args.workload, torch, si, dev)
+    res, st = measure(S, args, torch, kdv, dev, hip, stream, sh, note, K, Wm)
+    H, Dn, Dr, R, Dv, L, T = S.H, S.Dn, S.Dr, S.R, S.Dv, S.L, S.T
+    lps = S.layers_per_step
+    dims, fx, ws_bytes, wk, kern_us = st["dims"], st["fx"], st["ws_bytes"], st["wk"], st["kern_us"]
+    ps = S.pool_slots
+
+    # The prefix/tail split of the same step: per layer, a prefix-only call over the L prefix rows, the tree call
+    # over the T tail rows (L = 0) and the LSE merge of the two (one stream, so they share a workspace).
+    split_bufs = [torch.empty_like(st["out_t"]), torch.empty_like(st["lse_t"]), torch.empty_like(st["out_t"]),
+                  torch.empty_like(st["lse_t"])]
+    split_ptr = [t.data_ptr() for t in split_bufs]
+
+    def split_step(set_ptrs):
+        rc = kdv.kdv_build_tree_mask(fx["parent"], T, fx["mask"], fx["status"], sh)
+        if rc:
+            raise kdv.KdvError(rc, "kdv_build_tree_mask")
+        for lp in set_ptrs:
+            rc = kdv.kdv_prefix_mla_attn(dims, *lp, ps, fx["pt"], L, T, split_ptr[0], split_ptr[1], fx["ws"],
+                                         ws_bytes, sh)
+            if rc:
+                raise kdv.KdvError(rc, "kdv_prefix_mla_attn")
+            rc = kdv.kdv_verify_mla_attn(dims, *lp, ps, fx["pt"] + 4 * L, 0, T, fx["mask"], split_ptr[2],
+                                         split_ptr[3], fx["ws"], ws_bytes, sh)
+            if rc:
+                raise kdv.KdvError(rc, "kdv_verify_mla_attn")
+            rc = kdv.kdv_merge_attn_states(split_ptr[0], split_ptr[1], split_ptr[2], split_ptr[3], T * H, Dv,
+                                           fx["out"], fx["lse"], sh)
+            if rc:
+                raise kdv.KdvError(rc, "kdv_merge_attn_states")
+    per_split_step = dict(tree_mask=1, q_absorb=2 * lps, splitkv=2 * lps, combine_up=2 * lps, merge_states=lps)
     ms_split = None
     if L >= 1:
         log(f"[bench] timing {K} steps of the prefix/tail split (cold)")
-        run_steps(cold_ptrs, 2, split_step)
+        st["run_steps"](st["cold_ptrs"], 2, split_step)
         note("split warm-up", per_split_step, 2)
-        ms_split = timed(cold_ptrs, K, split_step)
-        note_timed("split cold", per_split_step, K)
-
-    # per-kernel device time: events stamped by each kernel's own dispatch
-    log("[bench] per-kernel timing")
-    EvArr = ctypes.c_void_p * 6
-    Kp = min(K, max(1, 400 // layers_per_step))
-    n_calls = Kp * layers_per_step
-    ev_list = [EvArr(*[hip.event() for _ in range(6)]) for _ in range(n_calls)]
-    per_step_evs = []
-    for i in range(Kp):
-        per_step_evs.append(ev_list[i * layers_per_step:(i + 1) * layers_per_step])
-
-    def step_ev(set_ptrs, evs):
-        rc = kdv.kdv_build_tree_mask(fixed["parent"], T, fixed["mask"], fixed["status"], sh)
-        if rc:
-            raise kdv.KdvError(rc, "kdv_build_tree_mask")
-        for lp, ev in zip(set_ptrs, evs):
-            rc = kdv.kdv_verify_mla_attn_profiled(dims, *lp, pool_slots, fixed["pt"], L, T, fixed["mask"],
-                                                  fixed["out"], fixed["lse"], fixed["ws"], ws_bytes, sh,
-                                                  ctypes.addressof(ev))
-            if rc:
-                raise kdv.KdvError(rc, "kdv_verify_mla_attn_profiled")
-
-    # Eager launches (events stamped inside a captured graph cannot be timed), queued behind a spin kernel so
-    # that the kernels run back to back as in the graph.
-    kern_mode = "eager, kernel-stamped HIP events, queued behind a spin kernel"
-    torch.cuda.synchronize()
-    torch.cuda._sleep(int(2.4e9 * 0.05))
-    for i in range(Kp):
-        step_ev(cold_ptrs[i % len(cold_ptrs)], per_step_evs[i])
-    torch.cuda.synchronize()
-    note("eager cold, kernel events", per_step_eager, Kp)
-    names = ["q_absorb", "splitkv", "combine_up"]
-    samples = {n: [] for n in names}
-    for ev in ev_list:
-        for k, n in enumerate(names):
-            samples[n].append(1e3 * hip.elapsed_ms(ev[2 * k], ev[2 * k + 1]))
-    kern_us = {n: float(np.mean(v)) for n, v in samples.items()}
-    kern_pct = {n: [round(float(np.percentile(v, 10)), 3), round(float(np.percentile(v, 90)), 3)]
-                for n, v in samples.items()}
+        ms_split = st["timed"](st["cold_ptrs"], K, split_step)
+        st["note_timed"]("split cold", per_split_step, K)
 
     # The tree mask (once per verify step) and the greedy tree accept that follows verification: launch-bound,
     # timed as one HIP graph of many launches.
@@ -413,16 +474,16 @@ def run(args, torch, si, kdv, dev, hip, stream, sh):
         return 1e3 * hip.elapsed_ms(e0, e1) / n
 
     def mask_launch():
-        rc = kdv.kdv_build_tree_mask(fixed["parent"], T, fixed["mask"], fixed["status"], sh)
+        rc = kdv.kdv_build_tree_mask(fx["parent"], T, fx["mask"], fx["status"], sh)
         if rc:
             raise kdv.KdvError(rc, "kdv_build_tree_mask")
     kern_us["tree_mask"] = graph_us(mask_launch, counts=dict(tree_mask=1))
-    _, acc_tok, acc_pred = si.accept_inputs(0, T, follow=0.8, parent=parent_np)
+    _, acc_tok, acc_pred = si.accept_inputs(0, T, follow=0.8, parent=S.parent_np)
     acc_in = [torch.from_numpy(a.astype(np.int32)).to(dev) for a in (acc_tok, acc_pred)]
     acc_out = [torch.empty((n,), dtype=torch.int32, device=dev) for n in (T, 1, 1, 1)]
 
     def accept_launch():
-        rc = kdv.kdv_tree_accept(fixed["parent"], acc_in[0].data_ptr(), acc_in[1].data_ptr(), T,
+        rc = kdv.kdv_tree_accept(fx["parent"], acc_in[0].data_ptr(), acc_in[1].data_ptr(), T,
                                  *[t.data_ptr() for t in acc_out], sh)
         if rc:
             raise kdv.KdvError(rc, "kdv_tree_accept")
@@ -445,49 +506,42 @@ def run(args, torch, si, kdv, dev, hip, stream, sh):
 
     def merge_launch():
         rc = kdv.kdv_merge_attn_states(split_ptr[0], split_ptr[1], split_ptr[2], split_ptr[3], T * H, Dv,
-                                       fixed["out"], fixed["lse"], sh)
+                                       fx["out"], fx["lse"], sh)
         if rc:
             raise kdv.KdvError(rc, "kdv_merge_attn_states")
     merge_us = graph_us(merge_launch, counts=dict(merge_states=1)) if L >= 1 else None
     torch.cuda.synchronize()
 
-    batch_row = batched_verify_row(torch, si, kdv, dev, sh, graph_us, note) if args.workload != "full61" else None
+    batch_row = None
+    if args.workload != "full61" and not args.no_extra:
+        batch_row = batched_verify_row(torch, si, kdv, dev, sh, graph_us, note)
 
     mfma_peak = measured_mfma_peak(torch, kdv, dev, hip, sh, note)
-
-    us_layer_cold = 1e3 * ms_cold / (K * layers_per_step)
-    us_layer_hot = 1e3 * ms_hot / (K * layers_per_step)
-    tflops_cold = wk["flops"] / (us_layer_cold * 1e-6) / 1e12
-    tflops_hot = wk["flops"] / (us_layer_hot * 1e-6) / 1e12
     sk_tflops = wk["flops_splitkv"] / (kern_us["splitkv"] * 1e-6) / 1e12
 
     result = {
         "metric": METRIC,
-        "value": round(tflops_cold, 3),
+        "value": res["tflops"],
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": K,
         "warmup": Wm,
-        "ms_per_step": round(ms_cold / K, 6),
+        "ms_per_step": round(res["us_per_layer"] * lps / 1e3, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": desc, "heads": H, "tree_nodes": T, "prefix_len": L, "kv_lora_rank": R,
-                   "qk_rope_dim": Dr, "qk_nope_dim": Dn, "v_head_dim": Dv, "layers_per_step": layers_per_step,
-                   "kv_splits": splits, "timing": "one HIP graph of K steps" if not args.no_graph else "eager",
-                   "buffers": "cold: rotation over > 512 MiB of distinct layer buffers"},
-        "us_per_layer": round(us_layer_cold, 3),
-        "frac_bf16_peak": round(tflops_cold / PEAK_BF16_TFLOPS, 4),
-        "hbm_gbs": round(wk["bytes"] / (us_layer_cold * 1e-6) / 1e9, 1),
-        "hot": {"us_per_layer": round(us_layer_hot, 3), "tflops": round(tflops_hot, 3),
-                "frac_bf16_peak": round(tflops_hot / PEAK_BF16_TFLOPS, 4)},
-        "kernels_us": {k: round(v, 3) for k, v in kern_us.items()},
-        "kernels_us_p10_p90": kern_pct,
-        "kernel_timing": kern_mode,
-        "kernel_calls": n_calls,
-        "work_per_layer": {"gflop": round(wk["flops"] / 1e9, 4), "mbytes": round(wk["bytes"] / 1e6, 3)},
+        "config": {"workload": S.desc, "heads": H, "tree_nodes": T, "prefix_len": L, "kv_lora_rank": R,
+                   "qk_rope_dim": Dr, "qk_nope_dim": Dn, "v_head_dim": Dv, "layers_per_step": lps,
+                   "kv_splits": res["kv_splits"], "timing": res["timing"], "buffers": res["buffers"]},
+    }
+    for k in ("us_per_layer", "frac_bf16_peak", "hbm_gbs", "frac_hbm_peak", "us_per_layer_eager_p10_p50_p90", "hot",
+              "kernels_us", "kernels_us_p10_p90", "work_per_layer"):
+        result[k] = res[k]
+    result["kernels_us"]["tree_mask"] = round(kern_us["tree_mask"], 3)
+    result.update({
+        "kernel_timing": "eager, kernel-stamped HIP events, queued behind a spin kernel",
         "roofline": {"bound": "mfma", "kernel": "splitkv", "achieved": round(sk_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(sk_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_from_profile(args.workload),
@@ -501,20 +555,56 @@ def run(args, torch, si, kdv, dev, hip, stream, sh):
                       "draft_tree": {"us": round(build_us, 3), "block": 16, "topk": 8, "budget": 32,
                                      "nodes": int(b_out[2].item()), "timing": "one HIP graph of 200 launches",
                                      "bound": "latency of 31 dependent wave-wide selections"}},
-    }
+    })
     if batch_row is not None:
         result["next_rows"]["batched_verify"] = batch_row
     if ms_split is not None:
         result["next_rows"]["prefix_tail_split"] = {
-            "us_per_layer": round(1e3 * ms_split / (K * layers_per_step), 3),
-            "single_call_us_per_layer": round(us_layer_cold, 3),
+            "us_per_layer": round(1e3 * ms_split / (K * lps), 3),
+            "single_call_us_per_layer": res["us_per_layer"],
             "merge_us": round(merge_us, 3),
             "parts": "prefix-only attention over L rows + tree attention over the T tail rows + LSE merge",
             "timing": "one HIP graph of K steps, cold rotation; merge alone: one HIP graph of 200 launches"}
 
+    # The other configurations of the measured metric, each with its own inputs and the same measurement
+    extra = {}
+    if args.workload == "kimi5553" and not args.no_extra:
+        del S, st
+        torch.cuda.empty_cache()
+        Ke, We = min(K, 20), min(Wm, 3)
+        sweep = []
+        for Lx in SWEEP_L:
+            for Tx in SWEEP_T:
+                Sx = setup_workload(f"kimi:{Lx}:{Tx}", torch, si, dev)
+                r, _ = measure(Sx, args, torch, kdv, dev, hip, stream, sh, note, Ke, We)
+                r["bound"] = "hbm (weight streaming)" if Lx <= 1663 else "mfma"
+                sweep.append(r)
+                del Sx
+                torch.cuda.empty_cache()
+        extra["context_sweep"] = sweep
+        for wname in ("long200k", "full61"):
+            Sx = setup_workload(wname, torch, si, dev)
+            r, _ = measure(Sx, args, torch, kdv, dev, hip, stream, sh, note, min(Ke, 10) if wname == "full61" else Ke,
+                           min(We, 2))
+            extra[wname] = r
+            del Sx
+            torch.cuda.empty_cache()
+        result["configs"] = extra
+
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(args, inp, wk, layers_per_step)
+        result["cpu_baseline"] = cpu_baseline(args, S_inp(args, si), wk, lps, extra)
     print(json.dumps(result), flush=True)
+
+
+def S_inp(args, si):
+    kind, Lk, Tk, seed = parse_workload(args.workload)
+    if kind == "kimi5553":
+        return si.kimi(L=5553, T=15, seed=0, dist="literal")
+    if kind == "long200k":
+        return si.long_fragmented(seed=0, dist="literal")
+    if kind == "full61":
+        return None
+    return si.kimi(L=Lk, T=Tk, seed=seed, dist="literal")
 
 
 def measured_mfma_peak(torch, kdv, dev, hip, sh, note, iters=2048):
@@ -594,55 +684,107 @@ def batched_verify_row(torch, si, kdv, dev, sh, graph_us, note, C=10, L=5553, T=
             "timing": "one HIP graph of 20 calls, hot buffers (shared pool of the ten requests: 64 MiB)"}
 
 
-def cpu_baseline(args, inp, wk, layers_per_step):
-    """The fp64 oracle, as it stands, on the host cores, over a bounded sample of the same workload."""
-    import oracle
-    import synth_inputs as si
+def _cpu_info():
+    """Host CPU as the machine reports it: model name, family / model numbers, logical CPUs."""
+    info = {"cpu_model": "unknown", "cpu_family": None, "cpu_model_number": None, "host_cpus": os.cpu_count()}
+    try:
+        for ln in open("/proc/cpuinfo"):
+            k, _, v = ln.partition(":")
+            k, v = k.strip(), v.strip()
+            if k == "model name" and info["cpu_model"] == "unknown":
+                info["cpu_model"] = v
+            elif k == "cpu family" and info["cpu_family"] is None:
+                info["cpu_family"] = int(v)
+            elif k == "model" and info["cpu_model_number"] is None:
+                info["cpu_model_number"] = int(v)
+    except Exception:
+        pass
+    return info
+
+
+def _blas():
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+        pools = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        threads = max([i.get("num_threads", 1) for i in pools] or [1])
+        name = ", ".join(sorted({f"{i.get('internal_api')} {i.get('version')}" for i in pools})) or "unknown"
+        return threads, name
     except Exception:
-        threads = os.cpu_count()
+        return os.cpu_count(), "unknown"
+
+
+def _time_oracle(fn, seconds, max_calls=200):
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        fn()
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or n >= max_calls:
+            return el / n, n, el
+
+
+def cpu_baseline(args, inp, wk, layers_per_step, extra):
+    """The fp64 oracle, as it stands, on the host cores, over bounded samples of the measured workloads; the
+    headline layer also on one thread; the heapq tree builder at the GPU builder's settings."""
+    import oracle
+    import synth_inputs as si
+    threads, blas = _blas()
     if inp is None:  # full61: one layer of the same shape, generated on the host
         parent, table = si.full61_shared()
         inp = si.full61_layer(0, parent, table)
         heads = [0, 1]
-        frac = len(heads) / inp.H
         sample = f"oracle on heads {heads} of one 8-head layer (all 32 nodes, 131072-token prefix)"
     elif inp.L > 100000:
         heads = [0, 1]
-        frac = len(heads) / inp.H
         sample = f"oracle on heads {heads} of the layer (all nodes)"
     else:
         heads = None
-        frac = 1.0
         sample = "oracle on whole layers of the timed workload"
+    frac = 1.0 if heads is None else len(heads) / inp.H
     log("[bench] cpu baseline (oracle)")
-    t0 = time.perf_counter()
-    n = 0
-    while True:
-        oracle.verify_inputs(inp, heads=heads)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= args.cpu_seconds or n >= 200:
-            break
-    s_per_layer = el / n / frac
+    sec, n, el = _time_oracle(lambda: oracle.verify_inputs(inp, heads=heads), args.cpu_seconds)
+    s_per_layer = sec / frac
     wk1 = work(inp.H, inp.Dn, inp.Dr, inp.R, inp.Dv, inp.L, inp.T, inp.parent)
-    cpu_model, blas = "unknown", "unknown"
+    res = {"value": round(wk1["flops"] / s_per_layer / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+           **_cpu_info(), "blas": blas,
+           "kind": "oracle", "sample": f"{sample}; {n} calls in {el:.1f} s",
+           "seconds_per_layer": round(s_per_layer, 4)}
     try:
-        cpu_model = next(ln.split(":", 1)[1].strip() for ln in open("/proc/cpuinfo") if ln.startswith("model name"))
-    except Exception:
-        pass
-    try:
-        from threadpoolctl import threadpool_info
-        blas = ", ".join(sorted({f"{i.get('internal_api')} {i.get('version')}" for i in threadpool_info()
-                                 if i.get("user_api") == "blas"})) or "unknown"
-    except Exception:
-        pass
-    return {"value": round(wk1["flops"] / s_per_layer / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
-            "cpu_model": cpu_model, "blas": blas,
-            "kind": "oracle", "sample": f"{sample}; {n} calls in {el:.1f} s",
-            "seconds_per_layer": round(s_per_layer, 4), "host_cpus": os.cpu_count()}
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1, user_api="blas"):
+            sec1, n1, el1 = _time_oracle(lambda: oracle.verify_inputs(inp, heads=heads), args.cpu_seconds / 2)
+        res["single_thread"] = {"seconds_per_layer": round(sec1 / frac, 4),
+                                "value": round(wk1["flops"] / (sec1 / frac) / 1e12, 6), "cores": 1,
+                                "sample": f"{sample}; {n1} calls in {el1:.1f} s, BLAS limited to one thread"}
+    except Exception as e:  # threadpoolctl missing: say so
+        res["single_thread"] = {"error": repr(e)}
+    # the other configurations: seconds per layer of the oracle on a small sample each
+    if extra:
+        per_cfg = {}
+        for r in extra.get("context_sweep", []):
+            L, T = r["prefix_len"], r["tree_nodes"]
+            xi = si.kimi(L=L, T=T, seed=2 * SWEEP_L.index(L) + SWEEP_T.index(T), dist="literal")
+            sx, nx, _ = _time_oracle(lambda: oracle.verify_inputs(xi, heads=[0, 1, 2, 3]), 1.0, 20)
+            per_cfg[f"kimi:{L}:{T}"] = {"seconds_per_layer": round(sx * xi.H / 4, 4),
+                                        "sample": f"heads 0-3 of the layer, {nx} calls"}
+        if "long200k" in extra:
+            xi = si.long_fragmented(seed=0, dist="literal")
+            sx, nx, _ = _time_oracle(lambda: oracle.verify_inputs(xi, heads=[0]), 1.0, 5)
+            per_cfg["long200k"] = {"seconds_per_layer": round(sx * xi.H, 3), "sample": f"head 0, {nx} calls"}
+        if "full61" in extra:
+            parent, table = si.full61_shared()
+            xi = si.full61_layer(0, parent, table)
+            sx, nx, _ = _time_oracle(lambda: oracle.verify_inputs(xi, heads=[0]), 1.0, 5)
+            per_cfg["full61"] = {"seconds_per_layer": round(sx * xi.H, 3), "seconds_per_step": round(61 * sx * xi.H, 2),
+                                 "sample": f"head 0 of layer 0, {nx} calls"}
+        res["configs_seconds_per_layer"] = per_cfg
+    # the best-first tree builder (heapq, pure Python) at the GPU builder's settings: block 16, top-8, budget 32
+    b_logp, b_tok = si.draft_topk(0, 16, 8)
+    sb, nb, _ = _time_oracle(lambda: oracle.build_draft_tree(b_logp, b_tok, 32, 7), 1.0, 20000)
+    res["draft_tree"] = {"us_per_tree": round(sb * 1e6, 2), "us_per_batch_of_64": round(64 * sb * 1e6, 1),
+                         "cores": 1, "sample": f"oracle.build_draft_tree (heapq, one thread), {nb} trees"}
+    return res
 
 
 # ------------------------------------------------------------------------------------------------ profiles
@@ -670,7 +812,7 @@ def source_hash():
 
 
 def traffic_profile_path(workload):
-    return os.path.join(ROOT, "profiles", f"splitkv_{workload}_hbm_traffic.md")
+    return os.path.join(ROOT, "profiles", f"splitkv_{profile_tag(workload)}_hbm_traffic.md")
 
 
 def traffic_from_profile(workload):
@@ -761,7 +903,7 @@ def summarize_profile(d, workload):
             if seg:
                 avg = sum(e - s for _, s, e in seg) / len(seg) / 1e3
                 lines.append(f"| {k} | {name} | {len(seg)} | {avg:.2f} |")
-                if name == "eager cold, kernel events":
+                if name == f"{workload}: eager cold, kernel events":
                     eager[k] = avg
     lines += ["", "Eager cold launches under the tracer against bench.py's kernel-stamped HIP events without it:", "",
               "| kernel | traced average us | bench.py events us |", "|---|---|---|"]
@@ -770,7 +912,7 @@ def summarize_profile(d, workload):
     # step span in the timed cold replay (includes gaps between kernels): q_absorb starts every layer
     tm = sorted(durs["q_absorb_kernel"])
     ph, _ = _phases(bench, "q_absorb_kernel")
-    a, b = ph["graph cold, timed replay"]
+    a, b = ph[f"{workload}: graph cold, timed replay"]
     lps = bench["config"]["layers_per_step"]
     span = lps * (tm[b - 1][1] - tm[a][1]) / (b - a - 1) / 1e3 if b - a > 1 else float("nan")
     lines += ["", f"Cold timed replay: one step every {span:.2f} us under the tracer "
@@ -779,7 +921,7 @@ def summarize_profile(d, workload):
               "(kdv_verify_mla_attn_tree); the eager per-kernel launches and the split phases use the separate "
               "mask kernel.  bench.py's kernel-stamped HIP events are taken over its eager cold launches without "
               "the tracer (the tracer lengthens event-bracketed launches).", ""]
-    with open(os.path.join(out_dir, f"verify_{workload}_kernel_trace.md"), "w") as f:
+    with open(os.path.join(out_dir, f"verify_{profile_tag(workload)}_kernel_trace.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
 
     # HBM traffic of the split-KV kernel: FETCH_SIZE and WRITE_SIZE, scaled by the copy calibration
@@ -811,7 +953,7 @@ def summarize_profile(d, workload):
         if k not in fetch or k not in write:
             continue
         ph, total = _phases(fb, k)
-        a, b = ph["eager cold, kernel events"]
+        a, b = ph[f"{workload}: eager cold, kernel events"]
         fv, wv = fetch[k][a:b], write[k][a:b]
         if len(fetch[k]) != total or len(write[k]) != total:
             raise SystemExit(f"{k}: counter dispatch count mismatch")
@@ -827,7 +969,7 @@ def summarize_profile(d, workload):
                    "traffic_bytes_per_launch": round(fb_bytes + wb_bytes)}
     lines += ["", "Record read by bench.py (`roofline.traffic`, used only while the kernel source hash matches):",
               "", "```json", json.dumps(rec), "```", ""]
-    with open(os.path.join(out_dir, f"splitkv_{workload}_hbm_traffic.md"), "w") as f:
+    with open(os.path.join(out_dir, f"splitkv_{profile_tag(workload)}_hbm_traffic.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     if os.path.isdir(os.path.join(d, "mfma")):
         _summarize_mfma(d, workload, cmds, bench, durs, out_dir)
@@ -857,12 +999,12 @@ def _summarize_mfma(d, workload, cmds, trace_bench, durs, out_dir):
         if k not in insts or k not in busy or k not in durs:
             continue
         ph, total = _phases(mb, k)
-        a, b = ph["eager cold, kernel events"]
+        a, b = ph[f"{workload}: eager cold, kernel events"]
         iv, bv = insts[k][a:b], busy[k][a:b]
         if len(insts[k]) != total or not iv:
             continue
         tph, _ = _phases(trace_bench, k)
-        ta, tb = tph["eager cold, kernel events"]
+        ta, tb = tph[f"{workload}: eager cold, kernel events"]
         seg = sorted(durs[k])[ta:tb]
         us = sum(e - s_ for _, s_, e in seg) / len(seg) / 1e3
         n = sum(iv) / len(iv)
@@ -870,7 +1012,7 @@ def _summarize_mfma(d, workload, cmds, trace_bench, durs, out_dir):
         gflop = n * 32768 / 1e9
         frac = cyc / (simds * us * 1e-6 * mhz * 1e6)
         lines.append(f"| {k} | {n:.0f} | {gflop:.3f} | {us:.2f} | {gflop / (us * 1e-6) / 1e3:.1f} | {frac:.3f} |")
-    with open(os.path.join(out_dir, f"verify_{workload}_mfma.md"), "w") as f:
+    with open(os.path.join(out_dir, f"verify_{profile_tag(workload)}_mfma.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
 
 

@@ -9,7 +9,7 @@
 # Run from anywhere on the GPU machine: bash profile_bench.sh [workload]
 R=$(cd "$(dirname "$0")" && pwd)
 W=${1:-kimi5553}
-O=$R/gpurun_out/profile_$W
+O=$R/gpurun_out/profile_${W//:/_}
 mkdir -p "$O"
 : > "$O/commands.txt"
 cd /tmp && export TMPDIR=/tmp
@@ -28,18 +28,18 @@ run() {  # run <seconds> <stdout file> <command...>: log the command, stop the s
   fi
 }
 
-run 300 "$O/plain_bench.json" python3 "$R/bench.py" --workload "$W" --steps 50 --warmup 5 --no-cpu-baseline
+run 300 "$O/plain_bench.json" python3 "$R/bench.py" --workload "$W" --steps 50 --warmup 5 --no-cpu-baseline --no-extra
 run 300 "$O/trace_bench.json" rocprofv3 --kernel-trace --stats -f csv -d "$O/trace" -o run -- \
-  python3 "$R/bench.py" --workload "$W" --steps 50 --warmup 5 --no-cpu-baseline
+  python3 "$R/bench.py" --workload "$W" --steps 50 --warmup 5 --no-cpu-baseline --no-extra
 run 120 "$O/fetch_bench.json" rocprofv3 --pmc FETCH_SIZE -f csv -d "$O/fetch" -o run -- \
-  python3 "$R/bench.py" --workload "$W" --steps 10 --warmup 2 --no-cpu-baseline
+  python3 "$R/bench.py" --workload "$W" --steps 10 --warmup 2 --no-cpu-baseline --no-extra
 run 120 "$O/write_bench.json" rocprofv3 --pmc WRITE_SIZE -f csv -d "$O/write" -o run -- \
-  python3 "$R/bench.py" --workload "$W" --steps 10 --warmup 2 --no-cpu-baseline
+  python3 "$R/bench.py" --workload "$W" --steps 10 --warmup 2 --no-cpu-baseline --no-extra
 run 120 "$O/mfma_bench.json" rocprofv3 --pmc SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES -f csv -d "$O/mfma" -o run -- \
-  python3 "$R/bench.py" --workload "$W" --steps 10 --warmup 2 --no-cpu-baseline
+  python3 "$R/bench.py" --workload "$W" --steps 10 --warmup 2 --no-cpu-baseline --no-extra
 run 120 "$O/copy_fetch.json" rocprofv3 --pmc FETCH_SIZE -f csv -d "$O/copy_fetch" -o run -- \
   python3 "$R/bench.py" --copy-calibration
 run 120 "$O/copy_write.json" rocprofv3 --pmc WRITE_SIZE -f csv -d "$O/copy_write" -o run -- \
   python3 "$R/bench.py" --copy-calibration
-echo "python3 \$REPO/bench.py --workload $W --summarize-profile gpurun_out/profile_$W" >> "$O/commands.txt"
+echo "python3 \$REPO/bench.py --workload $W --summarize-profile gpurun_out/profile_${W//:/_}" >> "$O/commands.txt"
 python3 "$R/bench.py" --workload "$W" --summarize-profile "$O"

@@ -9,11 +9,11 @@ import pytest
 
 import bench
 
-PHASES = [["warm-up", {"q_absorb_kernel": 2, "splitkv_kernel": 2, "combine_up_kernel": 2}],
-          ["graph cold, upload replay", {"q_absorb_kernel": 3, "splitkv_kernel": 3, "combine_up_kernel": 3}],
-          ["graph cold, timed replay", {"q_absorb_kernel": 3, "splitkv_kernel": 3, "combine_up_kernel": 3}],
-          ["eager cold, kernel events", {"tree_mask_kernel": 2, "q_absorb_kernel": 2, "splitkv_kernel": 2,
-                                         "combine_up_kernel": 2}],
+PHASES = [["kimi5553: warm-up", {"q_absorb_kernel": 2, "splitkv_kernel": 2, "combine_up_kernel": 2}],
+          ["kimi5553: graph cold, upload replay", {"q_absorb_kernel": 3, "splitkv_kernel": 3, "combine_up_kernel": 3}],
+          ["kimi5553: graph cold, timed replay", {"q_absorb_kernel": 3, "splitkv_kernel": 3, "combine_up_kernel": 3}],
+          ["kimi5553: eager cold, kernel events", {"tree_mask_kernel": 2, "q_absorb_kernel": 2, "splitkv_kernel": 2,
+                                                   "combine_up_kernel": 2}],
           ["launch-timing graph: tree_mask", {"tree_mask_kernel": 4}]]
 NAMES = {"tree_mask_kernel": "kdv::tree_mask_kernel(int const*, int, unsigned int*, int*)",
          "q_absorb_kernel": "void kdv::q_absorb_kernel<128, 512, 64>(...)",
@@ -96,11 +96,11 @@ def profile_dir(tmp_path):
 def test_phases_follow_the_ledger():
     ph, total = bench._phases(_bench_json(), "splitkv_kernel")
     assert total == 10
-    assert ph["graph cold, timed replay"] == (5, 8)
-    assert ph["eager cold, kernel events"] == (8, 10)
+    assert ph["kimi5553: graph cold, timed replay"] == (5, 8)
+    assert ph["kimi5553: eager cold, kernel events"] == (8, 10)
     assert ph["launch-timing graph: tree_mask"] == (10, 10)
     ph, total = bench._phases(_bench_json(), "tree_mask_kernel")
-    assert total == 6 and ph["eager cold, kernel events"] == (0, 2)
+    assert total == 6 and ph["kimi5553: eager cold, kernel events"] == (0, 2)
 
 
 def test_summaries_from_a_synthetic_profile(profile_dir):
@@ -109,7 +109,7 @@ def test_summaries_from_a_synthetic_profile(profile_dir):
     assert sorted(os.listdir(out)) == ["splitkv_kimi5553_hbm_traffic.md", "verify_kimi5553_kernel_trace.md",
                                       "verify_kimi5553_mfma.md"]
     trace = open(os.path.join(out, "verify_kimi5553_kernel_trace.md")).read()
-    assert "| splitkv_kernel | graph cold, timed replay | 3 | 24.00 |" in trace
+    assert "| splitkv_kernel | kimi5553: graph cold, timed replay | 3 | 24.00 |" in trace
     assert "| splitkv_kernel | 24.00 | 24.40 |" in trace  # traced eager average beside bench.py's events
     traffic = open(os.path.join(out, "splitkv_kimi5553_hbm_traffic.md")).read()
     rec = json.loads(traffic.split("```json\n")[1].split("\n```")[0])
@@ -121,3 +121,12 @@ def test_summaries_from_a_synthetic_profile(profile_dir):
     # 354960 MFMAs x 32768 flop over 24 us; busy = 32 cycles each over 1024 SIMDs x 24 us x 2.4 GHz
     busy = 354960 * 32 / (1024 * 24e-6 * 2400e6)
     assert f"| splitkv_kernel | 354960 | 11.631 | 24.00 | 484.6 | {busy:.3f} |" in mfma
+
+
+def test_workload_names():
+    assert bench.parse_workload("kimi5553")[0] == "kimi5553"
+    assert bench.parse_workload("kimi:13:9") == ("kimi", 13, 9, 0)
+    assert bench.parse_workload("kimi:16384:15") == ("kimi", 16384, 15, 9)
+    assert bench.profile_tag("kimi:16384:15") == "kimi_L16384_T15"
+    with pytest.raises(SystemExit):
+        bench.parse_workload("sweep:1")
