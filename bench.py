@@ -53,8 +53,10 @@ KERNEL_SOURCES = ("speculative_decoding_tree_parent_amd/csrc/verify.hip",
                   "speculative_decoding_tree_parent_amd/csrc/common.h",
                   "speculative_decoding_tree_parent_amd/csrc/tree_mask.h",
                   "speculative_decoding_tree_parent_amd/csrc/tree.hip")
-KERNELS = ("tree_mask_kernel", "q_absorb_kernel", "splitkv_kernel", "combine_up_kernel", "tree_accept_kernel",
-           "draft_tree_kernel", "merge_states_kernel")
+KERNELS = ("tree_mask_kernel", "verify_fused_kernel", "q_absorb_kernel", "splitkv_kernel", "combine_up_kernel",
+           "tree_accept_kernel", "draft_tree_kernel", "merge_states_kernel")
+FUSED_NAMES = ["verify_fused"]
+SPLIT_NAMES = ["q_absorb", "splitkv", "combine_up"]
 
 
 def log(msg):
@@ -220,6 +222,8 @@ def measure(S, args, torch, kdv, dev, hip, stream, sh, note, K, Wm, full=True):
     ws_bytes = kdv.verify_workspace_bytes(dims, T, L)
     ws_t = torch.zeros((ws_bytes,), dtype=torch.uint8, device=dev)
     splits = kdv.kdv_verify_num_splits(dims, T, L)
+    nk = kdv.kdv_verify_kernel_count(dims, T, L)
+    names = FUSED_NAMES if nk == 1 else SPLIT_NAMES
     wk = work(H, Dn, Dr, R, Dv, L, T, S.parent_np)
 
     def ptrs(t):
@@ -269,8 +273,8 @@ def measure(S, args, torch, kdv, dev, hip, stream, sh, note, K, Wm, full=True):
         torch.cuda.synchronize()
         return ms
 
-    per_step = dict(q_absorb=lps, splitkv=lps, combine_up=lps)  # (the mask is built inside the first call)
-    per_step_eager = dict(tree_mask=1, q_absorb=lps, splitkv=lps, combine_up=lps)
+    per_step = {n: lps for n in names}  # (the mask is built inside the first call)
+    per_step_eager = dict(tree_mask=1, **per_step)
 
     def note_timed(what, counts, n):
         if args.no_graph:
@@ -296,9 +300,9 @@ def measure(S, args, torch, kdv, dev, hip, stream, sh, note, K, Wm, full=True):
     # per-kernel device time and per-step spread: events stamped by each kernel's own dispatch, eager launches
     # queued behind a spin kernel so that they run back to back as in the graph
     log(f"[bench] {S.name}: per-kernel timing")
-    EvArr = ctypes.c_void_p * 6
+    EvArr = ctypes.c_void_p * (2 * nk)
     Kp = min(K, max(1, 400 // lps))
-    ev_list = [EvArr(*[hip.event() for _ in range(6)]) for _ in range(Kp * lps)]
+    ev_list = [EvArr(*[hip.event() for _ in range(2 * nk)]) for _ in range(Kp * lps)]
 
     def step_ev(set_ptrs, evs):
         rc = kdv.kdv_build_tree_mask(fx["parent"], T, fx["mask"], fx["status"], sh)
@@ -315,13 +319,12 @@ def measure(S, args, torch, kdv, dev, hip, stream, sh, note, K, Wm, full=True):
         step_ev(cold_ptrs[i % len(cold_ptrs)], ev_list[i * lps:(i + 1) * lps])
     torch.cuda.synchronize()
     note(f"{S.name}: eager cold, kernel events", per_step_eager, Kp)
-    names = ["q_absorb", "splitkv", "combine_up"]
     samples = {n: [] for n in names}
     for ev in ev_list:
         for k, n in enumerate(names):
             samples[n].append(1e3 * hip.elapsed_ms(ev[2 * k], ev[2 * k + 1]))
     # a layer's span: first kernel's start to last kernel's end (per layer of every eager step)
-    spans = [1e3 * hip.elapsed_ms(ev[0], ev[5]) for ev in ev_list]
+    spans = [1e3 * hip.elapsed_ms(ev[0], ev[2 * nk - 1]) for ev in ev_list]
     kern_us = {n: float(np.mean(v)) for n, v in samples.items()}
     kern_pct = {n: [round(float(np.percentile(v, 10)), 3), round(float(np.percentile(v, 90)), 3)]
                 for n, v in samples.items()}
@@ -334,7 +337,7 @@ def measure(S, args, torch, kdv, dev, hip, stream, sh, note, K, Wm, full=True):
     touched = min(K, S.n_cold) * S.set_bytes if lps == 1 else S.set_bytes
     res = {
         "workload": S.desc, "heads": H, "tree_nodes": T, "prefix_len": L, "layers_per_step": lps,
-        "kv_splits": splits,
+        "kv_splits": splits, "kernels_per_call": nk,
         "us_per_layer": round(us_cold, 3),
         "tflops": round(tf_cold, 3), "frac_bf16_peak": round(tf_cold / PEAK_BF16_TFLOPS, 4),
         "hbm_gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
@@ -351,7 +354,7 @@ def measure(S, args, torch, kdv, dev, hip, stream, sh, note, K, Wm, full=True):
                   "; eager p10/p50/p90: first kernel's start to last kernel's end of each layer, kernel-stamped events",
     }
     state = dict(dims=dims, fx=fx, ws_bytes=ws_bytes, cold_ptrs=cold_ptrs, out_t=out_t, lse_t=lse_t, wk=wk,
-                 kern_us=kern_us, timed=timed, step=step, note_timed=note_timed, run_steps=run_steps)
+                 kern_us=kern_us, timed=timed, step=step, note_timed=note_timed, run_steps=run_steps, names=names)
     return res, state
 
 
@@ -446,7 +449,7 @@ def run(args, torch, si, kdv, dev, hip, stream, sh):
                                            fx["out"], fx["lse"], sh)
             if rc:
                 raise kdv.KdvError(rc, "kdv_merge_attn_states")
-    per_split_step = dict(tree_mask=1, q_absorb=2 * lps, splitkv=2 * lps, combine_up=2 * lps, merge_states=lps)
+    per_split_step = dict(tree_mask=1, **{n: 2 * lps for n in st["names"]}, merge_states=lps)
     ms_split = None
     if L >= 1:
         log(f"[bench] timing {K} steps of the prefix/tail split (cold)")
@@ -514,10 +517,13 @@ def run(args, torch, si, kdv, dev, hip, stream, sh):
 
     batch_row = None
     if args.workload != "full61" and not args.no_extra:
-        batch_row = batched_verify_row(torch, si, kdv, dev, sh, graph_us, note)
+        batch_row = batched_verify_row(torch, si, kdv, dev, sh, graph_us, note, st["names"])
 
     mfma_peak = measured_mfma_peak(torch, kdv, dev, hip, sh, note)
-    sk_tflops = wk["flops_splitkv"] / (kern_us["splitkv"] * 1e-6) / 1e12
+    # the dominant kernel: the single launch (all of the call's work) or, with three launches, the split-KV pass
+    dom = "verify_fused" if "verify_fused" in kern_us else "splitkv"
+    dom_flops = wk["flops"] if dom == "verify_fused" else wk["flops_splitkv"]
+    sk_tflops = dom_flops / (kern_us[dom] * 1e-6) / 1e12
 
     result = {
         "metric": METRIC,
@@ -542,12 +548,12 @@ def run(args, torch, si, kdv, dev, hip, stream, sh):
     result["kernels_us"]["tree_mask"] = round(kern_us["tree_mask"], 3)
     result.update({
         "kernel_timing": "eager, kernel-stamped HIP events, queued behind a spin kernel",
-        "roofline": {"bound": "mfma", "kernel": "splitkv", "achieved": round(sk_tflops, 2),
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(sk_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(sk_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic_from_profile(args.workload),
+                     "traffic": traffic_from_profile(args.workload, dom),
                      "measured_mfma_peak": round(mfma_peak, 1),
                      "frac_of_measured_peak": round(sk_tflops / mfma_peak, 4),
-                     "work_per_launch_gflop": round(wk["flops_splitkv"] / 1e9, 4)},
+                     "work_per_launch_gflop": round(dom_flops / 1e9, 4)},
         "cpu_baseline": None,
         "dispatch_phases": ledger,
         "next_rows": {"tree_accept": {"us": round(accept_us, 3), "nodes": T, "accepted_path_nodes": n_path,
@@ -626,7 +632,7 @@ def measured_mfma_peak(torch, kdv, dev, hip, sh, note, iters=2048):
     return blocks * 4 * iters * 4 * 32768 / (ms * 1e-3) / 1e12
 
 
-def batched_verify_row(torch, si, kdv, dev, sh, graph_us, note, C=10, L=5553, T=15):
+def batched_verify_row(torch, si, kdv, dev, sh, graph_us, note, single_names, C=10, L=5553, T=15):
     """Ten concurrent 15-node trees over 5553-token prefixes (the pages' C = 10 serving level, at the headline
     shape): one kdv_verify_mla_attn_batch call against the same requests as C single calls (hot buffers)."""
     log(f"[bench] batched verify: {C} requests")
@@ -646,7 +652,7 @@ def batched_verify_row(torch, si, kdv, dev, sh, graph_us, note, C=10, L=5553, T=
     lse = torch.empty((C * T, H), dtype=torch.float32, device=dev)
     Ls, Ts = [L] * C, [T] * C
     ws_b = kdv.verify_batch_workspace_bytes(dims, Ls, Ts)
-    ws = torch.empty((ws_b,), dtype=torch.uint8, device=dev)
+    ws = torch.zeros((ws_b,), dtype=torch.uint8, device=dev)
     la, lp = kdv._host_i32(Ls)
     ta, tp = kdv._host_i32(Ts)
     base = [t.data_ptr() for t in (wuk, wuv, ckv, kpe)]
@@ -672,7 +678,7 @@ def batched_verify_row(torch, si, kdv, dev, sh, graph_us, note, C=10, L=5553, T=
                 raise kdv.KdvError(rc, "kdv_verify_mla_attn")
     call = dict(q_absorb=1, splitkv=1, combine_up=1)
     batch_us = graph_us(batch_launch, n=20, counts=call, label="batch: graph of batched calls")
-    single_us = graph_us(singles_launch, n=20, counts={k: C * v for k, v in call.items()},
+    single_us = graph_us(singles_launch, n=20, counts={k: C for k in single_names},
                          label="batch: graph of single calls")
     torch.cuda.synchronize()
     assert int(status.sum().item()) == 0
@@ -811,14 +817,14 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
-def traffic_profile_path(workload):
-    return os.path.join(ROOT, "profiles", f"splitkv_{profile_tag(workload)}_hbm_traffic.md")
+def traffic_profile_path(workload, kernel):
+    return os.path.join(ROOT, "profiles", f"{kernel}_{profile_tag(workload)}_hbm_traffic.md")
 
 
-def traffic_from_profile(workload):
-    """HBM bytes per split-KV launch from the committed counter summary, or None when there is none or the
-    kernel source has changed since the counters were taken."""
-    path = traffic_profile_path(workload)
+def traffic_from_profile(workload, kernel):
+    """HBM bytes per launch of the dominant kernel from the committed counter summary, or None when there is none
+    or the kernel source has changed since the counters were taken."""
+    path = traffic_profile_path(workload, kernel)
     if not os.path.exists(path):
         return None
     m = re.search(r"```json\n(.*?)\n```", open(path).read(), re.S)
@@ -910,8 +916,9 @@ def summarize_profile(d, workload):
     for k, v in eager.items():
         lines.append(f"| {k} | {v:.2f} | {ev.get(k, float('nan')):.2f} |")
     # step span in the timed cold replay (includes gaps between kernels): q_absorb starts every layer
-    tm = sorted(durs["q_absorb_kernel"])
-    ph, _ = _phases(bench, "q_absorb_kernel")
+    first = "verify_fused_kernel" if "verify_fused_kernel" in durs else "q_absorb_kernel"
+    tm = sorted(durs[first])
+    ph, _ = _phases(bench, first)
     a, b = ph[f"{workload}: graph cold, timed replay"]
     lps = bench["config"]["layers_per_step"]
     span = lps * (tm[b - 1][1] - tm[a][1]) / (b - a - 1) / 1e3 if b - a > 1 else float("nan")
@@ -949,6 +956,7 @@ def summarize_profile(d, workload):
              f"(`--steps {fb['steps']} --warmup {fb['warmup']}`):", "",
              "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | fetched MB | written MB |", "|---|---|---|---|---|"]
     rec = None
+    dom_kernel = "verify_fused_kernel" if "verify_fused_kernel" in fetch else "splitkv_kernel"
     for k in KERNELS:
         if k not in fetch or k not in write:
             continue
@@ -962,14 +970,14 @@ def summarize_profile(d, workload):
         fk, wk_ = sum(fv) / len(fv), sum(wv) / len(wv)
         fb_bytes, wb_bytes = fk * f_fac * 1024, wk_ * w_fac * 1024
         lines.append(f"| {k} | {fk:.1f} | {wk_:.1f} | {fb_bytes / 1e6:.3f} | {wb_bytes / 1e6:.3f} |")
-        if k == "splitkv_kernel":
+        if k == dom_kernel:
             rec = {"kernel": k, "workload": workload, "source_sha256": source_hash(),
                    "fetch_kib_per_dispatch": round(fk, 2), "write_kib_per_dispatch": round(wk_, 2),
                    "fetch_factor": round(f_fac, 4), "write_factor": round(w_fac, 4),
                    "traffic_bytes_per_launch": round(fb_bytes + wb_bytes)}
     lines += ["", "Record read by bench.py (`roofline.traffic`, used only while the kernel source hash matches):",
               "", "```json", json.dumps(rec), "```", ""]
-    with open(os.path.join(out_dir, f"splitkv_{profile_tag(workload)}_hbm_traffic.md"), "w") as f:
+    with open(os.path.join(out_dir, f"{dom_kernel[:-len('_kernel')]}_{profile_tag(workload)}_hbm_traffic.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     if os.path.isdir(os.path.join(d, "mfma")):
         _summarize_mfma(d, workload, cmds, bench, durs, out_dir)

@@ -25,7 +25,8 @@ KDV_ERR_ALIGN = -4
 KDV_ERR_WORKSPACE = -5
 KDV_ERR_HIP = -6
 KDV_ERR_PAGE = -7
-KDV_WS_HEADER = 256
+KDV_ERR_TIMEOUT = -8
+KDV_WS_HEADER = 65536
 KDV_NOALLOC_SCRATCH_BYTES = 32 << 20
 KDV_MAX_TREE_NODES = 64
 KDV_MAX_DRAFT_ENTRIES = 4096
@@ -36,7 +37,7 @@ EXPORTED = ("kdv_build_draft_tree", "kdv_build_tree_mask", "kdv_merge_attn_state
             "kdv_tree_accept", "kdv_verify_batch_workspace_bytes", "kdv_verify_mla_attn_batch",
             "kdv_verify_workspace_bytes", "kdv_verify_mla_attn", "kdv_verify_mla_attn_profiled",
             "kdv_verify_mla_attn_tree", "kdv_verify_mla_attn_noalloc",
-            "kdv_verify_num_splits", "kdv_mfma_probe", "kdv_status_string")
+            "kdv_verify_num_splits", "kdv_verify_kernel_count", "kdv_mfma_probe", "kdv_status_string")
 
 
 class KdvMlaDims(ctypes.Structure):
@@ -67,6 +68,8 @@ def _load() -> ctypes.CDLL:
     lib.kdv_verify_workspace_bytes.restype = sz
     lib.kdv_verify_num_splits.argtypes = [dims_p, i32, i32]
     lib.kdv_verify_num_splits.restype = i32
+    lib.kdv_verify_kernel_count.argtypes = [dims_p, i32, i32]
+    lib.kdv_verify_kernel_count.restype = i32
     lib.kdv_verify_mla_attn.argtypes = [dims_p, vp, vp, vp, vp, vp, vp, i64, vp, i32, i32, vp, vp, vp, vp, sz, vp]
     lib.kdv_verify_mla_attn.restype = ctypes.c_int
     lib.kdv_verify_mla_attn_profiled.argtypes = [dims_p, vp, vp, vp, vp, vp, vp, i64, vp, i32, i32, vp, vp, vp, vp,
@@ -121,6 +124,10 @@ def kdv_verify_num_splits(dims: KdvMlaDims, T: int, L: int) -> int:
     return _lib.kdv_verify_num_splits(ctypes.byref(dims), T, L)
 
 
+def kdv_verify_kernel_count(dims: KdvMlaDims, T: int, L: int) -> int:
+    return _lib.kdv_verify_kernel_count(ctypes.byref(dims), T, L)
+
+
 def kdv_verify_mla_attn(dims: KdvMlaDims, q_nope: int, q_rope: int, w_uk: int, w_uv: int, c_kv: int, k_pe: int,
                         pool_slots: int, page_table: int, L: int, T: int, mask: int, out: int, lse: int | None,
                         workspace: int, workspace_bytes: int, stream: int | None) -> int:
@@ -132,7 +139,7 @@ def kdv_verify_mla_attn_profiled(dims: KdvMlaDims, q_nope: int, q_rope: int, w_u
                                  k_pe: int, pool_slots: int, page_table: int, L: int, T: int, mask: int, out: int,
                                  lse: int | None, workspace: int, workspace_bytes: int, stream: int | None,
                                  events: int) -> int:
-    """`events`: address of six hipEvent_t handles: start/stop of each of the three kernels (include/kdv.h)."""
+    """`events`: address of 2 * kdv_verify_kernel_count() hipEvent_t handles: start/stop of each kernel (include/kdv.h)."""
     return _lib.kdv_verify_mla_attn_profiled(ctypes.byref(dims), q_nope, q_rope, w_uk, w_uv, c_kv, k_pe, pool_slots,
                                              page_table, L, T, mask, out, lse, workspace, workspace_bytes, stream,
                                              events)
@@ -232,6 +239,19 @@ def _bf16_ptr(t, what: str) -> int:
     return _ptr(t, torch.bfloat16 if t.dtype == torch.bfloat16 else torch.int16, what)
 
 
+def new_workspace(nbytes: int, device) -> "torch.Tensor":
+    """A device workspace of nbytes, zeroed (its first KDV_WS_HEADER bytes must be zero before the first call)."""
+    import torch
+    return torch.zeros((nbytes,), dtype=torch.uint8, device=device)
+
+
+def wait_status(workspace) -> int:
+    """KDV_OK, or KDV_ERR_TIMEOUT if a wait inside the last single-launch verify call on this workspace gave up.
+    Reads the device (synchronising with it)."""
+    import torch
+    return int(workspace[4:8].view(torch.int32).item())
+
+
 def debug_status(workspace) -> int:
     """The page-table status a call made with KDV_DEBUG set wrote into its workspace (KDV_OK or KDV_ERR_PAGE).
     Reads the device (synchronising with it)."""
@@ -313,7 +333,7 @@ def verify_mla_attn(dims: KdvMlaDims, q_nope, q_rope, w_uk, w_uv, c_kv, k_pe, pa
     if out is None:
         out = torch.empty((T, H, dims.v_head_dim), dtype=torch.bfloat16, device=q_nope.device)
     if workspace is None:
-        workspace = torch.empty((verify_workspace_bytes(dims, T, L),), dtype=torch.uint8, device=q_nope.device)
+        workspace = torch.zeros((verify_workspace_bytes(dims, T, L),), dtype=torch.uint8, device=q_nope.device)
     lse_ptr = None if lse is None else _ptr(lse, torch.float32, "lse")
     rc = kdv_verify_mla_attn(dims, bf(q_nope, "q_nope"), bf(q_rope, "q_rope"), bf(w_uk, "w_uk"), bf(w_uv, "w_uv"),
                              bf(c_kv, "c_kv"), bf(k_pe, "k_pe"), c_kv.shape[0] if pool_slots is None else pool_slots,
@@ -344,7 +364,7 @@ def prefix_mla_attn(dims: KdvMlaDims, q_nope, q_rope, w_uk, w_uv, c_kv, k_pe, pa
         n = kdv_prefix_workspace_bytes(dims, T, L)
         if n == 0:
             raise KdvError(KDV_ERR_SHAPE, "kdv_prefix_workspace_bytes")
-        workspace = torch.empty((n,), dtype=torch.uint8, device=q_nope.device)
+        workspace = torch.zeros((n,), dtype=torch.uint8, device=q_nope.device)
     rc = kdv_prefix_mla_attn(dims, bf(q_nope, "q_nope"), bf(q_rope, "q_rope"), bf(w_uk, "w_uk"), bf(w_uv, "w_uv"),
                              bf(c_kv, "c_kv"), bf(k_pe, "k_pe"), c_kv.shape[0] if pool_slots is None else pool_slots,
                              _ptr(page_table, torch.int32, "page_table"), L, T, bf(out, "out"),
@@ -418,7 +438,7 @@ def verify_mla_attn_batch(dims: KdvMlaDims, q_nope, q_rope, w_uk, w_uv, c_kv, k_
     if out is None:
         out = torch.empty((n_nodes, H, dims.v_head_dim), dtype=torch.bfloat16, device=q_nope.device)
     if workspace is None:
-        workspace = torch.empty((verify_batch_workspace_bytes(dims, Ls, Ts),), dtype=torch.uint8,
+        workspace = torch.zeros((verify_batch_workspace_bytes(dims, Ls, Ts),), dtype=torch.uint8,
                                 device=q_nope.device)
     la, lp = _host_i32(Ls)
     ta, tp = _host_i32(Ts)
@@ -454,7 +474,7 @@ def verify_mla_attn_tree(dims: KdvMlaDims, q_nope, q_rope, w_uk, w_uv, c_kv, k_p
     if out is None:
         out = torch.empty((T, H, dims.v_head_dim), dtype=torch.bfloat16, device=dev)
     if workspace is None:
-        workspace = torch.empty((verify_workspace_bytes(dims, T, L),), dtype=torch.uint8, device=dev)
+        workspace = torch.zeros((verify_workspace_bytes(dims, T, L),), dtype=torch.uint8, device=dev)
     lse_ptr = None if lse is None else _ptr(lse, torch.float32, "lse")
     rc = kdv_verify_mla_attn_tree(dims, bf(q_nope, "q_nope"), bf(q_rope, "q_rope"), bf(w_uk, "w_uk"),
                                   bf(w_uv, "w_uv"), bf(c_kv, "c_kv"), bf(k_pe, "k_pe"), c_kv.shape[0],

@@ -33,7 +33,7 @@ def _single(inp, pool_slots):
     dev = si.to_device(inp)
     mask, _ = kdv.build_tree_mask(dev["parent"])
     dims = kdv.make_dims(**inp.dims())
-    ws = torch.empty((kdv.verify_workspace_bytes(dims, inp.T, inp.L),), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros((kdv.verify_workspace_bytes(dims, inp.T, inp.L),), dtype=torch.uint8, device="cuda")
     ws[:4].fill_(0x55)  # neither status value
     lse = torch.zeros((inp.T, inp.H), dtype=torch.float32, device="cuda")
     out, lse = kdv.verify_mla_attn(dims, dev["q_nope"], dev["q_rope"], dev["w_uk"], dev["w_uv"], dev["c_kv"],
@@ -65,7 +65,7 @@ def test_prefix_and_batch_checked(debug_on):
     dev = si.to_device(inp)
     dims = kdv.make_dims(**inp.dims())
     n = kdv.kdv_prefix_workspace_bytes(dims, inp.T, inp.L)
-    ws = torch.empty((n,), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros((n,), dtype=torch.uint8, device="cuda")
     pt = dev["page_table"][:inp.L].contiguous()
     out, lse = kdv.prefix_mla_attn(dims, dev["q_nope"], dev["q_rope"], dev["w_uk"], dev["w_uv"], dev["c_kv"],
                                    dev["k_pe"], pt, inp.L, workspace=ws, pool_slots=inp.L - 1)
@@ -86,7 +86,7 @@ def test_prefix_and_batch_checked(debug_on):
     args = (bdims, b16([r.q_nope for r in reqs]), b16([r.q_rope for r in reqs]), b16([reqs[0].w_uk]),
             b16([reqs[0].w_uv]), b16([reqs[0].c_kv]), b16([reqs[0].k_pe]), torch.from_numpy(table).cuda(),
             [r.L for r in reqs], [r.T for r in reqs], mask)
-    ws = torch.empty((kdv.verify_batch_workspace_bytes(bdims, args[8], args[9]),), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros((kdv.verify_batch_workspace_bytes(bdims, args[8], args[9]),), dtype=torch.uint8, device="cuda")
     out, _ = kdv.verify_mla_attn_batch(*args, workspace=ws, pool_slots=bad_pool)
     torch.cuda.synchronize()
     assert kdv.debug_status(ws) == kdv.KDV_ERR_PAGE and torch.isnan(out.float()).all()

@@ -67,7 +67,7 @@ def test_tree_verify_graph_replays():
     lse = torch.empty((T, H), dtype=torch.float32, device="cuda")
     mask = torch.empty((T, (T + 31) // 32), dtype=torch.int32, device="cuda")
     status = torch.empty((1,), dtype=torch.int32, device="cuda")
-    ws = torch.empty((kdv.verify_workspace_bytes(dims, T, inp.L),), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros((kdv.verify_workspace_bytes(dims, T, inp.L),), dtype=torch.uint8, device="cuda")
 
     def call():
         kdv.verify_mla_attn_tree(dims, dev["q_nope"], dev["q_rope"], dev["w_uk"], dev["w_uv"], dev["c_kv"],
@@ -99,7 +99,7 @@ def test_batched_verify_graph_replays():
     n, H, Dv = sum(Ts), r0.H, r0.dims()["v_head_dim"]
     out = torch.empty((n, H, Dv), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((n, H), dtype=torch.float32, device="cuda")
-    ws = torch.empty((kdv.verify_batch_workspace_bytes(dims, Ls, Ts),), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros((kdv.verify_batch_workspace_bytes(dims, Ls, Ts),), dtype=torch.uint8, device="cuda")
     # the other call: one request of the same batch through the single-request path, into its own buffers
     one = si.to_device(reqs[3])
 

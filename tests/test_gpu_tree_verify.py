@@ -76,7 +76,7 @@ def test_tree_call_without_status():
     T, H = inp.T, inp.H
     mask = torch.empty((T, 1), dtype=torch.int32, device="cuda")
     out = torch.empty((T, H, inp.Dv), dtype=torch.bfloat16, device="cuda")
-    ws = torch.empty((kdv.verify_workspace_bytes(dims, T, inp.L),), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros((kdv.verify_workspace_bytes(dims, T, inp.L),), dtype=torch.uint8, device="cuda")
     rc = kdv.kdv_verify_mla_attn_tree(dims, *[dev[k].data_ptr() for k in ("q_nope", "q_rope", "w_uk", "w_uv", "c_kv",
                                                                          "k_pe")],
                                       inp.pool_slots, dev["page_table"].data_ptr(), inp.L, T,

@@ -53,7 +53,7 @@ def _run_both(inp):
                                                  mask.data_ptr(), out.data_ptr(), lse.data_ptr(), s)
         else:
             n = kdv.kdv_verify_workspace_bytes(dims, T, inp.L)
-            ws = torch.empty((n,), dtype=torch.uint8, device="cuda")
+            ws = torch.zeros((n,), dtype=torch.uint8, device="cuda")
             rc = kdv.kdv_verify_mla_attn(dims, *ptrs, inp.pool_slots, dev["page_table"].data_ptr(), inp.L, T,
                                          mask.data_ptr(), out.data_ptr(), lse.data_ptr(), ws.data_ptr(), n, s)
         assert rc == kdv.KDV_OK, kdv.kdv_status_string(rc)
