@@ -59,3 +59,40 @@ def test_lds_dma_blocks_have_no_outputs_and_set_m0_first(name, lines, ops):
     assert i >= 2 and lines[0].startswith("s_mov_b32 m0") and re.fullmatch(r"s_nop\s+\d+", lines[i - 1]), \
         f"{name}: M0 write and one wait state must precede the DMA: {lines}"
     assert '"m0"' in ops, f"{name}: M0 must be listed as clobbered"
+
+
+# ------------------------------------------------------------------ counted wait in the split-KV prologue
+# The prologue of a split-KV segment issues, per wave, one LDS-DMA load of the first tile's page-table slice and
+# then its share of the query tile's DMA instructions (instruction ins = wave + 4k while ins * 64 lanes < the
+# tile's 16-byte chunks), and waits with `s_waitcnt vmcnt(QINS / 4)` before reading the slice.  Loads complete in
+# issue order, so the slice has landed once at most QINS / 4 loads are outstanding -- provided every wave issued
+# at least QINS / 4 query instructions after it.  Checked for both compiled shapes (the source's constants are
+# read from the text so that a change there shows up here).
+def _segment_prologue_text():
+    with open(os.path.join(CSRC, "verify.hip")) as f:
+        text = f.read()
+    start = text.index("void splitkv_segment(")
+    return text[start:text.index("seg_body<R, DR>(", start)]
+
+
+def test_prologue_counted_wait_is_where_the_argument_needs_it():
+    t = _segment_prologue_text()
+    pt = t.index("dma4_lane_addr(page_table")           # the page-table slice load ...
+    q = t.index("dma16_lane_addr(q_cat")                 # ... then the query-tile loads ...
+    w = t.index("wait_vmem_below<QINS / 4>();")          # ... then the counted wait ...
+    r = t.index("const int slot0 = pt_s[lane];")         # ... then the read of the slice
+    assert pt < q < w < r
+    assert "constexpr int QINS = (M_TILE * (DQ / 8) + 63) / 64;" in t
+    assert "const int ins = wave + 4 * k, pos = ins * 64 + lane;" in t
+    assert "if (ins * 64 < M_TILE * QC) {" in t
+
+
+@pytest.mark.parametrize("R,DR", [(512, 64), (64, 16)])
+def test_prologue_counted_wait_covers_the_page_table_slice(R, DR):
+    M_TILE, waves = 64, 4
+    QC = (R + DR) // 8                       # 16-byte chunks of a query row
+    QINS = (M_TILE * QC + 63) // 64          # query-tile DMA instructions of the workgroup
+    QN = (M_TILE * QC + 255) // 256          # loop trips per wave
+    issued = [sum(1 for k in range(QN) if (w + 4 * k) * 64 < M_TILE * QC) for w in range(waves)]
+    assert sum(issued) == QINS
+    assert min(issued) >= QINS // 4, (issued, QINS // 4)

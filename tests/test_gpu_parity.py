@@ -4,7 +4,8 @@ Mask: bit-exact.  Outputs: tests/parity.py (max|diff| <= 2e-2 relative to max(1,
 max|ref|); lse within the bf16-rounding bound derived in tests/parity.py.  Sizes span several 64-row KV tiles with ragged tails, every tree-size edge
 (1, 32/33 -> two mask words, 64 = maximum), head counts that leave a partial 64-row query tile, forced
 split counts, the full Kimi-shape workload (64 heads, 15 nodes, 5553-token prefix) in the launch
-configuration the benchmark times, the context sweep, a 200k-token prefix scattered over a 262144-slot
+configuration the benchmark times, the context sweep (also over seeds 0-9 with unit and peaked scores, and a
+one-bit mask mutation caught at 16384 tokens), a 200k-token prefix scattered over a 262144-slot
 pool with unused slots poisoned to NaN (sampled heads), and one layer of the 8-head / 32-node /
 131072-token verify step.
 """
@@ -16,7 +17,7 @@ import torch
 
 import oracle
 import synth_inputs as si
-from tests.parity import lse_passes, lse_tolerance, out_errors, out_passes
+from tests.parity import lse_passes, lse_tolerance, out_errors, out_passes, out_passes_qlat
 
 pytestmark = pytest.mark.gpu
 
@@ -71,7 +72,7 @@ def check(inp, heads=None, **kw):
     got, glse = run_gpu(inp, **kw)
     ref, rlse = oracle.verify_inputs(inp, heads=heads)
     sel = slice(None) if heads is None else (slice(None), list(heads))
-    ok, err = out_passes(got[sel], ref[sel])
+    ok, err = out_passes_qlat(got[sel], ref[sel], inp, heads)
     assert ok, f"output parity failed: {err}"
     if glse is not None:
         tol = lse_tolerance(inp, heads)
@@ -146,6 +147,19 @@ def test_kimi_small_prefix(L, T):
 def test_context_sweep(L, T):
     seed = [13, 1663, 3333, 5553, 16384].index(L) * 2 + (T == 15)
     check(si.kimi(L=L, T=T, seed=seed, dist="literal"))
+
+
+# The context sweep over seeds 0-9 with the unit and peaked score distributions.  Above 13 tokens the oracle runs
+# on four sampled heads (the kernel computes all 64; a head's rows span every query tile boundary class).
+SWEEP_HEADS = (0, 21, 42, 63)
+
+
+@pytest.mark.parametrize("seed", range(10))
+@pytest.mark.parametrize("dist", ["unit", "peak4"])
+@pytest.mark.parametrize("L", [13, 1663, 3333, 5553, 16384])
+@pytest.mark.parametrize("T", [9, 15])
+def test_context_sweep_seeds(L, T, dist, seed):
+    check(si.kimi(L=L, T=T, seed=100 + seed, dist=dist), heads=None if L == 13 else SWEEP_HEADS)
 
 
 @pytest.mark.parametrize("T", [1, 2, 31, 32, 33, 64])
@@ -251,6 +265,43 @@ def test_mutated_mask_fails_parity(mutation):
     assert not ok, f"mutated mask passed: {err}"
     good, _ = run_gpu(inp)
     assert out_passes(good, ref)[0]
+
+
+def _plant_peak(inp, t, j, h=0, alpha=16.0):
+    """Make tree key j score about alpha above every prefix key for node t in head h: its latent and rotary rows
+    become alpha times node t's unit-normalised absorbed query (the same modified inputs go to the oracle)."""
+    qlat = inp.f32("q_nope")[t, h].astype(np.float64) @ inp.f32("w_uk")[h].astype(np.float64)
+    qr = inp.f32("q_rope")[t, h].astype(np.float64)
+    norm = np.sqrt(qlat @ qlat + qr @ qr)
+    row = inp.page_table[inp.L + j]
+    inp.c_kv[row] = si.f32_to_bf16_bits((alpha * qlat / norm).astype(np.float32))
+    inp.k_pe[row] = si.f32_to_bf16_bits((alpha * qr / norm).astype(np.float32))
+    inp._f32.clear()
+
+
+@pytest.mark.parametrize("mutation", ["drop_root_of_deepest", "add_non_ancestor"])
+def test_mutated_mask_fails_parity_long_context(mutation):
+    """A one-bit mask error is caught at 16384 prefix tokens too, where one tree key is a small share of the
+    softmax mass: the key the mutation concerns is made to dominate the affected node's scores in head 0."""
+    inp = si.kimi(L=16384, T=15, seed=12, dist="unit")
+    mask, _ = oracle.tree_mask(inp.parent)
+    depth = [len(oracle.ancestor_path(inp.parent, t)) for t in range(inp.T)]
+    t = int(np.argmax(depth))
+    anc = set(oracle.ancestor_path(inp.parent, t))
+    bad = mask.copy()
+    if mutation == "drop_root_of_deepest":
+        j = 0
+        bad[t, 0] &= ~np.uint32(1)
+    else:
+        j = next(j for j in range(inp.T) if j not in anc)
+        bad[t, 0] |= np.uint32(1) << np.uint32(j)
+    _plant_peak(inp, t, j)
+    ref, _ = oracle.verify_inputs(inp, heads=[0])
+    got, _ = run_gpu(inp, mask_np=bad)
+    ok, err = out_passes(got[:, [0]], ref[:, [0]])
+    assert not ok, f"mutated mask passed: {err}"
+    good, _ = run_gpu(inp)
+    assert out_passes(good[:, [0]], ref[:, [0]])[0]
 
 
 def test_invalid_tree_reports_status():

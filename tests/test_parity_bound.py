@@ -6,12 +6,15 @@
 - an lse off by twice the bound fails, and the device's own rounding of q_lat, emulated here on the CPU
   (float32 accumulation, bf16 round to nearest even, exact scores), passes.
 """
+import copy
+
 import numpy as np
 import pytest
 import torch
 
 import oracle
 import synth_inputs as si
+from tests import parity
 from tests.parity import LSE_SLACK, bf16_round_f64, lse_passes, lse_tolerance
 
 
@@ -60,3 +63,49 @@ def test_emulated_device_rounding_passes_and_planted_error_fails(dist):
     bad = emu.copy()
     bad[4, 1] = ref[4, 1] + 2 * tol[4, 1]
     assert not lse_passes(bad, ref, tol)[0]
+
+
+# ------------------------------------------------------------------ output effect of the q_lat rounding
+def _scaled_identity_inputs(scale_w: float, seed: int = 5):
+    """Oracle-only inputs (Dn = R) whose W_UK[h] is scale_w times the identity, so that q_lat = scale_w q_nope."""
+    inp = si.make_inputs(num_heads=3, qk_nope_dim=64, qk_rope_dim=16, kv_lora_rank=64, v_head_dim=32, L=40, T=7,
+                         seed=seed, dist="peak4")
+    w = np.zeros((inp.H, inp.Dn, inp.R), dtype=np.float32)
+    for h in range(inp.H):
+        w[h] = scale_w * np.eye(inp.Dn, inp.R, dtype=np.float32)
+    inp.w_uk = si.f32_to_bf16_bits(w)
+    inp._f32.clear()
+    return inp
+
+
+def test_qlat_output_effect_matches_the_oracle_on_rounded_queries():
+    # q_lat = 3 q_nope is not a bfloat16 value in general; the same oracle on W_UK = I and q_nope = bf16(3 q_nope)
+    # sees exactly the rounded q_lat, so the difference of the two oracle outputs is the effect to predict.
+    inp = _scaled_identity_inputs(3.0)
+    rounded = copy.deepcopy(inp)
+    q3 = 3.0 * inp.f32("q_nope").astype(np.float64)
+    rounded.q_nope = si.f32_to_bf16_bits(bf16_round_f64(q3)[0].astype(np.float32))
+    rounded.w_uk = si.f32_to_bf16_bits(np.stack([np.eye(inp.Dn, inp.R, dtype=np.float32)] * inp.H))
+    rounded._f32.clear()
+    base, _ = oracle.verify_inputs(inp)
+    moved, _ = oracle.verify_inputs(rounded)
+    eff = parity.qlat_output_effect(inp)
+    assert np.abs(moved - base).max() > 1e-4            # the rounding matters on these inputs
+    np.testing.assert_allclose(eff, moved - base, rtol=0, atol=1e-12)
+
+
+def test_qlat_output_effect_vanishes_for_representable_queries():
+    inp = _scaled_identity_inputs(1.0)                   # q_lat = q_nope: already bfloat16
+    assert np.abs(parity.qlat_output_effect(inp)).max() == 0.0
+
+
+def test_qlat_criterion_still_rejects_wrong_outputs():
+    inp = si.kimi(L=300, T=9, seed=108, dist="peak4")
+    heads = (0, 63)
+    ref, _ = oracle.verify_inputs(inp, heads=heads)
+    sel = (slice(None), list(heads))
+    bad = ref.copy()
+    bad[4, 63] *= 1.05
+    assert not parity.out_passes_qlat(bad[sel], ref[sel], inp, heads)[0]
+    assert not parity.out_passes_qlat(np.zeros_like(ref[sel]), ref[sel], inp, heads)[0]
+    assert parity.out_passes_qlat(ref[sel], ref[sel], inp, heads)[0]
