@@ -53,10 +53,9 @@ KERNEL_SOURCES = ("speculative_decoding_tree_parent_amd/csrc/verify.hip",
                   "speculative_decoding_tree_parent_amd/csrc/common.h",
                   "speculative_decoding_tree_parent_amd/csrc/tree_mask.h",
                   "speculative_decoding_tree_parent_amd/csrc/tree.hip")
-KERNELS = ("tree_mask_kernel", "verify_fused_kernel", "q_absorb_kernel", "splitkv_kernel", "combine_up_kernel",
+KERNELS = ("tree_mask_kernel", "q_absorb_kernel", "splitkv_kernel", "combine_up_kernel",
            "tree_accept_kernel", "draft_tree_kernel", "merge_states_kernel")
-FUSED_NAMES = ["verify_fused"]
-SPLIT_NAMES = ["q_absorb", "splitkv", "combine_up"]
+KERNEL_NAMES = ["q_absorb", "splitkv", "combine_up"]
 
 
 def log(msg):
@@ -222,8 +221,9 @@ def measure(S, args, torch, kdv, dev, hip, stream, sh, note, K, Wm, full=True):
     ws_bytes = kdv.verify_workspace_bytes(dims, T, L)
     ws_t = torch.zeros((ws_bytes,), dtype=torch.uint8, device=dev)
     splits = kdv.kdv_verify_num_splits(dims, T, L)
+    names = KERNEL_NAMES
     nk = kdv.kdv_verify_kernel_count(dims, T, L)
-    names = FUSED_NAMES if nk == 1 else SPLIT_NAMES
+    assert nk == len(names)
     wk = work(H, Dn, Dr, R, Dv, L, T, S.parent_np)
 
     def ptrs(t):
@@ -521,8 +521,8 @@ def run(args, torch, si, kdv, dev, hip, stream, sh):
 
     mfma_peak = measured_mfma_peak(torch, kdv, dev, hip, sh, note)
     # the dominant kernel: the single launch (all of the call's work) or, with three launches, the split-KV pass
-    dom = "verify_fused" if "verify_fused" in kern_us else "splitkv"
-    dom_flops = wk["flops"] if dom == "verify_fused" else wk["flops_splitkv"]
+    dom = "splitkv"
+    dom_flops = wk["flops_splitkv"]
     sk_tflops = dom_flops / (kern_us[dom] * 1e-6) / 1e12
 
     result = {
@@ -916,7 +916,7 @@ def summarize_profile(d, workload):
     for k, v in eager.items():
         lines.append(f"| {k} | {v:.2f} | {ev.get(k, float('nan')):.2f} |")
     # step span in the timed cold replay (includes gaps between kernels): q_absorb starts every layer
-    first = "verify_fused_kernel" if "verify_fused_kernel" in durs else "q_absorb_kernel"
+    first = "q_absorb_kernel"
     tm = sorted(durs[first])
     ph, _ = _phases(bench, first)
     a, b = ph[f"{workload}: graph cold, timed replay"]
@@ -956,7 +956,7 @@ def summarize_profile(d, workload):
              f"(`--steps {fb['steps']} --warmup {fb['warmup']}`):", "",
              "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | fetched MB | written MB |", "|---|---|---|---|---|"]
     rec = None
-    dom_kernel = "verify_fused_kernel" if "verify_fused_kernel" in fetch else "splitkv_kernel"
+    dom_kernel = "splitkv_kernel"
     for k in KERNELS:
         if k not in fetch or k not in write:
             continue

@@ -62,14 +62,13 @@ typedef enum kdv_status {
   KDV_ERR_ALIGN = -4,     /* a bf16/fp32 array or the workspace is not 16-byte aligned            */
   KDV_ERR_WORKSPACE = -5, /* workspace smaller than kdv_verify_workspace_bytes()                  */
   KDV_ERR_HIP = -6,       /* a HIP launch or query failed                                         */
-  KDV_ERR_PAGE = -7,      /* a page-table entry outside [0, pool_slots) (device side, KDV_DEBUG)  */
-  KDV_ERR_TIMEOUT = -8    /* a wait inside the single-launch verify kernel gave up (device side)  */
+  KDV_ERR_PAGE = -7       /* a page-table entry outside [0, pool_slots) (device side, KDV_DEBUG)  */
 } kdv_status;
 
 #define KDV_MAX_TREE_NODES 64
 #define KDV_MAX_BATCH 16           /* requests per kdv_verify_mla_attn_batch call */
 #define KDV_MAX_DRAFT_ENTRIES 4096 /* block x K entries of the drafter's top-K table */
-#define KDV_WS_HEADER 65536        /* bytes at the start of every verify workspace: status words and counters */
+#define KDV_WS_HEADER 256          /* bytes at the start of every verify workspace: the KDV_DEBUG status */
 #define KDV_NOALLOC_SCRATCH_BYTES (32u << 20) /* device array behind kdv_verify_mla_attn_noalloc (32 MiB) */
 
 /* Best-first construction of the draft tree on the device ("The Architecture of Diagnosis...", section
@@ -164,19 +163,11 @@ size_t kdv_verify_workspace_bytes(const kdv_mla_dims* d, int32_t T, int32_t L);
  *   lse        : device fp32 [T][H], nullable; natural-log sum of exp of the scaled visible scores,
  *                for merging with attention computed elsewhere.
  *   workspace  : device scratch of workspace_bytes >= kdv_verify_workspace_bytes(d, T, L); 16-byte
- *                aligned.  Its first KDV_WS_HEADER bytes hold two status words and the counters that order
- *                the tasks of the single-launch kernel: they must be zero before the workspace's first use
- *                (clear them once after allocating it); every call leaves the counters zero.  The rest is
- *                undefined after a call.  int32 at offset 0: the KDV_DEBUG page-table status (above); at
- *                offset 4: KDV_OK, or KDV_ERR_TIMEOUT if a wait inside the single-launch kernel gave up (its
- *                results are then wrong; no such wait runs for longer than the slowest split of the call in a
- *                correct run, and each gives up after about a second).  Calls that share a workspace must be
- *                ordered on one stream.
- * The call is one kernel launch (kdv_verify_kernel_count) whenever its task counters fit in the header, which
- * every default split plan does: the query absorption, the split-KV pass and the split combine with the W_UV
- * up-projection run as tasks of one grid, ordered by those counters; each workgroup waits only for tasks that
- * running workgroups hold, so the launch needs no co-residency guarantee.  Otherwise (a very large KDV_SPLITS)
- * it is three launches of the same steps.
+ *                aligned; no initial contents are needed.  After a call its int32 at offset 0 holds the
+ *                KDV_DEBUG page-table status (above) when that check ran; the rest is undefined.  Calls that
+ *                share a workspace must be ordered on one stream.
+ * The call is three kernel launches on the stream: the query absorption, the split-KV pass, and the split
+ * combine with the W_UV up-projection.
  * Returns KDV_OK or a negative kdv_status (nothing enqueued on error). */
 int kdv_verify_mla_attn(const kdv_mla_dims* d, const uint16_t* q_nope, const uint16_t* q_rope,
                         const uint16_t* w_uk, const uint16_t* w_uv, const uint16_t* c_kv, const uint16_t* k_pe,
@@ -212,8 +203,8 @@ int kdv_verify_mla_attn_tree(const kdv_mla_dims* d, const uint16_t* q_nope, cons
 
 /* Same computation as kdv_verify_mla_attn, for measurement: `events` points to 2 * kdv_verify_kernel_count(d, T, L)
  * hipEvent_t created by the caller.  events[2k] and events[2k+1] receive the start and end timestamps of kernel k
- * as the hardware dispatches it (one kernel: the single launch; three: q absorption, split-KV pass, split combine
- * with the W_UV up-projection), so hipEventElapsedTime gives each kernel's device time.  Errors as
+ * as the hardware dispatches it (q absorption, split-KV pass, split combine with the W_UV up-projection), so
+ * hipEventElapsedTime gives each kernel's device time.  Errors as
  * kdv_verify_mla_attn, plus KDV_ERR_NULL if events is NULL. */
 int kdv_verify_mla_attn_profiled(const kdv_mla_dims* d, const uint16_t* q_nope, const uint16_t* q_rope,
                                  const uint16_t* w_uk, const uint16_t* w_uv, const uint16_t* c_kv,
@@ -288,9 +279,8 @@ int kdv_merge_attn_states(const uint16_t* out_a, const float* lse_a, const uint1
  * (diagnostic; 0 if unsupported). */
 int32_t kdv_verify_num_splits(const kdv_mla_dims* d, int32_t T, int32_t L);
 
-/* Number of kernels one kdv_verify_mla_attn call launches for these arguments on the current device: 1 (the
- * single launch) or 3 (absorption, split-KV, combine; only with a very large KDV_SPLITS); 0 if unsupported.
- * The batched call always launches 3. */
+/* Number of kernels one kdv_verify_mla_attn call launches for these arguments: 3 (absorption, split-KV,
+ * combine); 0 if unsupported.  The batched call launches 3 as well. */
 int32_t kdv_verify_kernel_count(const kdv_mla_dims* d, int32_t T, int32_t L);
 
 /* DIAGNOSTIC ONLY, not part of the attention path: a measurement aid for the benchmark.  Launches `blocks` workgroups of 256 threads in which every wave issues `iters`

@@ -25,8 +25,7 @@ KDV_ERR_ALIGN = -4
 KDV_ERR_WORKSPACE = -5
 KDV_ERR_HIP = -6
 KDV_ERR_PAGE = -7
-KDV_ERR_TIMEOUT = -8
-KDV_WS_HEADER = 65536
+KDV_WS_HEADER = 256
 KDV_NOALLOC_SCRATCH_BYTES = 32 << 20
 KDV_MAX_TREE_NODES = 64
 KDV_MAX_DRAFT_ENTRIES = 4096
@@ -240,16 +239,9 @@ def _bf16_ptr(t, what: str) -> int:
 
 
 def new_workspace(nbytes: int, device) -> "torch.Tensor":
-    """A device workspace of nbytes, zeroed (its first KDV_WS_HEADER bytes must be zero before the first call)."""
+    """A device workspace of nbytes (zeroed, so that reading the KDV_DEBUG status word before any check is defined)."""
     import torch
     return torch.zeros((nbytes,), dtype=torch.uint8, device=device)
-
-
-def wait_status(workspace) -> int:
-    """KDV_OK, or KDV_ERR_TIMEOUT if a wait inside the last single-launch verify call on this workspace gave up.
-    Reads the device (synchronising with it)."""
-    import torch
-    return int(workspace[4:8].view(torch.int32).item())
 
 
 def debug_status(workspace) -> int:

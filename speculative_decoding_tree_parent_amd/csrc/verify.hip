@@ -403,8 +403,7 @@ __device__ __forceinline__ void tile_compute(const char* tile, const bf16x8 (&q)
   }
 }
 
-// The part of a split-KV segment after its prologue, shared by the split-KV kernel and the fused kernel: the
-// query tile (staged in LDS at qbuf) into registers, the loop over the segment's KV tiles (the first one already
+// The part of a split-KV segment after its prologue: the query tile (staged in LDS at qbuf) into registers, the loop over the segment's KV tiles (the first one already
 // gathered into the first KV buffer, the next tile's page-table slice in slot_v), and the partial (O / l, max,
 // sum) of the segment into partial slot `split`.  All threads of the workgroup call it together.
 template <int R, int DR>
@@ -1000,355 +999,6 @@ __global__ __launch_bounds__(COMB_THREADS) void combine_up_kernel(const uint16_t
 }
 
 
-// ------------------------------------------------------------------------------------------------ fused kernel
-// One launch for a single request: the query absorption, the split-KV pass and the split combine with the W_UV
-// up-projection, as tasks of one grid, with their order kept by counters in the workspace header (all zero between
-// calls; the last workgroup to finish zeroes them again):
-//   - absorb tasks (head, 128 latent columns, 32 nodes; plus the ancestor mask when the call builds it) are claimed
-//     from a counter by any workgroup; a workgroup waits for all of them to be done only after none is left to
-//     claim, so it waits only for tasks that running workgroups are working on;
-//   - split task b (a (KV split, query tile) pair, placed over the XCDs as by the split-KV kernel) is workgroup b's:
-//     it claims it when it starts, gathers the first KV tile's page-table slice before absorbing and the tile itself
-//     right after, and runs it once every absorb task is done;
-//   - combine task b (a head and a block of RT nodes, as by the combine kernel) is also workgroup b's; before it
-//     waits for the splits of a query tile it needs, it claims and runs any of them no workgroup has claimed yet,
-//     so this wait too is only for running workgroups.  No workgroup needs another to be resident at the same time.
-// A wait that exceeds WAIT_TICKS of the 100 MHz real-time counter gives up, marks the call failed (the int32 at
-// offset 4 of the workspace reads KDV_ERR_TIMEOUT after it) and goes on, so that every workgroup ends.
-struct FusedCounters {
-  int absorb_next;  // next absorb task to claim
-  int absorb_done;  // absorb tasks finished
-  int exit_count;   // workgroups finished
-  int error;        // a wait gave up
-  int slots[1];     // split-task claims [split_blocks], then splits done per query tile [m_tiles]
-};
-constexpr int WS_COUNTERS = 256;  // byte offset of the counters in the workspace header
-constexpr int COUNTER_SLOTS = (KDV_WS_HEADER - WS_COUNTERS) / 4 - 4;
-constexpr uint64_t WAIT_TICKS = 1ull << 27;  // ~1.3 s
-
-struct FusedArgs {
-  const uint16_t* q_nope;
-  const uint16_t* q_rope;
-  const uint16_t* w_uk;
-  const uint16_t* w_uv;
-  const uint16_t* c_kv;
-  const uint16_t* k_pe;
-  const int32_t* page_table;
-  const uint32_t* mask;    // read by the split tasks (written by the mask task first when parent != nullptr)
-  const int32_t* parent;   // nullptr, or the tree whose ancestor mask the call builds into `mask`
-  int32_t* tree_status;
-  uint16_t* out;
-  float* lse;
-  uint16_t* q_cat;
-  uint16_t* part_o;
-  float2* part_ml;
-  int32_t* hdr;            // workspace header: [0] KDV_DEBUG page-table status, [1] wait status of the last call
-  FusedCounters* cnt;
-  const int32_t* dbg;      // nullptr, or hdr (KDV_DEBUG)
-  ReqArgs rq;
-  int H;
-  float scale_log2;
-  int split_blocks, comb_blocks, n_abs_q, n_abs;
-};
-
-// (split, query tile) of split-KV block b, as splitkv_kernel places them; false for a padding block.
-__device__ __forceinline__ bool split_task_of(const ReqArgs& rq, int b, int& split, int& mt) {
-  const int xcd = b % NUM_XCD, j = b / NUM_XCD;
-  const int kl = xcd * rq.lin + j;
-  split = rq.lin > 0 ? kl / rq.m_tiles : (xcd - rq.xoff + NUM_XCD) % NUM_XCD + NUM_XCD * (j / rq.m_tiles);
-  mt = rq.lin > 0 ? kl % rq.m_tiles : j % rq.m_tiles;
-  return split < rq.splits;
-}
-// The block of (split, query tile): the inverse of split_task_of.
-__device__ __forceinline__ int split_task_block(const ReqArgs& rq, int split, int mt) {
-  if (rq.lin > 0) {
-    const int kl = split * rq.m_tiles + mt;
-    return (kl % rq.lin) * NUM_XCD + kl / rq.lin;
-  }
-  return ((split / NUM_XCD) * rq.m_tiles + mt) * NUM_XCD + (split % NUM_XCD + rq.xoff) % NUM_XCD;
-}
-
-// Value of thread 0's v in every thread (two barriers: the slot may be reused right after).  Read through
-// readfirstlane so that the compiler knows it is wave-uniform (it is): branches on it stay scalar.
-__device__ __forceinline__ int from_thread0(int v, int* slot) {
-  if (threadIdx.x == 0) *slot = v;
-  __syncthreads();
-  const int r = __builtin_amdgcn_readfirstlane(*slot);
-  __syncthreads();
-  return r;
-}
-
-__device__ __forceinline__ int load_relaxed(const int* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Thread 0: wait until *p >= target (bounded), then an agent-scope acquire.  Returns false if it gave up.
-__device__ __forceinline__ bool wait_at_least(const int* p, int target, FusedCounters* cnt) {
-  bool ok = true;
-  if (load_relaxed(p) < target) {
-    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-    while (load_relaxed(p) < target) {
-      __builtin_amdgcn_s_sleep(2);
-      if (__builtin_amdgcn_s_memrealtime() - t0 > WAIT_TICKS) {
-        __hip_atomic_fetch_or(&cnt->error, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        ok = false;
-        break;
-      }
-    }
-  }
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  return ok;
-}
-
-// After every wave's stores of a task have completed (wait_vmem_all + barrier): thread 0 publishes them.
-__device__ __forceinline__ void signal_done(int* p) {
-  if (threadIdx.x == 0) __hip_atomic_fetch_add(p, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// The kernel's arguments, read through a pointer into the kernel-argument segment that each phase of the kernel
-// takes afresh: the compiler then loads a phase's arguments (scalar loads) where the phase uses them instead of
-// keeping them in registers across the split-KV loop of the phase before.
-typedef __attribute__((address_space(4))) const FusedArgs KArgs;
-__device__ __forceinline__ KArgs* fused_args() {
-  KArgs* p = (KArgs*)__builtin_amdgcn_kernarg_segment_ptr();
-  asm volatile("" : "+s"(p));
-  return p;
-}
-
-// A copy of the request's parameters (field by field: they sit in the kernel-argument address space).
-__device__ __forceinline__ ReqArgs load_req(KArgs* A) {
-  ReqArgs r;
-  r.L = A->rq.L;
-  r.T = A->rq.T;
-  r.N = A->rq.N;
-  r.node0 = A->rq.node0;
-  r.pt0 = A->rq.pt0;
-  r.mask0 = A->rq.mask0;
-  r.m_tiles = A->rq.m_tiles;
-  r.Mp = A->rq.Mp;
-  r.tiles_per_split = A->rq.tiles_per_split;
-  r.splits = A->rq.splits;
-  r.xoff = A->rq.xoff;
-  r.lin = A->rq.lin;
-  r.po = A->rq.po;
-  r.pml = A->rq.pml;
-  r.sk_base = A->rq.sk_base;
-  return r;
-}
-
-// Split task part 1: the page-table slice of its first KV tile into pt_s (this wave's 64 entries), by DMA.
-__device__ __forceinline__ void split_start(KArgs* A, int split, int* pt_s, int lane) {
-  const ReqArgs rq = load_req(A);
-  dma4_lane_addr(A->page_table + min(split * rq.tiles_per_split * KV_TILE + lane, rq.N - 1), lds_address(pt_s));
-}
-
-// Split task part 2 (the slice has landed): the first KV tile into the first KV buffer, and the next tile's slice.
-template <int R, int DR>
-__device__ __forceinline__ void split_first_tile(KArgs* A, int split, const int* pt_s, char* kvbuf, TileDma<R, DR>& dma,
-                                                 int& slot_v, int lane) {
-  const ReqArgs rq = load_req(A);
-  const int ntiles = (rq.N + KV_TILE - 1) / KV_TILE;
-  const int tile_begin = split * rq.tiles_per_split, tile_end = min(tile_begin + rq.tiles_per_split, ntiles);
-  dma.target(kvbuf, pt_s[lane]);
-#pragma unroll
-  for (int k = 0; k < TileDma<R, DR>::NK; ++k) dma.issue(k);
-  slot_v = 0;
-  if (tile_begin + 1 < tile_end) slot_v = A->page_table[min((tile_begin + 1) * KV_TILE + lane, rq.N - 1)];
-}
-
-// Split task part 3 (every absorb task done): the query tile, the KV loop, the partial, and the tile's count.
-template <int R, int DR>
-__device__ __forceinline__ void split_run(KArgs* A, int split, int mt, char* kvbuf, uint4 (*pbuf)[2][2][64],
-                                          float (*mxch)[2][32], float (*psum)[2][32], TileDma<R, DR>& dma, int slot_v,
-                                          int* tile_done) {
-  using TL = TileLayout<R, DR>;
-  constexpr int DQ = R + DR;
-  const ReqArgs rq = load_req(A);
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int H = A->H, T = rq.T, L = rq.L, N = rq.N;
-  const int ntiles = (N + KV_TILE - 1) / KV_TILE;
-  const int tile_begin = split * rq.tiles_per_split, tile_end = min(tile_begin + rq.tiles_per_split, ntiles);
-  const int wi = wave >> 1, c = lane & 31;
-  const int M = T * H, m = mt * M_TILE + wi * 32 + c;
-  const int me = min(m, M - 1), t_row = me / H, W = (T + 31) >> 5;
-  const bool tree_rows = N > L;
-  const uint32_t* mask = A->mask;
-  const uint32_t mw0 = tree_rows ? mask[t_row * W] : 0u;
-  const uint32_t mw1 = (tree_rows && W == 2) ? mask[t_row * W + 1] : 0u;
-  // the query tile into the second KV buffer, staged as the split-KV kernel's prologue stages it
-  char* qbuf = kvbuf + TL::BYTES;
-  constexpr int QC = DQ / 8, QN = (M_TILE * QC + 255) / 256;
-  const uint32_t qlds = lds_address(qbuf);
-  const uint16_t* q_cat = A->q_cat;
-#pragma unroll
-  for (int k = 0; k < QN; ++k) {
-    const int ins = wave + 4 * k, pos = ins * 64 + lane;
-    if (ins * 64 < M_TILE * QC) {
-      const int r = pos / QC, chk = qswz<QC>(r, pos % QC);
-      const int gr = min(mt * M_TILE + r, M - 1);
-      dma16_lane_addr(q_cat + (size_t)gr * DQ + chk * 8, qlds + ins * 1024);
-    }
-  }
-  wait_vmem_all();
-  __syncthreads();
-  seg_body<R, DR>(kvbuf, qbuf, pbuf, mxch, psum, dma, slot_v, A->page_table, tile_begin, tile_end, L, N, mw0, mw1,
-                  A->scale_log2, mt, split, rq.Mp, A->part_o, A->part_ml);
-  wait_vmem_all();  // this wave's partial stores are complete
-  __syncthreads();
-  signal_done(&tile_done[mt]);
-}
-
-template <int DN, int R, int DR, int DV, int RT>
-__global__ __launch_bounds__(NTHREADS, 1) void verify_fused_kernel(const FusedArgs a) {
-  using TL = TileLayout<R, DR>;
-  __shared__ __attribute__((aligned(1024))) char kvbuf[2 * TL::BYTES];
-  __shared__ uint4 pbuf[2][2][2][64];  // [row block][kv half][16-row k-step][lane]: P^T fragments (bf16)
-  __shared__ float mxch[2][2][32];     // [row block][kv half][row]: proposed reference
-  __shared__ float psum[2][2][32];     // [row block][kv half][row]: half-tile row sum
-  __shared__ int bslot[2];
-  static_assert(DN * 128 * 2 <= TL::BYTES, "the W_UK block fits in one KV buffer");
-  static_assert(DV * R * 2 + RT * (R + 8) * 2 + 4 * 64 * 10 * 4 <= 2 * TL::BYTES, "combine LDS fits in the KV buffers");
-  (void)a;  // read through fused_args()
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int b = blockIdx.x;
-  int* pt_s = reinterpret_cast<int*>(&pbuf[0][0][0][0]) + wave * 64;  // a split's first page-table slice (per wave)
-  bool failed;  // the page table failed its KDV_DEBUG check: NaN results, nothing gathered
-  {
-    KArgs* A = fused_args();
-    failed = A->dbg != nullptr && *A->dbg != KDV_OK;
-  }
-
-  // ---- phase 1: this workgroup's split task claimed and started, the absorb tasks, the split task run
-  if (!failed) {
-    KArgs* A = fused_args();
-    const ReqArgs rq = load_req(A);
-    FusedCounters* cnt = A->cnt;
-    int my_split = -1, my_mt = 0;
-    if (b < A->split_blocks && split_task_of(rq, b, my_split, my_mt)) {
-      const int won = from_thread0(
-          tid == 0 ? __hip_atomic_exchange(&cnt->slots[b], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0 : 0,
-          bslot);
-      if (!won) my_split = -1;
-    } else {
-      my_split = -1;
-    }
-    TileDma<R, DR> dma(A->c_kv, A->k_pe, wave, lane);
-    int slot_v = 0;
-    if (my_split >= 0) split_start(A, my_split, pt_s, lane);
-    bool first = my_split >= 0;  // the first KV tile is still to be gathered
-    const int T = rq.T, H = A->H;
-    for (;;) {
-      const int k = from_thread0(
-          tid == 0 ? __hip_atomic_fetch_add(&cnt->absorb_next, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0,
-          bslot);
-      if (k >= A->n_abs) break;
-      if (k == A->n_abs_q) {  // the ancestor mask of the tree (one wave)
-        if (wave == 0) build_ancestor_mask(A->parent, T, const_cast<uint32_t*>(A->mask), A->tree_status, lane);
-      } else {
-        const int nnb = (T + 31) / 32, ncb = (R + 127) / 128;
-        const int h = k / (ncb * nnb), cb = (k / nnb) % ncb, nb = k % nnb;
-        absorb_block<DN, R, DR>(A->q_nope, A->q_rope, A->w_uk, A->q_cat, T, H, h, cb, nb * 32, kvbuf + TL::BYTES);
-      }
-      wait_vmem_all();  // this wave's q_cat (or mask) stores, and the page-table slice, are complete
-      __syncthreads();
-      signal_done(&cnt->absorb_done);
-      if (first) {
-        split_first_tile<R, DR>(A, my_split, pt_s, kvbuf, dma, slot_v, lane);
-        first = false;
-      }
-    }
-    if (first) {
-      wait_vmem_all();  // the page-table slice
-      split_first_tile<R, DR>(A, my_split, pt_s, kvbuf, dma, slot_v, lane);
-    }
-    if (tid == 0) wait_at_least(&cnt->absorb_done, A->n_abs, cnt);
-    __syncthreads();
-    if (my_split >= 0) split_run<R, DR>(A, my_split, my_mt, kvbuf, pbuf, mxch, psum, dma, slot_v, cnt->slots + A->split_blocks);
-  }
-
-  // ---- phase 2: the combine task of this workgroup
-  {
-    KArgs* A = fused_args();
-    const ReqArgs rq = load_req(A);
-    const int T = rq.T, H = A->H;
-    const int TB = (T + RT - 1) / RT;
-    const int ch = (b % NUM_XCD) + NUM_XCD * ((b / NUM_XCD) / TB), ct0 = ((b / NUM_XCD) % TB) * RT;
-    if (b < A->comb_blocks && ch < H) {
-      const int nrow = min(RT, T - ct0);
-      if (failed) {
-        combine_block_nan<DV, NTHREADS>(A->out, A->lse, H, ch, ct0, nrow);
-      } else {
-        FusedCounters* cnt = A->cnt;
-        int* claims = cnt->slots;
-        int* tile_done = cnt->slots + A->split_blocks;
-        // First make sure every split of the query tiles it reads has been claimed, running any that no workgroup
-        // has claimed: lane l of wave 0 looks at split s0 + l of a tile; thread 0 claims the first open one.
-        for (int i = 0; i < nrow; ++i) {
-          const int mt = ((ct0 + i) * H + ch) / M_TILE;
-          if (i > 0 && mt == ((ct0 + i - 1) * H + ch) / M_TILE) continue;
-          for (int s0 = 0; s0 < rq.splits; s0 += 64) {
-            int p = -1;
-            if (wave == 0) {
-              const int sx = s0 + lane;
-              const bool open = sx < rq.splits && load_relaxed(&claims[split_task_block(rq, sx, mt)]) == 0;
-              const uint64_t bal = __ballot(open);
-              if (bal != 0) {
-                const int sp = s0 + __builtin_ctzll(bal);
-                p = -2;  // an open split: claim it, or look again if another workgroup got there first
-                if (lane == 0 && __hip_atomic_exchange(&claims[split_task_block(rq, sp, mt)], 1, __ATOMIC_RELAXED,
-                                                       __HIP_MEMORY_SCOPE_AGENT) == 0)
-                  p = sp;
-              }
-            }
-            p = from_thread0(p, bslot);
-            if (p == -1) continue;  // every split of this group is claimed
-            if (p >= 0) {
-              TileDma<R, DR> dma(A->c_kv, A->k_pe, wave, lane);
-              int slot_v = 0;
-              split_start(A, p, pt_s, lane);
-              wait_vmem_all();
-              split_first_tile<R, DR>(A, p, pt_s, kvbuf, dma, slot_v, lane);
-              split_run<R, DR>(A, p, mt, kvbuf, pbuf, mxch, psum, dma, slot_v, tile_done);
-            }
-            s0 -= 64;  // look at this group again
-          }
-          if (tid == 0) wait_at_least(&tile_done[mt], rq.splits, cnt);
-          __syncthreads();
-        }
-        uint16_t* o_s = reinterpret_cast<uint16_t*>(kvbuf + DV * R * 2);
-        float* gx = reinterpret_cast<float*>(kvbuf + DV * R * 2 + ((RT * (R + 8) * 2 + 15) & ~15));
-        combine_block<R, DV, RT, NTHREADS>(A->part_o, A->part_ml, rq.splits, rq.Mp, A->w_uv, A->out, A->lse, H, ch,
-                                           ct0, nrow, kvbuf, o_s, gx);
-      }
-    }
-  }
-
-  // ---- phase 3: the last workgroup to finish zeroes the counters for the next call
-  {
-    KArgs* A = fused_args();
-    FusedCounters* cnt = A->cnt;
-    __syncthreads();
-    const int last = from_thread0(
-        tid == 0 ? __hip_atomic_fetch_add(&cnt->exit_count, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
-                       (int)gridDim.x - 1
-                 : 0,
-        bslot);
-    if (last) {
-      if (tid == 0) {
-        A->hdr[1] = load_relaxed(&cnt->error) != 0 ? KDV_ERR_TIMEOUT : KDV_OK;
-        cnt->absorb_next = 0;
-        cnt->absorb_done = 0;
-        cnt->exit_count = 0;
-        cnt->error = 0;
-      }
-      const int nslots = A->split_blocks + A->rq.m_tiles;
-      for (int i = tid; i < nslots; i += NTHREADS) cnt->slots[i] = 0;
-    }
-  }
-}
-
 // ------------------------------------------------------------------------------------------------ state merge
 // Two attention results over disjoint sets of KV positions, (out_a, lse_a) and (out_b, lse_b), combine into
 // the result over their union.  With M = max(lse_a, lse_b) and w_x = e^(lse_x - M) (each part's softmax
@@ -1384,11 +1034,6 @@ __global__ __launch_bounds__(NTHREADS) void merge_states_kernel(const uint16_t* 
   }
   *reinterpret_cast<bf16x8*>(out + idx * 8) = o;
   if (lse != nullptr && idx % cpr == 0) lse[r] = lo;
-}
-
-// ------------------------------------------------------------------------------------------------ zero fill
-__global__ __launch_bounds__(NTHREADS) void zero_fill_kernel(int32_t* __restrict__ p, int n) {
-  for (int i = blockIdx.x * NTHREADS + threadIdx.x; i < n; i += gridDim.x * NTHREADS) p[i] = 0;
 }
 
 // ------------------------------------------------------------------------------------------------ page-table check
@@ -1436,7 +1081,6 @@ struct Plan {
   int H, nodes;           // heads, nodes of all requests
   int split_blocks, comb_blocks;
   int comb_rt;            // tree nodes per combine workgroup (4; 2 or 1 for a small single request, 16 for a batch)
-  bool fused;             // a single-request entry point (one launch when the counters fit)
   BatchArgs<MAX_BATCH> ba;
   size_t off_qcat, off_po, off_pml, total;   // workspace regions (after a KDV_WS_HEADER-byte header)
 };
@@ -1510,7 +1154,6 @@ static int make_plan(const kdv_mla_dims* d, int C, const int32_t* Ls, const int3
   // all of W_UV[h] (128 KB), so ten 15-node requests at 4 nodes cost 2560 gathers, at 16 nodes 640.
   const int cus_rt = cus > 0 ? cus : 256;
   p->comb_rt = 4;
-  p->fused = false;
   if (C == 1) {
     for (int rt = 1; rt < 4; rt *= 2)
       if ((int64_t)NUM_XCD * ((H + NUM_XCD - 1) / NUM_XCD) * ((Ts[0] + rt - 1) / rt) <= cus_rt) {
@@ -1618,15 +1261,6 @@ static int make_plan(const kdv_mla_dims* d, int C, const int32_t* Ls, const int3
   return KDV_OK;
 }
 
-// The single-launch kernel serves one request whose counters fit in the workspace header (every default plan;
-// not a very large forced split count), unless the call is a batch (even of one request).
-// The single-launch path is switched off: a GPU run of the test suite with it on ended in a GPU memory fault whose
-// cause has not been found (its first probe runs were correct); until it is, every call takes the three launches.
-constexpr bool kFusedEnabled = false;
-static bool fused_fits(const Plan& pl) {
-  return kFusedEnabled && pl.fused && pl.ba.n == 1 && pl.split_blocks + pl.ba.r[0].m_tiles <= COUNTER_SLOTS;
-}
-
 // Launch one kernel; with `ev` (start, stop) the events take the kernel's own start and end timestamps.
 template <typename... KArgs, typename... Args>
 static void launch_n(void (*k)(KArgs...), dim3 grid, int threads, hipStream_t st, hipEvent_t const* ev, Args... args) {
@@ -1650,38 +1284,6 @@ static void launch_all(const Plan& pl, float sm_scale, const uint16_t* q_nope, c
   uint16_t* part_o = reinterpret_cast<uint16_t*>(ws + pl.off_po);
   float2* part_ml = reinterpret_cast<float2*>(ws + pl.off_pml);
   const float scale_log2 = sm_scale * 1.44269504088896340736f;
-  if constexpr (kFusedEnabled) if (fused_fits(pl)) {
-    FusedArgs a;
-    a.q_nope = q_nope;
-    a.q_rope = q_rope;
-    a.w_uk = w_uk;
-    a.w_uv = w_uv;
-    a.c_kv = c_kv;
-    a.k_pe = k_pe;
-    a.page_table = page_table;
-    a.mask = mask;
-    a.parent = parent;
-    a.tree_status = status;
-    a.out = out;
-    a.lse = lse;
-    a.q_cat = q_cat;
-    a.part_o = part_o;
-    a.part_ml = part_ml;
-    a.hdr = reinterpret_cast<int32_t*>(ws);
-    a.cnt = reinterpret_cast<FusedCounters*>(ws + WS_COUNTERS);
-    a.dbg = dbg;
-    a.rq = pl.ba.r[0];
-    a.H = pl.H;
-    a.scale_log2 = scale_log2;
-    a.split_blocks = pl.split_blocks;
-    a.comb_blocks = pl.comb_blocks;
-    a.n_abs_q = pl.H * ((R + 127) / 128) * ((pl.nodes + 31) / 32);
-    a.n_abs = a.n_abs_q + (parent != nullptr ? 1 : 0);
-    auto k = pl.comb_rt == 1 ? verify_fused_kernel<DN, R, DR, DV, 1>
-             : pl.comb_rt == 2 ? verify_fused_kernel<DN, R, DR, DV, 2> : verify_fused_kernel<DN, R, DR, DV, 4>;
-    launch(k, dim3(std::max(pl.split_blocks, pl.comb_blocks)), st, ev, a);
-    return;
-  }
   // The query absorption is per node: the packed nodes of all requests in one grid.  With `parent` (one
   // request) an extra block builds the tree mask the split-KV kernel then reads.
   launch(q_absorb_kernel<DN, R, DR>, dim3(pl.H + (parent != nullptr ? 1 : 0), (R + 127) / 128, (pl.nodes + 31) / 32), st,
@@ -1744,8 +1346,7 @@ extern "C" size_t kdv_prefix_workspace_bytes(const kdv_mla_dims* d, int32_t T, i
 extern "C" int32_t kdv_verify_kernel_count(const kdv_mla_dims* d, int32_t T, int32_t L) {
   kdv::Plan p;
   if (kdv::make_plan(d, 1, &L, &T, &p) != KDV_OK) return 0;
-  p.fused = true;
-  return kdv::fused_fits(p) ? 1 : 3;
+  return 3;
 }
 
 extern "C" int32_t kdv_verify_num_splits(const kdv_mla_dims* d, int32_t T, int32_t L) {
@@ -1759,7 +1360,7 @@ static int verify_impl(const kdv_mla_dims* d, int32_t C, const int32_t* Ls, cons
                        const uint16_t* c_kv, const uint16_t* k_pe, int64_t pool_slots, const int32_t* page_table,
                        const uint32_t* mask, uint16_t* out, float* lse, void* workspace, size_t workspace_bytes,
                        void* stream, hipEvent_t const* ev, bool with_tree = true,
-                       const int32_t* parent = nullptr, int32_t* status = nullptr, bool batch = false) {
+                       const int32_t* parent = nullptr, int32_t* status = nullptr) {
   using namespace kdv;
   if (d == nullptr || Ls == nullptr || Ts == nullptr || q_nope == nullptr || q_rope == nullptr ||
       w_uk == nullptr || w_uv == nullptr || c_kv == nullptr || k_pe == nullptr || page_table == nullptr ||
@@ -1777,7 +1378,6 @@ static int verify_impl(const kdv_mla_dims* d, int32_t C, const int32_t* Ls, cons
   Plan pl;
   const int st = make_plan(d, C, Ls, Ts, &pl, with_tree);
   if (st != KDV_OK) return st;
-  pl.fused = !batch;
   if (workspace_bytes < pl.total) return KDV_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
@@ -1821,20 +1421,13 @@ constexpr int MAX_DEVICES = 64;
 static std::mutex scratch_mu;
 static void* scratch_ptr[MAX_DEVICES];
 
-static int scratch_of_current_device(void** out, hipStream_t stream) {
+static int scratch_of_current_device(void** out) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return KDV_ERR_HIP;
   std::lock_guard<std::mutex> lock(scratch_mu);
   if (scratch_ptr[dev] == nullptr) {
     void* p = nullptr;
     if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return KDV_ERR_HIP;
-    // the workspace header must start at zero (static device memory is zero-initialised; cleared once more here
-    // by a kernel on the call's stream, never by a memset, so that a first call under graph capture records no
-    // memset node)
-    (void)hipGetLastError();
-    hipLaunchKernelGGL(zero_fill_kernel, dim3(16), dim3(NTHREADS), 0, stream, static_cast<int32_t*>(p),
-                       KDV_WS_HEADER / 4);
-    if (hipGetLastError() != hipSuccess) return KDV_ERR_HIP;
     scratch_ptr[dev] = p;
   }
   *out = scratch_ptr[dev];
@@ -1859,7 +1452,7 @@ extern "C" int kdv_verify_mla_attn_noalloc(const kdv_mla_dims* d, const uint16_t
   if (st != KDV_OK) return st;
   if (pl.total > KDV_NOALLOC_SCRATCH_BYTES) return KDV_ERR_WORKSPACE;
   void* ws = nullptr;
-  const int sst = kdv::scratch_of_current_device(&ws, static_cast<hipStream_t>(stream));
+  const int sst = kdv::scratch_of_current_device(&ws);
   if (sst != KDV_OK) return sst;
   return verify_impl(d, 1, &L, &T, q_nope, q_rope, w_uk, w_uv, c_kv, k_pe, pool_slots, page_table, mask, out, lse,
                      ws, KDV_NOALLOC_SCRATCH_BYTES, stream, nullptr);
@@ -1894,7 +1487,7 @@ extern "C" int kdv_verify_mla_attn_batch(const kdv_mla_dims* d, int32_t C, const
                                          uint16_t* out, float* lse, void* workspace, size_t workspace_bytes,
                                          void* stream) {
   return verify_impl(d, C, L, T, q_nope, q_rope, w_uk, w_uv, c_kv, k_pe, pool_slots, page_table, mask, out, lse,
-                     workspace, workspace_bytes, stream, nullptr, true, nullptr, nullptr, /*batch=*/true);
+                     workspace, workspace_bytes, stream, nullptr);
 }
 
 extern "C" int kdv_prefix_mla_attn(const kdv_mla_dims* d, const uint16_t* q_nope, const uint16_t* q_rope,
@@ -1945,7 +1538,6 @@ extern "C" const char* kdv_status_string(int status) {
     case KDV_ERR_WORKSPACE: return "workspace smaller than kdv_verify_workspace_bytes()";
     case KDV_ERR_HIP: return "HIP launch or query failed";
     case KDV_ERR_PAGE: return "a page-table entry is outside [0, pool_slots) (KDV_DEBUG check)";
-    case KDV_ERR_TIMEOUT: return "a wait inside the single-launch verify kernel gave up";
     default: return "unknown kdv status";
   }
 }
