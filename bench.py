@@ -53,9 +53,10 @@ KERNEL_SOURCES = ("speculative_decoding_tree_parent_amd/csrc/verify.hip",
                   "speculative_decoding_tree_parent_amd/csrc/common.h",
                   "speculative_decoding_tree_parent_amd/csrc/tree_mask.h",
                   "speculative_decoding_tree_parent_amd/csrc/tree.hip")
-KERNELS = ("tree_mask_kernel", "q_absorb_kernel", "splitkv_kernel", "combine_up_kernel",
+KERNELS = ("tree_mask_kernel", "q_absorb_kernel", "splitkv_kernel", "combine_up_kernel", "short_attn_up_kernel",
            "tree_accept_kernel", "draft_tree_kernel", "merge_states_kernel")
 KERNEL_NAMES = ["q_absorb", "splitkv", "combine_up"]
+SHORT_KERNEL_NAMES = ["q_absorb", "short_attn_up"]  # a call whose L + T rows fit in one KV tile (T <= 32)
 
 
 def log(msg):
@@ -85,7 +86,8 @@ def work(H, Dn, Dr, R, Dv, L, T, parent):
     N = L + T
     b = N * (R + Dr) * 2 + H * (Dn + Dv) * R * 2 + T * H * (Dn + Dr) * 2 + T * H * Dv * 2 + 4 * N
     return dict(flops=f_absorb + f_scores + f_pv + f_up, flops_splitkv=f_scores + f_pv, bytes=float(b),
-                bytes_splitkv=float(N * (R + Dr) * 2 + T * H * (R + Dr) * 2 + 4 * N))
+                bytes_splitkv=float(N * (R + Dr) * 2 + T * H * (R + Dr) * 2 + 4 * N),
+                bytes_short=float(H * Dv * R * 2 + N * (R + Dr) * 2 + T * H * (R + Dr) * 2 + T * H * Dv * 2 + 4 * N))
 
 
 # ------------------------------------------------------------------------------------------------ HIP events
@@ -221,8 +223,8 @@ def measure(S, args, torch, kdv, dev, hip, stream, sh, note, K, Wm, full=True):
     ws_bytes = kdv.verify_workspace_bytes(dims, T, L)
     ws_t = torch.zeros((ws_bytes,), dtype=torch.uint8, device=dev)
     splits = kdv.kdv_verify_num_splits(dims, T, L)
-    names = KERNEL_NAMES
     nk = kdv.kdv_verify_kernel_count(dims, T, L)
+    names = KERNEL_NAMES if nk == 3 else SHORT_KERNEL_NAMES
     assert nk == len(names)
     wk = work(H, Dn, Dr, R, Dv, L, T, S.parent_np)
 
@@ -520,10 +522,16 @@ def run(args, torch, si, kdv, dev, hip, stream, sh):
         batch_row = batched_verify_row(torch, si, kdv, dev, sh, graph_us, note, st["names"])
 
     mfma_peak = measured_mfma_peak(torch, kdv, dev, hip, sh, note)
-    # the dominant kernel: the single launch (all of the call's work) or, with three launches, the split-KV pass
-    dom = "splitkv"
-    dom_flops = wk["flops_splitkv"]
-    sk_tflops = dom_flops / (kern_us[dom] * 1e-6) / 1e12
+    # the dominant kernel: the split-KV pass (MFMA-bound), or for a one-tile sequence the short-sequence kernel,
+    # which streams its W_UV rows (HBM-bound)
+    if "splitkv" in kern_us:
+        dom, bound, unit, peak = "splitkv", "mfma", "TFLOP/s", PEAK_BF16_TFLOPS
+        dom_work = wk["flops_splitkv"]
+        achieved = dom_work / (kern_us[dom] * 1e-6) / 1e12
+    else:
+        dom, bound, unit, peak = "short_attn_up", "hbm", "GB/s", PEAK_HBM_GBS
+        dom_work = wk["bytes_short"]
+        achieved = dom_work / (kern_us[dom] * 1e-6) / 1e9
 
     result = {
         "metric": METRIC,
@@ -548,12 +556,13 @@ def run(args, torch, si, kdv, dev, hip, stream, sh):
     result["kernels_us"]["tree_mask"] = round(kern_us["tree_mask"], 3)
     result.update({
         "kernel_timing": "eager, kernel-stamped HIP events, queued behind a spin kernel",
-        "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(sk_tflops, 2),
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(sk_tflops / PEAK_BF16_TFLOPS, 4),
+        "roofline": {"bound": bound, "kernel": dom, "achieved": round(achieved, 2),
+                     "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
                      "traffic": traffic_from_profile(args.workload, dom),
-                     "measured_mfma_peak": round(mfma_peak, 1),
-                     "frac_of_measured_peak": round(sk_tflops / mfma_peak, 4),
-                     "work_per_launch_gflop": round(dom_flops / 1e9, 4)},
+                     **({"measured_mfma_peak": round(mfma_peak, 1),
+                         "frac_of_measured_peak": round(achieved / mfma_peak, 4),
+                         "work_per_launch_gflop": round(dom_work / 1e9, 4)} if bound == "mfma" else
+                        {"work_per_launch_mbytes": round(dom_work / 1e6, 4)})},
         "cpu_baseline": None,
         "dispatch_phases": ledger,
         "next_rows": {"tree_accept": {"us": round(accept_us, 3), "nodes": T, "accepted_path_nodes": n_path,
@@ -956,7 +965,7 @@ def summarize_profile(d, workload):
              f"(`--steps {fb['steps']} --warmup {fb['warmup']}`):", "",
              "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | fetched MB | written MB |", "|---|---|---|---|---|"]
     rec = None
-    dom_kernel = "splitkv_kernel"
+    dom_kernel = "splitkv_kernel" if "splitkv_kernel" in fetch else "short_attn_up_kernel"
     for k in KERNELS:
         if k not in fetch or k not in write:
             continue

@@ -167,7 +167,9 @@ size_t kdv_verify_workspace_bytes(const kdv_mla_dims* d, int32_t T, int32_t L);
  *                KDV_DEBUG page-table status (above) when that check ran; the rest is undefined.  Calls that
  *                share a workspace must be ordered on one stream.
  * The call is three kernel launches on the stream: the query absorption, the split-KV pass, and the split
- * combine with the W_UV up-projection.
+ * combine with the W_UV up-projection.  When all L + T rows fit in one 64-row KV tile and T <= 32 (and no
+ * split count is forced with KDV_SPLITS), it is two: the query absorption, then one kernel that takes the
+ * scores, the softmax, the latent output and the W_UV product for each (head, block of output columns).
  * Returns KDV_OK or a negative kdv_status (nothing enqueued on error). */
 int kdv_verify_mla_attn(const kdv_mla_dims* d, const uint16_t* q_nope, const uint16_t* q_rope,
                         const uint16_t* w_uk, const uint16_t* w_uv, const uint16_t* c_kv, const uint16_t* k_pe,
@@ -203,8 +205,8 @@ int kdv_verify_mla_attn_tree(const kdv_mla_dims* d, const uint16_t* q_nope, cons
 
 /* Same computation as kdv_verify_mla_attn, for measurement: `events` points to 2 * kdv_verify_kernel_count(d, T, L)
  * hipEvent_t created by the caller.  events[2k] and events[2k+1] receive the start and end timestamps of kernel k
- * as the hardware dispatches it (q absorption, split-KV pass, split combine with the W_UV up-projection), so
- * hipEventElapsedTime gives each kernel's device time.  Errors as
+ * as the hardware dispatches it (q absorption, split-KV pass, split combine with the W_UV up-projection; or q
+ * absorption and the short-sequence kernel), so hipEventElapsedTime gives each kernel's device time.  Errors as
  * kdv_verify_mla_attn, plus KDV_ERR_NULL if events is NULL. */
 int kdv_verify_mla_attn_profiled(const kdv_mla_dims* d, const uint16_t* q_nope, const uint16_t* q_rope,
                                  const uint16_t* w_uk, const uint16_t* w_uv, const uint16_t* c_kv,
@@ -280,7 +282,9 @@ int kdv_merge_attn_states(const uint16_t* out_a, const float* lse_a, const uint1
 int32_t kdv_verify_num_splits(const kdv_mla_dims* d, int32_t T, int32_t L);
 
 /* Number of kernels one kdv_verify_mla_attn call launches for these arguments: 3 (absorption, split-KV,
- * combine); 0 if unsupported.  The batched call launches 3 as well. */
+ * combine), or 2 (absorption, short-sequence attention with the up-projection) when L + T <= 64 and T <= 32
+ * and KDV_SPLITS is unset; 0 if unsupported.  The prefix-only call and batches of two or more requests always
+ * launch 3. */
 int32_t kdv_verify_kernel_count(const kdv_mla_dims* d, int32_t T, int32_t L);
 
 /* DIAGNOSTIC ONLY, not part of the attention path: a measurement aid for the benchmark.  Launches `blocks` workgroups of 256 threads in which every wave issues `iters`

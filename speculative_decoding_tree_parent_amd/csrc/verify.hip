@@ -13,8 +13,11 @@
 //              with an online softmax; the partial (O, max, sum) of the split goes to the workspace.
 //   combine_up : log-sum-exp merge of the splits -> lse and the latent output o[t,h] (bf16, in LDS), then
 //              out[t,h] = W_UV[h] o[t,h]                                   (bf16 MFMA)
+// A single call whose L + T rows fit in one KV tile (and T <= 32) replaces the last two with one kernel,
+// short_attn_up: per (head, block of output columns) the scores, an exact one-tile softmax, P V and W_UV.
 #include <hip/hip_ext.h>
 #include <algorithm>
+#include <type_traits>
 #include <mutex>
 #include <math.h>
 #include <stdlib.h>
@@ -998,6 +1001,240 @@ __global__ __launch_bounds__(COMB_THREADS) void combine_up_kernel(const uint16_t
   combine_block<R, DV, RT, COMB_THREADS>(part_o, part_ml, S, Mp, w_uv, out, lse, H, h, t0, nrow, w_s, o_s, gx);
 }
 
+// ------------------------------------------------------------------------------------------------ short sequence
+// When a single request's whole KV sequence fits in one tile (N = L + T <= 64 rows) and its tree has at most 32
+// nodes, the split-KV pass and the combine become one kernel with no partials.  Workgroup (h, j) gathers the N
+// rows once, scores head h's T query rows against them over the full contraction, takes the softmax with each
+// row's own maximum as reference (one tile: no running rescale), forms the latent output o = P V / l (bf16, as
+// the combine rounds it) and multiplies it by its VC rows v0 .. v0 + VC - 1 of W_UV[h].  The work per step:
+//   scores  S^T[n][t] = K[n] . Q[t]: wave (key block nb = w % 2, contraction half kh = w / 2), 32 keys x 32
+//           nodes; the two halves meet in LDS;
+//   softmax waves 0 and 1 (one key block each; the row maxima and sums meet in LDS); P^T fragments to LDS in
+//           the value MFMA's operand order (the score layout already is that order, as in the split-KV loop);
+//   values  O^T[r][t] = sum_n V^T[r][n] P^T[n][t] over the 64 tile rows: each wave R/4 latent columns;
+//   output  D[v][t] = sum_r W_UV[h][v][r] o[t][r]: wave (v block, contraction part), parts summed in LDS.
+// Rows n >= N of the tile repeat row N - 1 and are masked; node rows t >= T repeat node T - 1, never stored.
+template <int R, int DR, int DV>
+__global__ __launch_bounds__(NTHREADS) void short_attn_up_kernel(
+    const uint16_t* __restrict__ q_cat, const uint16_t* __restrict__ c_kv, const uint16_t* __restrict__ k_pe,
+    const int32_t* __restrict__ page_table, const uint32_t* __restrict__ mask, const uint16_t* __restrict__ w_uv,
+    int L, int T, int H, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse,
+    const int32_t* __restrict__ dbg) {
+  using TL = TileLayout<R, DR>;
+  using PV = PvSplit<R>;
+  constexpr int DQ = R + DR, KB = DQ / 16;  // score k-steps
+  constexpr bool EVEN = KB % 2 == 0;        // split over the two wave halves (odd KB, narrow test shape: half 0)
+  constexpr int KH0 = EVEN ? KB / 2 : KB;   // k-steps per scoring wave
+  constexpr int VC = DV >= 64 ? 64 : DV;  // output columns per workgroup
+  constexpr int VB = VC / 32, KQ = 4 / VB, KS = R / 16, KSQ = KS / KQ;
+  constexpr int CPR = R / 8, WSW = CPR < 16 ? CPR : 16, OP = R + 8;
+  constexpr int WINS = VC * R * 2 / 1024;  // W_UV DMA instructions (all waves)
+  constexpr float LN2 = 0.69314718055994530942f;
+  static_assert(DV % VC == 0 && VC % 32 == 0 && 4 % VB == 0 && KS % KQ == 0, "output blocks");
+  static_assert(WINS % 4 == 0, "W_UV rows must split evenly over the four waves");
+  static_assert(32 * OP * 2 <= TL::BYTES, "the latent output rows fit in the KV tile's LDS");
+  static_assert(KQ - 1 <= 3 && VB * (KQ - 1) <= 3, "output partial sums fit in the exchange buffer");
+  __shared__ __attribute__((aligned(1024))) char kvbuf[TL::BYTES];  // the KV tile; then the latent output rows
+  __shared__ __attribute__((aligned(1024))) char w_s[VC * R * 2];
+  __shared__ uint4 pfr[4][64];        // P^T fragments of the tile's four 16-row k-steps (bf16), lane order
+  __shared__ float red[3][16][64];    // partial sums exchanged between waves [part][register][lane]
+  __shared__ float mx[2][32], sm[2][32];  // per key block: row maximum (unscaled), row sum
+
+  const int h = blockIdx.x, v0 = blockIdx.y * VC;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, c = lane & 31;
+  const int N = L + T, tq = min(c, T - 1);
+  if (dbg != nullptr && *dbg != KDV_OK) {  // page table failed its check: NaN results, nothing gathered (uniform)
+    for (int k = tid; k < T * VC; k += NTHREADS) out[((size_t)(k / VC) * H + h) * DV + v0 + k % VC] = 0x7FC0;
+    if (lse != nullptr && blockIdx.y == 0 && tid < T) lse[tid * H + h] = __builtin_nanf("");
+    return;
+  }
+
+  // ---- loads.  The query fragments, the mask word and the page-table entries are ordinary loads, issued first
+  // and complete before the gathers go out: the compiler's own waits do not count the gathers, so a wait it placed
+  // for one of these loads later would also wait for every gather.  The gather of the KV rows needs the entries,
+  // and the W_UV rows (needed last) go out after it.
+  const int nb = wave & 1, kh = wave >> 1;
+  const int kb0 = EVEN ? kh * KH0 : 0;  // this wave's first score k-step
+  bf16x8 qf[KH0];
+  {
+    const uint16_t* qrow = q_cat + ((size_t)tq * H + h) * DQ + g * 8;
+#pragma unroll
+    for (int i = 0; i < KH0; ++i) qf[i] = load_bf16x8(qrow + (kb0 + i) * 16);
+  }
+  const uint32_t mw = mask[tq];  // T <= 32: one word per node
+  const int slot = page_table[min(lane, N - 1)];
+#pragma unroll
+  for (int i = 0; i < KH0; ++i) asm volatile("" ::"v"(qf[i]));
+  asm volatile("" ::"v"(mw), "v"(slot));
+  TileDma<R, DR> dma(c_kv, k_pe, wave, lane);
+  dma.target(kvbuf, slot);
+#pragma unroll
+  for (int k = 0; k < TileDma<R, DR>::NK; ++k) dma.issue(k);
+  {
+    const char* wsrc = reinterpret_cast<const char*>(w_uv + ((size_t)h * DV + v0) * R);
+    const uint32_t wl = lds_address(w_s);
+#pragma unroll
+    for (int k = 0; k < WINS / 4; ++k) {
+      const int ins = wave + 4 * k, pos = ins * 64 + lane, r = pos / CPR, p = pos % CPR;
+      dma16_lane_addr(wsrc + (size_t)r * (R * 2) + ((p ^ (r & (WSW - 1))) << 4), wl + ins * 1024);
+    }
+  }
+  wait_vmem_below<WINS / 4>();  // the KV rows of this wave are in LDS; the W_UV rows may still be in flight
+  __syncthreads();
+
+  // ---- scores: S^T[n][t] for tile rows n = nb*32 + (r/4)*8 + g*4 + r%4 (register r), node t = c
+  float s[16];
+  {
+    f32x16 acc0 = zero16(), acc1 = zero16();
+    const int nrow = nb * 32 + c;
+    // the k-steps of one wave half, with its first k-step a compile-time constant (every offset is then a
+    // per-lane base plus an immediate); fragment i + QD is requested before the MFMA of fragment i
+    auto half = [&](auto first) {
+      constexpr int F = decltype(first)::value;
+      auto kfrag = [&](int i) -> bf16x8 {
+        const int kb = F + i;
+        const int off = (kb < R / 16) ? TL::ckv(nrow, 2 * kb + g) : TL::kpe(nrow, 2 * (kb - R / 16) + g);
+        return *reinterpret_cast<const bf16x8*>(kvbuf + off);
+      };
+      constexpr int QD = KH0 < 6 ? KH0 : 6;
+      bf16x8 kf[QD];
+#pragma unroll
+      for (int i = 0; i < QD; ++i) kf[i] = kfrag(i);
+#pragma unroll
+      for (int i = 0; i < KH0; ++i) {
+        const bf16x8 a = kf[i % QD];
+        if (i + QD < KH0) kf[i % QD] = kfrag(i + QD);
+        if (i & 1) acc1 = mfma32(a, qf[i], acc1);
+        else acc0 = mfma32(a, qf[i], acc0);
+      }
+    };
+    if (kh == 0) half(std::integral_constant<int, 0>{});  // (wave-uniform)
+    else if (EVEN) half(std::integral_constant<int, KH0>{});
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = acc0[r] + acc1[r];
+  }
+  if (kh == 1) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) red[nb][r][lane] = s[r];
+  }
+  __syncthreads();
+  if (kh == 0) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] += red[nb][r][lane];
+    const int jb = nb * 32 + g * 4 - L;  // tree index of register 0's row
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int j = jb + (r >> 2) * 8 + (r & 3);
+      const bool vis = (j < 0) | ((j < T) & (((mw >> (j & 31)) & 1u) != 0u));
+      s[r] = vis ? s[r] : -INFINITY;
+      tmax = fmaxf(tmax, s[r]);
+    }
+    tmax = pair_max(tmax);
+    if (g == 0) mx[nb][c] = tmax;
+  }
+  __syncthreads();
+  // every node sees its own row (tree position L + t), so each row's maximum is finite
+  const float M = fmaxf(mx[0][c], mx[1][c]) * scale_log2;  // (scale > 0)
+  if (kh == 0) {
+    bf16x8 pk[2];
+    float ps;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float p0 = fast_exp2(fmaf(s[e], scale_log2, -M)), p1 = fast_exp2(fmaf(s[8 + e], scale_log2, -M));
+      ps = (e == 0) ? p0 + p1 : ps + (p0 + p1);
+      pk[0][e] = (__bf16)p0;
+      pk[1][e] = (__bf16)p1;
+    }
+    ps = pair_sum(ps);
+    pfr[nb * 2 + 0][lane] = __builtin_bit_cast(uint4, pk[0]);
+    pfr[nb * 2 + 1][lane] = __builtin_bit_cast(uint4, pk[1]);
+    if (g == 0) sm[nb][c] = ps;
+  }
+  __syncthreads();
+
+  // ---- values: O^T[r][t] for this wave's latent columns col0 .. col0 + CPW - 1
+  constexpr int DBW = PV::DBW;
+  const float inv = 1.f / (sm[0][c] + sm[1][c]);
+  const int col0 = wave * PV::CPW;
+  f32x16 o[DBW];
+#pragma unroll
+  for (int db = 0; db < DBW; ++db) o[db] = zero16();
+  if (wave < PV::WAVES) {
+    const int rl = g * 4 + ((lane & 15) >> 2);
+    const int cl = ((lane & 31) >> 4) * 2 + ((lane & 3) >> 1);
+    const int sub = (lane & 1) * 8;
+    bf16x8 pf[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) pf[ks] = __builtin_bit_cast(bf16x8, pfr[ks][lane]);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int db = 0; db < DBW; ++db) {
+        const int ch = (col0 + db * 32) / 8 + cl;
+        const bf16x8 a = concat_tr(lds_read_tr16(kvbuf + TL::ckv(ks * 16 + rl, ch) + sub),
+                                   lds_read_tr16(kvbuf + TL::ckv(ks * 16 + rl + 8, ch) + sub));
+        o[db] = mfma32(a, pf[ks], o[db]);
+      }
+  }
+  __syncthreads();  // every wave is done with the KV tile: its LDS takes the latent output rows
+  uint16_t* o_s = reinterpret_cast<uint16_t*>(kvbuf);
+  if (wave < PV::WAVES) {
+#pragma unroll
+    for (int db = 0; db < DBW; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        bf16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (__bf16)(o[db][q4 * 4 + e] * inv);
+        *reinterpret_cast<bf16x4*>(o_s + c * OP + col0 + db * 32 + q4 * 8 + g * 4) = v;
+      }
+  }
+  if (lse != nullptr && blockIdx.y == 0 && wave == 0 && g == 0 && c < T)
+    lse[c * H + h] = (M + log2f(sm[0][c] + sm[1][c])) * LN2;
+  wait_vmem_all();  // this wave's W_UV rows
+  __syncthreads();  // the latent output rows and all of W_UV are in LDS
+
+  // ---- output: D[v][t] = sum_r W_UV[h][v0 + v][r] o[t][r], wave (v block vb, contraction part kq)
+  const int vb = wave % VB, kq = wave / VB;
+  const char* wrow = w_s + (vb * 32 + c) * (R * 2);
+  const int wsz = (vb * 32 + c) & (WSW - 1);
+  const uint16_t* orow = o_s + tq * OP + g * 8;
+  f32x16 u0 = zero16(), u1 = zero16();
+#pragma unroll
+  for (int i = 0; i < KSQ; ++i) {
+    const int ks = kq * KSQ + i;
+    const bf16x8 a = *reinterpret_cast<const bf16x8*>(wrow + (((2 * ks + g) ^ wsz) << 4));
+    const bf16x8 b = *reinterpret_cast<const bf16x8*>(orow + ks * 16);
+    if (i & 1) u1 = mfma32(a, b, u1);
+    else u0 = mfma32(a, b, u0);
+  }
+  float u[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) u[r] = u0[r] + u1[r];
+  if (kq > 0) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) red[(kq - 1) * VB + vb][r][lane] = u[r];
+  }
+  __syncthreads();
+  if (kq == 0 && c < T) {
+#pragma unroll
+    for (int q = 1; q < KQ; ++q)  // parts in a fixed order
+#pragma unroll
+      for (int r = 0; r < 16; ++r) u[r] += red[(q - 1) * VB + vb][r][lane];
+    uint16_t* dst = out + ((size_t)c * H + h) * DV + v0 + vb * 32 + g * 4;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      bf16x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = (__bf16)u[q4 * 4 + e];
+      *reinterpret_cast<bf16x4*>(dst + q4 * 8) = v;
+    }
+  }
+}
+
 
 // ------------------------------------------------------------------------------------------------ state merge
 // Two attention results over disjoint sets of KV positions, (out_a, lse_a) and (out_b, lse_b), combine into
@@ -1081,6 +1318,7 @@ struct Plan {
   int H, nodes;           // heads, nodes of all requests
   int split_blocks, comb_blocks;
   int comb_rt;            // tree nodes per combine workgroup (4; 2 or 1 for a small single request, 16 for a batch)
+  bool short_seq;         // one request whose L + T rows fit in one KV tile, T <= 32: short_attn_up_kernel
   BatchArgs<MAX_BATCH> ba;
   size_t off_qcat, off_po, off_pml, total;   // workspace regions (after a KDV_WS_HEADER-byte header)
 };
@@ -1250,6 +1488,9 @@ static int make_plan(const kdv_mla_dims* d, int C, const int32_t* Ls, const int3
   }
   p->split_blocks = (int)blk_s;
   p->comb_blocks = (int)blk_c;
+  // A single verify whose whole sequence fits in one tile takes the short-sequence kernel instead of the split-KV
+  // pass and the combine (unless a split count is forced: that always takes the split path).
+  p->short_seq = C == 1 && with_tree && env_splits <= 0 && Ls[0] + Ts[0] <= KV_TILE && Ts[0] <= 32;
   size_t off = KDV_WS_HEADER;  // header: the debug page-table status (int32 at offset 0)
   p->off_qcat = off;
   off += align256((size_t)nodes * H * DQ * 2);
@@ -1289,6 +1530,12 @@ static void launch_all(const Plan& pl, float sm_scale, const uint16_t* q_nope, c
   launch(q_absorb_kernel<DN, R, DR>, dim3(pl.H + (parent != nullptr ? 1 : 0), (R + 127) / 128, (pl.nodes + 31) / 32), st,
          ev ? ev + 0 : nullptr, q_nope, q_rope, w_uk, q_cat, pl.nodes, pl.H, parent, const_cast<uint32_t*>(mask),
          status, dbg);
+  if (pl.short_seq) {
+    const ReqArgs& r = pl.ba.r[0];
+    launch(short_attn_up_kernel<R, DR, DV>, dim3(pl.H, DV / (DV >= 64 ? 64 : DV)), st, ev ? ev + 2 : nullptr,
+           (const uint16_t*)q_cat, c_kv, k_pe, page_table, mask, w_uv, r.L, r.T, pl.H, scale_log2, out, lse, dbg);
+    return;
+  }
   if (pl.ba.n == 1) {
     BatchArgs<1> one;
     one.n = 1;
@@ -1346,7 +1593,7 @@ extern "C" size_t kdv_prefix_workspace_bytes(const kdv_mla_dims* d, int32_t T, i
 extern "C" int32_t kdv_verify_kernel_count(const kdv_mla_dims* d, int32_t T, int32_t L) {
   kdv::Plan p;
   if (kdv::make_plan(d, 1, &L, &T, &p) != KDV_OK) return 0;
-  return 3;
+  return p.short_seq ? 2 : 3;
 }
 
 extern "C" int32_t kdv_verify_num_splits(const kdv_mla_dims* d, int32_t T, int32_t L) {
