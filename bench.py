@@ -451,7 +451,11 @@ def run(args, torch, si, kdv, dev, hip, stream, sh):
                                            fx["out"], fx["lse"], sh)
             if rc:
                 raise kdv.KdvError(rc, "kdv_merge_attn_states")
-    per_split_step = dict(tree_mask=1, **{n: 2 * lps for n in st["names"]}, merge_states=lps)
+    # the prefix-only pass always takes the split path; the tail pass (L = 0) may take the short-sequence kernel
+    tail_names = KERNEL_NAMES if kdv.kdv_verify_kernel_count(dims, T, 0) == 3 else SHORT_KERNEL_NAMES
+    per_split_step = dict(tree_mask=1, merge_states=lps)
+    for n in KERNEL_NAMES + tail_names:
+        per_split_step[n] = per_split_step.get(n, 0) + lps
     ms_split = None
     if L >= 1:
         log(f"[bench] timing {K} steps of the prefix/tail split (cold)")
@@ -965,7 +969,10 @@ def summarize_profile(d, workload):
              f"(`--steps {fb['steps']} --warmup {fb['warmup']}`):", "",
              "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | fetched MB | written MB |", "|---|---|---|---|---|"]
     rec = None
-    dom_kernel = "splitkv_kernel" if "splitkv_kernel" in fetch else "short_attn_up_kernel"
+    # the workload's own dominant kernel: split-KV, or the short-sequence kernel when the call has no split-KV pass
+    sk_ph, _ = _phases(fb, "splitkv_kernel")
+    sk_a, sk_b = sk_ph.get(f"{workload}: eager cold, kernel events", (0, 0))
+    dom_kernel = "splitkv_kernel" if sk_b > sk_a else "short_attn_up_kernel"
     for k in KERNELS:
         if k not in fetch or k not in write:
             continue
