@@ -91,23 +91,34 @@ __global__ __launch_bounds__(64) void draft_tree_kernel(const float* __restrict_
     const int d = __builtin_amdgcn_readlane(c_depth, w), p = __builtin_amdgcn_readlane(c_parent, w);
     const int r = __builtin_amdgcn_readlane(c_rank, w);
     const float ps = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(n_score), p));  // parent's score
+    // The three table entries this step needs sit at wave-uniform addresses: every lane reads them together
+    // (LDS broadcasts), so the step waits for one LDS round trip instead of three in turn.  An entry that is not
+    // needed is read at a valid stand-in address and ignored.
+    const bool sib = r + 1 < K, child = d < block;
+    const int e = (d - 1) * K + r;
+    const int32_t tk = s_tok[e];
+    const float l_sib = s_logp[sib ? e + 1 : e];
+    const float l_child = s_logp[child ? d * K : 0];
+    asm volatile("" ::"v"(tk), "v"(l_sib), "v"(l_child));  // (keeps the three reads together, ahead of the branches)
+    // the lowest free slot once the winner's slot has taken its sibling or been freed
+    const unsigned long long freem = __ballot(!cand) | (sib ? 0ull : (1ull << w));
     if (j == n) {  // node n joins
       n_score = s;
       n_parent = p;
-      n_token = s_tok[(d - 1) * K + r];
+      n_token = tk;
     }
     if (j == w) {  // the winner's slot takes its next sibling, if any
-      cand = r + 1 < K;
-      if (cand) {
-        c_score = ps + s_logp[(d - 1) * K + r + 1];
+      cand = sib;
+      if (sib) {
+        c_score = ps + l_sib;
         c_rank = r + 1;
       }
     }
-    if (d < block) {  // first child of node n, in the lowest free slot
-      const int f = __builtin_ctzll(__ballot(!cand));
+    if (child) {  // first child of node n, in the lowest free slot
+      const int f = __builtin_ctzll(freem);
       if (j == f) {
         cand = true;
-        c_score = s + s_logp[d * K];
+        c_score = s + l_child;
         c_depth = d + 1;
         c_parent = n;
         c_rank = 0;
