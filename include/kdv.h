@@ -168,8 +168,8 @@ size_t kdv_verify_workspace_bytes(const kdv_mla_dims* d, int32_t T, int32_t L);
  *                share a workspace must be ordered on one stream.
  * The call is three kernel launches on the stream: the query absorption, the split-KV pass, and the split
  * combine with the W_UV up-projection.  When all L + T rows fit in one 64-row KV tile and T <= 32 (and no
- * split count is forced with KDV_SPLITS), it is two: the query absorption, then one kernel that takes the
- * scores, the softmax, the latent output and the W_UV product for each (head, block of output columns).
+ * split count is forced with KDV_SPLITS), it is one kernel that takes the query absorption, the scores, the
+ * softmax, the latent output and the W_UV product for each (head, block of 32 output columns).
  * Returns KDV_OK or a negative kdv_status (nothing enqueued on error). */
 int kdv_verify_mla_attn(const kdv_mla_dims* d, const uint16_t* q_nope, const uint16_t* q_rope,
                         const uint16_t* w_uk, const uint16_t* w_uv, const uint16_t* c_kv, const uint16_t* k_pe,
@@ -193,7 +193,8 @@ int kdv_verify_mla_attn_noalloc(const kdv_mla_dims* d, const uint16_t* q_nope, c
 /* kdv_verify_mla_attn that builds the tree's ancestor mask itself: the mask of kdv_build_tree_mask(parent, T)
  * is written to `mask` (device uint32 [T][(T+31)/32], written; the caller can pass it to kdv_verify_mla_attn
  * for the other layers of the step) and `status` (device int32, nullable) by one extra block of the call's
- * first kernel, so the verify step needs no separate mask launch.  Other arguments and results as
+ * first kernel (on the short-sequence path, by the kernel's first workgroup, every workgroup building the rows
+ * it needs in LDS), so the verify step needs no separate mask launch.  Other arguments and results as
  * kdv_verify_mla_attn; KDV_ERR_NULL if parent is NULL, KDV_ERR_ALIGN if parent or status is not 4-byte
  * aligned.  A malformed tree is reported in `status` as for kdv_build_tree_mask, and its rows attend as that
  * mask says. */
@@ -205,8 +206,8 @@ int kdv_verify_mla_attn_tree(const kdv_mla_dims* d, const uint16_t* q_nope, cons
 
 /* Same computation as kdv_verify_mla_attn, for measurement: `events` points to 2 * kdv_verify_kernel_count(d, T, L)
  * hipEvent_t created by the caller.  events[2k] and events[2k+1] receive the start and end timestamps of kernel k
- * as the hardware dispatches it (q absorption, split-KV pass, split combine with the W_UV up-projection; or q
- * absorption and the short-sequence kernel), so hipEventElapsedTime gives each kernel's device time.  Errors as
+ * as the hardware dispatches it (q absorption, split-KV pass, split combine with the W_UV up-projection; or the
+ * short-sequence kernel alone), so hipEventElapsedTime gives each kernel's device time.  Errors as
  * kdv_verify_mla_attn, plus KDV_ERR_NULL if events is NULL. */
 int kdv_verify_mla_attn_profiled(const kdv_mla_dims* d, const uint16_t* q_nope, const uint16_t* q_rope,
                                  const uint16_t* w_uk, const uint16_t* w_uv, const uint16_t* c_kv,
@@ -282,8 +283,8 @@ int kdv_merge_attn_states(const uint16_t* out_a, const float* lse_a, const uint1
 int32_t kdv_verify_num_splits(const kdv_mla_dims* d, int32_t T, int32_t L);
 
 /* Number of kernels one kdv_verify_mla_attn call launches for these arguments: 3 (absorption, split-KV,
- * combine), or 2 (absorption, short-sequence attention with the up-projection) when L + T <= 64 and T <= 32
- * and KDV_SPLITS is unset; 0 if unsupported.  The prefix-only call and batches of two or more requests always
+ * combine), or 1 (the short-sequence kernel) when L + T <= 64 and T <= 32 and KDV_SPLITS is unset; 0 if
+ * unsupported.  The prefix-only call and batches of two or more requests always
  * launch 3. */
 int32_t kdv_verify_kernel_count(const kdv_mla_dims* d, int32_t T, int32_t L);
 

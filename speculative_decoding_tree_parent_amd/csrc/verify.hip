@@ -13,8 +13,8 @@
 //              with an online softmax; the partial (O, max, sum) of the split goes to the workspace.
 //   combine_up : log-sum-exp merge of the splits -> lse and the latent output o[t,h] (bf16, in LDS), then
 //              out[t,h] = W_UV[h] o[t,h]                                   (bf16 MFMA)
-// A single call whose L + T rows fit in one KV tile (and T <= 32) replaces the last two with one kernel,
-// short_attn_up: per (head, block of output columns) the scores, an exact one-tile softmax, P V and W_UV.
+// A single call whose L + T rows fit in one KV tile (and T <= 32) is one kernel instead, short_verify: per (head,
+// block of output columns) the absorption, the scores, an exact one-tile softmax, P V and the W_UV product.
 #include <hip/hip_ext.h>
 #include <algorithm>
 #include <type_traits>
@@ -1003,71 +1003,131 @@ __global__ __launch_bounds__(COMB_THREADS) void combine_up_kernel(const uint16_t
 
 // ------------------------------------------------------------------------------------------------ short sequence
 // When a single request's whole KV sequence fits in one tile (N = L + T <= 64 rows) and its tree has at most 32
-// nodes, the split-KV pass and the combine become one kernel with no partials.  Workgroup (h, j) gathers the N
-// rows once, scores head h's T query rows against them over the full contraction, takes the softmax with each
-// row's own maximum as reference (one tile: no running rescale), forms the latent output o = P V / l (bf16, as
-// the combine rounds it) and multiplies it by its VC rows v0 .. v0 + VC - 1 of W_UV[h].  The work per step:
-//   scores  S^T[n][t] = K[n] . Q[t]: wave (key block nb = w % 2, contraction half kh = w / 2), 32 keys x 32
-//           nodes; the two halves meet in LDS;
-//   softmax waves 0 and 1 (one key block each; the row maxima and sums meet in LDS); P^T fragments to LDS in
-//           the value MFMA's operand order (the score layout already is that order, as in the split-KV loop);
-//   values  O^T[r][t] = sum_n V^T[r][n] P^T[n][t] over the 64 tile rows: each wave R/4 latent columns;
-//   output  D[v][t] = sum_r W_UV[h][v][r] o[t][r]: wave (v block, contraction part), parts summed in LDS.
+// nodes, the whole call is one kernel: no q_cat, no partials, no second or third launch.  Workgroup (h, j) works on
+// head h and output columns v0 = j*VC .. v0 + VC - 1:
+//   absorb  the W_UK[h] rows are staged in LDS (rows of R columns, 16-byte chunks XOR-swizzled as a KV tile's
+//           latent rows) and every wave computes q_lat^T[r][t] = sum_k W_UK[h][k][r] q_nope[t,h][k] for R/4 latent
+//           columns r of the T <= 32 nodes t (A = W^T by transposed reads, B = q_nope from global);
+//   q tile  q_lat (bf16, as q_cat holds it) and q_rope go to LDS as 32 rows of R + DR elements, once W_UK is
+//           consumed; meanwhile the N KV rows and the workgroup's W_UV rows are gathered into the space W_UK held;
+//   scores  S^T[n][t] = K[n] . Q[t]: wave (key block nb = w % 2, contraction half kh = w / 2), 32 keys x 32 nodes;
+//           the two halves meet in LDS;
+//   softmax waves 0 and 1 (one key block each; row maxima and sums meet in LDS), each row's own maximum as the
+//           reference (one tile: no running rescale); P^T fragments to LDS in the value MFMA's operand order;
+//   values  O^T[r][t] = sum_n V^T[r][n] P^T[n][t] over the tile: each wave R/4 latent columns; o = O / l (bf16, as
+//           the combine rounds it) goes over the tile's LDS;
+//   output  D[v][t] = sum_r W_UV[h][v0 + v][r] o[t][r], the contraction split over the waves and summed in LDS.
+// A call that builds its tree mask builds the T rows it needs in every workgroup (one wave, in LDS); workgroup
+// (0, 0) also writes the mask and the tree status for the caller.
 // Rows n >= N of the tile repeat row N - 1 and are masked; node rows t >= T repeat node T - 1, never stored.
-template <int R, int DR, int DV>
-__global__ __launch_bounds__(NTHREADS) void short_attn_up_kernel(
-    const uint16_t* __restrict__ q_cat, const uint16_t* __restrict__ c_kv, const uint16_t* __restrict__ k_pe,
-    const int32_t* __restrict__ page_table, const uint32_t* __restrict__ mask, const uint16_t* __restrict__ w_uv,
-    int L, int T, int H, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse,
-    const int32_t* __restrict__ dbg) {
+template <int DN, int R, int DR, int DV>
+struct ShortLayout {
+  using TL = TileLayout<R, DR>;
+  static constexpr int DQ = R + DR;
+  static constexpr int VC = 32;                          // output columns per workgroup
+  static constexpr int QP = DQ + 8;                      // q-tile row pitch (elements)
+  static constexpr int OP = R + 8;                       // latent output row pitch (elements)
+  static constexpr int KV_OFF = 0, WUV_OFF = TL::BYTES, QT_OFF = WUV_OFF + VC * R * 2;
+  static constexpr int WUK_BYTES = DN * R * 2;
+  static constexpr int QT_BYTES = 32 * QP * 2;
+  static constexpr int BYTES = (QT_OFF + QT_BYTES > WUK_BYTES ? QT_OFF + QT_BYTES : WUK_BYTES);
+  static_assert(DV % VC == 0, "output column blocks");
+  static_assert(32 * OP * 2 <= TL::BYTES, "the latent output rows fit in the KV tile's LDS");
+  static_assert((WUK_BYTES / 1024) % 4 == 0 && (VC * R * 2 / 1024) % 4 == 0, "DMA rows split over four waves");
+};
+
+template <int DN, int R, int DR, int DV>
+__global__ __launch_bounds__(NTHREADS) void short_verify_kernel(
+    const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_rope, const uint16_t* __restrict__ w_uk,
+    const uint16_t* __restrict__ w_uv, const uint16_t* __restrict__ c_kv, const uint16_t* __restrict__ k_pe,
+    const int32_t* __restrict__ page_table, const int32_t* __restrict__ parent, uint32_t* __restrict__ mask,
+    int32_t* __restrict__ tree_status, int L, int T, int H, float scale_log2, uint16_t* __restrict__ out,
+    float* __restrict__ lse, const int32_t* __restrict__ dbg) {
+  using SL = ShortLayout<DN, R, DR, DV>;
   using TL = TileLayout<R, DR>;
   using PV = PvSplit<R>;
   constexpr int DQ = R + DR, KB = DQ / 16;  // score k-steps
   constexpr bool EVEN = KB % 2 == 0;        // split over the two wave halves (odd KB, narrow test shape: half 0)
   constexpr int KH0 = EVEN ? KB / 2 : KB;   // k-steps per scoring wave
-  constexpr int VC = DV >= 64 ? 64 : DV;  // output columns per workgroup
-  constexpr int VB = VC / 32, KQ = 4 / VB, KS = R / 16, KSQ = KS / KQ;
-  constexpr int CPR = R / 8, WSW = CPR < 16 ? CPR : 16, OP = R + 8;
-  constexpr int WINS = VC * R * 2 / 1024;  // W_UV DMA instructions (all waves)
+  constexpr int VC = SL::VC, KQ = 4, KS = R / 16, KSQ = KS / KQ;
+  constexpr int CK = R / 8, CPR = R / 8, WSW = CPR < 16 ? CPR : 16, OP = SL::OP, QP = SL::QP;
+  constexpr int AW = R / 32 < 4 ? R / 32 : 4;  // waves that absorb (R / 32 latent column blocks over them)
+  constexpr int RBW = R / 32 / AW;             // 32-column blocks per absorbing wave
+  constexpr int NKB = DN / 16;                 // absorption k-steps
+  constexpr int WUK_INS = SL::WUK_BYTES / 1024, WUV_INS = VC * R * 2 / 1024;  // DMA instructions (all waves)
   constexpr float LN2 = 0.69314718055994530942f;
-  static_assert(DV % VC == 0 && VC % 32 == 0 && 4 % VB == 0 && KS % KQ == 0, "output blocks");
-  static_assert(WINS % 4 == 0, "W_UV rows must split evenly over the four waves");
-  static_assert(32 * OP * 2 <= TL::BYTES, "the latent output rows fit in the KV tile's LDS");
-  static_assert(KQ - 1 <= 3 && VB * (KQ - 1) <= 3, "output partial sums fit in the exchange buffer");
-  __shared__ __attribute__((aligned(1024))) char kvbuf[TL::BYTES];  // the KV tile; then the latent output rows
-  __shared__ __attribute__((aligned(1024))) char w_s[VC * R * 2];
+  static_assert(KS % KQ == 0 && R % 32 == 0 && DN % 16 == 0, "shapes");
+  __shared__ __attribute__((aligned(1024))) char smem[SL::BYTES];
   __shared__ uint4 pfr[4][64];        // P^T fragments of the tile's four 16-row k-steps (bf16), lane order
   __shared__ float red[3][16][64];    // partial sums exchanged between waves [part][register][lane]
   __shared__ float mx[2][32], sm[2][32];  // per key block: row maximum (unscaled), row sum
+  __shared__ uint32_t smask[64];      // ancestor rows, when the call builds them
+  char* kvbuf = smem + SL::KV_OFF;
+  char* w_s = smem + SL::WUV_OFF;
+  uint16_t* q_s = reinterpret_cast<uint16_t*>(smem + SL::QT_OFF);
 
   const int h = blockIdx.x, v0 = blockIdx.y * VC;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, c = lane & 31;
   const int N = L + T, tq = min(c, T - 1);
+  if (parent != nullptr && wave == 0) {
+    build_ancestor_mask(parent, T, smask, nullptr, lane);
+    if (blockIdx.x == 0 && blockIdx.y == 0) build_ancestor_mask(parent, T, mask, tree_status, lane);
+  }
   if (dbg != nullptr && *dbg != KDV_OK) {  // page table failed its check: NaN results, nothing gathered (uniform)
     for (int k = tid; k < T * VC; k += NTHREADS) out[((size_t)(k / VC) * H + h) * DV + v0 + k % VC] = 0x7FC0;
     if (lse != nullptr && blockIdx.y == 0 && tid < T) lse[tid * H + h] = __builtin_nanf("");
     return;
   }
 
-  // ---- loads.  The query fragments, the mask word and the page-table entries are ordinary loads, issued first
-  // and complete before the gathers go out: the compiler's own waits do not count the gathers, so a wait it placed
-  // for one of these loads later would also wait for every gather.  The gather of the KV rows needs the entries,
-  // and the W_UV rows (needed last) go out after it.
-  const int nb = wave & 1, kh = wave >> 1;
-  const int kb0 = EVEN ? kh * KH0 : 0;  // this wave's first score k-step
-  bf16x8 qf[KH0];
+  // ---- W_UK[h] into LDS (lane l of instruction i fills position i*64 + l of the swizzled rows), then the
+  // ordinary loads: the absorption's q_nope fragments, the q_rope chunks of the q tile, the page-table entries
   {
-    const uint16_t* qrow = q_cat + ((size_t)tq * H + h) * DQ + g * 8;
-#pragma unroll
-    for (int i = 0; i < KH0; ++i) qf[i] = load_bf16x8(qrow + (kb0 + i) * 16);
+    const char* src = reinterpret_cast<const char*>(w_uk + (size_t)h * DN * R);
+    const uint32_t base = lds_address(smem);
+#pragma unroll 4
+    for (int k = 0; k < WUK_INS / 4; ++k) {
+      const int ins = wave + 4 * k, pos = ins * 64 + lane, row = pos / CK, p = pos % CK;
+      dma16_lane_addr(src + (size_t)row * (R * 2) + ((p ^ swz<CK>(row)) << 4), base + ins * 1024);
+    }
   }
-  const uint32_t mw = mask[tq];  // T <= 32: one word per node
-  const int slot = page_table[min(lane, N - 1)];
+  bf16x8 qn[NKB];
+  {
+    const uint16_t* qrow = q_nope + ((size_t)tq * H + h) * DN + g * 8;
 #pragma unroll
-  for (int i = 0; i < KH0; ++i) asm volatile("" ::"v"(qf[i]));
-  asm volatile("" ::"v"(mw), "v"(slot));
+    for (int kb = 0; kb < NKB; ++kb) qn[kb] = load_bf16x8(qrow + kb * 16);
+  }
+  constexpr int RCH = DR / 8;  // 16-byte chunks of a q_rope row
+  const int rrow = tid / RCH, rch = tid % RCH;
+  uint4 rv = make_uint4(0u, 0u, 0u, 0u);
+  if (rrow < 32) rv = *reinterpret_cast<const uint4*>(q_rope + ((size_t)min(rrow, T - 1) * H + h) * DR + rch * 8);
+  const int slot = page_table[min(lane, N - 1)];
+  wait_vmem_all();
+  __syncthreads();  // W_UK is in LDS (and the mask rows, when built here)
+  const uint32_t mw = parent != nullptr ? smask[tq] : mask[tq];  // T <= 32: one word per node
+
+  // ---- absorption: wave w < AW, latent column blocks w*RBW .. +RBW-1; D[r][t] in registers
+  f32x16 qa[RBW];
+#pragma unroll
+  for (int b = 0; b < RBW; ++b) qa[b] = zero16();
+  if (wave < AW) {
+    const int cl = ((lane & 31) >> 4) * 2 + ((lane & 3) >> 1), sub = (lane & 1) * 8;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      const int krow = kb * 16 + g * 8 + ((lane & 15) >> 2);
+#pragma unroll
+      for (int b = 0; b < RBW; ++b) {
+        const int ch = (wave * RBW + b) * 4 + cl;
+        const bf16x8 a = concat_tr(lds_read_tr16(smem + TL::ckv(krow, ch) + sub),
+                                   lds_read_tr16(smem + TL::ckv(krow + 4, ch) + sub));
+        qa[b] = mfma32(a, qn[kb], qa[b]);
+      }
+    }
+  }
+  __syncthreads();  // W_UK is consumed: its LDS takes the KV tile, the W_UV rows and the q tile
+
+  // ---- the KV rows and this workgroup's W_UV rows by DMA; the q tile (bf16) into LDS
   TileDma<R, DR> dma(c_kv, k_pe, wave, lane);
   dma.target(kvbuf, slot);
 #pragma unroll
@@ -1076,12 +1136,31 @@ __global__ __launch_bounds__(NTHREADS) void short_attn_up_kernel(
     const char* wsrc = reinterpret_cast<const char*>(w_uv + ((size_t)h * DV + v0) * R);
     const uint32_t wl = lds_address(w_s);
 #pragma unroll
-    for (int k = 0; k < WINS / 4; ++k) {
+    for (int k = 0; k < WUV_INS / 4; ++k) {
       const int ins = wave + 4 * k, pos = ins * 64 + lane, r = pos / CPR, p = pos % CPR;
       dma16_lane_addr(wsrc + (size_t)r * (R * 2) + ((p ^ (r & (WSW - 1))) << 4), wl + ins * 1024);
     }
   }
-  wait_vmem_below<WINS / 4>();  // the KV rows of this wave are in LDS; the W_UV rows may still be in flight
+  if (wave < AW) {
+#pragma unroll
+    for (int b = 0; b < RBW; ++b)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        bf16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (__bf16)qa[b][q4 * 4 + e];
+        *reinterpret_cast<bf16x4*>(q_s + c * QP + (wave * RBW + b) * 32 + q4 * 8 + g * 4) = v;
+      }
+  }
+  if (rrow < 32) *reinterpret_cast<uint4*>(q_s + rrow * QP + R + rch * 8) = rv;
+  __syncthreads();  // the q tile is complete
+
+  const int nb = wave & 1, kh = wave >> 1;
+  const int kb0 = EVEN ? kh * KH0 : 0;  // this wave's first score k-step
+  bf16x8 qf[KH0];
+#pragma unroll
+  for (int i = 0; i < KH0; ++i) qf[i] = *reinterpret_cast<const bf16x8*>(q_s + c * QP + (kb0 + i) * 16 + g * 8);
+  wait_vmem_below<WUV_INS / 4>();  // the KV rows of this wave are in LDS; the W_UV rows may still be in flight
   __syncthreads();
 
   // ---- scores: S^T[n][t] for tile rows n = nb*32 + (r/4)*8 + g*4 + r%4 (register r), node t = c
@@ -1197,10 +1276,10 @@ __global__ __launch_bounds__(NTHREADS) void short_attn_up_kernel(
   wait_vmem_all();  // this wave's W_UV rows
   __syncthreads();  // the latent output rows and all of W_UV are in LDS
 
-  // ---- output: D[v][t] = sum_r W_UV[h][v0 + v][r] o[t][r], wave (v block vb, contraction part kq)
-  const int vb = wave % VB, kq = wave / VB;
-  const char* wrow = w_s + (vb * 32 + c) * (R * 2);
-  const int wsz = (vb * 32 + c) & (WSW - 1);
+  // ---- output: D[v][t] = sum_r W_UV[h][v0 + v][r] o[t][r], wave = contraction part kq (one 32-column block)
+  const int kq = wave;
+  const char* wrow = w_s + c * (R * 2);
+  const int wsz = c & (WSW - 1);
   const uint16_t* orow = o_s + tq * OP + g * 8;
   f32x16 u0 = zero16(), u1 = zero16();
 #pragma unroll
@@ -1216,15 +1295,15 @@ __global__ __launch_bounds__(NTHREADS) void short_attn_up_kernel(
   for (int r = 0; r < 16; ++r) u[r] = u0[r] + u1[r];
   if (kq > 0) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) red[(kq - 1) * VB + vb][r][lane] = u[r];
+    for (int r = 0; r < 16; ++r) red[kq - 1][r][lane] = u[r];
   }
   __syncthreads();
   if (kq == 0 && c < T) {
 #pragma unroll
     for (int q = 1; q < KQ; ++q)  // parts in a fixed order
 #pragma unroll
-      for (int r = 0; r < 16; ++r) u[r] += red[(q - 1) * VB + vb][r][lane];
-    uint16_t* dst = out + ((size_t)c * H + h) * DV + v0 + vb * 32 + g * 4;
+      for (int r = 0; r < 16; ++r) u[r] += red[q - 1][r][lane];
+    uint16_t* dst = out + ((size_t)c * H + h) * DV + v0 + g * 4;
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       bf16x4 v;
@@ -1318,7 +1397,7 @@ struct Plan {
   int H, nodes;           // heads, nodes of all requests
   int split_blocks, comb_blocks;
   int comb_rt;            // tree nodes per combine workgroup (4; 2 or 1 for a small single request, 16 for a batch)
-  bool short_seq;         // one request whose L + T rows fit in one KV tile, T <= 32: short_attn_up_kernel
+  bool short_seq;         // one request whose L + T rows fit in one KV tile, T <= 32: short_verify_kernel alone
   BatchArgs<MAX_BATCH> ba;
   size_t off_qcat, off_po, off_pml, total;   // workspace regions (after a KDV_WS_HEADER-byte header)
 };
@@ -1525,17 +1604,18 @@ static void launch_all(const Plan& pl, float sm_scale, const uint16_t* q_nope, c
   uint16_t* part_o = reinterpret_cast<uint16_t*>(ws + pl.off_po);
   float2* part_ml = reinterpret_cast<float2*>(ws + pl.off_pml);
   const float scale_log2 = sm_scale * 1.44269504088896340736f;
+  if (pl.short_seq) {  // the whole call in one kernel (it builds the tree mask itself when given `parent`)
+    const ReqArgs& r = pl.ba.r[0];
+    launch(short_verify_kernel<DN, R, DR, DV>, dim3(pl.H, DV / ShortLayout<DN, R, DR, DV>::VC), st,
+           ev ? ev + 0 : nullptr, q_nope, q_rope, w_uk, w_uv, c_kv, k_pe, page_table, parent,
+           const_cast<uint32_t*>(mask), status, r.L, r.T, pl.H, scale_log2, out, lse, dbg);
+    return;
+  }
   // The query absorption is per node: the packed nodes of all requests in one grid.  With `parent` (one
   // request) an extra block builds the tree mask the split-KV kernel then reads.
   launch(q_absorb_kernel<DN, R, DR>, dim3(pl.H + (parent != nullptr ? 1 : 0), (R + 127) / 128, (pl.nodes + 31) / 32), st,
          ev ? ev + 0 : nullptr, q_nope, q_rope, w_uk, q_cat, pl.nodes, pl.H, parent, const_cast<uint32_t*>(mask),
          status, dbg);
-  if (pl.short_seq) {
-    const ReqArgs& r = pl.ba.r[0];
-    launch(short_attn_up_kernel<R, DR, DV>, dim3(pl.H, DV / (DV >= 64 ? 64 : DV)), st, ev ? ev + 2 : nullptr,
-           (const uint16_t*)q_cat, c_kv, k_pe, page_table, mask, w_uv, r.L, r.T, pl.H, scale_log2, out, lse, dbg);
-    return;
-  }
   if (pl.ba.n == 1) {
     BatchArgs<1> one;
     one.n = 1;
@@ -1593,7 +1673,7 @@ extern "C" size_t kdv_prefix_workspace_bytes(const kdv_mla_dims* d, int32_t T, i
 extern "C" int32_t kdv_verify_kernel_count(const kdv_mla_dims* d, int32_t T, int32_t L) {
   kdv::Plan p;
   if (kdv::make_plan(d, 1, &L, &T, &p) != KDV_OK) return 0;
-  return p.short_seq ? 2 : 3;
+  return p.short_seq ? 1 : 3;
 }
 
 extern "C" int32_t kdv_verify_num_splits(const kdv_mla_dims* d, int32_t T, int32_t L) {

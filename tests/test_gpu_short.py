@@ -1,6 +1,6 @@
 """GPU parity of the short-sequence verify path: one request whose L + T KV rows fit in one 64-row tile and whose
-tree has at most 32 nodes runs the query absorption and then short_attn_up_kernel (scores, a one-tile softmax,
-P V and the W_UV product in one kernel) instead of the split-KV pass and the combine.
+tree has at most 32 nodes runs as one kernel, short_verify_kernel (the query absorption, the scores, a one-tile
+softmax, P V and the W_UV product), instead of the query absorption, the split-KV pass and the combine.
 
 Cases: the tile's edges (N = 1, N = 64 with T = 15 and with T = 32, and the first shapes past them, which take the
 split path), head counts 1..128, chain and star trees, both score distributions, the 64-wide test shape, a pool
@@ -32,8 +32,8 @@ def kernels(inp):
     return kdv.kdv_verify_kernel_count(kdv.make_dims(**inp.dims()), inp.T, inp.L)
 
 
-@pytest.mark.parametrize("L,T,n", [(0, 1, 2), (13, 15, 2), (49, 15, 2), (50, 15, 3), (32, 32, 2), (33, 32, 3),
-                                   (0, 33, 3), (13, 9, 2), (5553, 15, 3)])
+@pytest.mark.parametrize("L,T,n", [(0, 1, 1), (13, 15, 1), (49, 15, 1), (50, 15, 3), (32, 32, 1), (33, 32, 3),
+                                   (0, 33, 3), (13, 9, 1), (5553, 15, 3)])
 def test_kernel_count(L, T, n):
     assert kdv.kdv_verify_kernel_count(kdv.make_dims(**si.KIMI_DIMS, sm_scale=0.072), T, L) == n
 
@@ -49,7 +49,7 @@ def test_kimi_tile_edges(L, T, dist):
 @pytest.mark.parametrize("H", [1, 3, 8, 100, 128])
 def test_kimi_head_counts(H):
     inp = si.make_inputs(**dict(si.KIMI_DIMS, num_heads=H), L=13, T=15, seed=H, dist="unit")
-    assert kernels(inp) == 2
+    assert kernels(inp) == 1
     check(inp)
 
 
@@ -64,7 +64,7 @@ def test_chain_and_star(shape, T):
 @pytest.mark.parametrize("dist", si.DISTRIBUTIONS)
 def test_tiny_shape(L, dist):
     inp = si.make_inputs(**si.TINY_DIMS, L=L, T=7, seed=L, dist=dist, parent=[-1, 0, 0, 1, 1, 2, 2])
-    assert kernels(inp) == 2
+    assert kernels(inp) == 1
     check(inp)
 
 
@@ -94,7 +94,7 @@ def test_forced_splits_take_the_split_path(monkeypatch):
     monkeypatch.setenv("KDV_SPLITS", "1")
     assert kernels(inp) == 3
     monkeypatch.delenv("KDV_SPLITS")
-    assert kernels(inp) == 2
+    assert kernels(inp) == 1
     check(inp, splits=1)
     check(inp)
 
@@ -158,7 +158,7 @@ def test_debug_check_short(monkeypatch, shape):
     monkeypatch.setenv("KDV_DEBUG", "1")
     inp = (si.kimi(L=13, T=15, seed=4, dist="unit") if shape == "kimi" else
            si.make_inputs(**si.TINY_DIMS, L=20, T=7, seed=4, dist="unit", parent=[-1, 0, 0, 1, 1, 2, 2]))
-    assert kernels(inp) == 2
+    assert kernels(inp) == 1
     dev = si.to_device(inp)
     mask, _ = kdv.build_tree_mask(dev["parent"])
     dims = kdv.make_dims(**inp.dims())
