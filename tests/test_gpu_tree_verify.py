@@ -40,7 +40,11 @@ def both(inp, parent=None):
 
 @pytest.mark.parametrize("maker,kw", [(si.tiny, dict(seed=0)), (si.kimi, dict(L=5553, T=15, seed=0)),
                                       (si.kimi, dict(L=100, T=33, seed=1)), (si.kimi, dict(L=0, T=64, seed=2)),
-                                      (si.make_inputs, dict(**si.FULL61_SHAPE, L=1000, T=32, seed=3))])
+                                      (si.make_inputs, dict(**si.FULL61_SHAPE, L=1000, T=32, seed=3)),
+                                      # one-tile sequences: the single short-sequence kernel builds the rows itself
+                                      (si.kimi, dict(L=13, T=15, seed=5)), (si.kimi, dict(L=0, T=32, seed=6)),
+                                      (si.kimi, dict(L=32, T=32, seed=7)),
+                                      (si.make_inputs, dict(**si.TINY_DIMS, L=20, T=7, seed=8))])
 def test_tree_call_equals_mask_then_verify(maker, kw):
     inp = maker(**kw)
     (o1, l1, m1, s1), (o2, l2, m2, s2), _ = both(inp)
@@ -58,8 +62,9 @@ def test_tree_call_matches_oracle():
     assert ok, err
 
 
-def test_tree_call_reports_malformed_tree():
-    inp = si.tiny(seed=1)
+@pytest.mark.parametrize("L", [128, 20])  # (20: the short-sequence kernel)
+def test_tree_call_reports_malformed_tree(L):
+    inp = si.make_inputs(**si.TINY_DIMS, L=L, T=7, seed=1)
     bad = [-1, 0, 5, 1, 1, 2, 2]  # node 2's parent is after it
     (o1, l1, m1, s1), (o2, l2, m2, s2), _ = both(inp, parent=bad)
     ref_mask, ref_status = oracle.tree_mask(bad)
@@ -69,8 +74,9 @@ def test_tree_call_reports_malformed_tree():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
-def test_tree_call_without_status():
-    inp = si.kimi(L=300, T=15, seed=7)
+@pytest.mark.parametrize("L", [300, 13])  # (13: the short-sequence kernel)
+def test_tree_call_without_status(L):
+    inp = si.kimi(L=L, T=15, seed=7)
     dev = si.to_device(inp)
     dims = kdv.make_dims(**inp.dims())
     T, H = inp.T, inp.H
