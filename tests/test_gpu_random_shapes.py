@@ -3,7 +3,7 @@ heads), the prefix length (0..3000, with a bias to one-tile and tile-boundary le
 score distribution, a forced split count (sometimes), and a contiguous or scattered, NaN-poisoned pool.  Each
 output and lse is checked against the oracle on up to four sampled heads, under the same bounds as the other
 parity tests.  The cases cover the three-kernel path, the single short-sequence kernel and forced split plans
-without naming them.
+without naming them.  Twelve more cases draw batches of 2..16 requests with their own prefix lengths and tree sizes.
 """
 import numpy as np
 import pytest
@@ -55,3 +55,21 @@ def test_random_shape(k):
     print(f"case {k}: H={dims['num_heads']} R={dims['kv_lora_rank']} L={L} T={T} {dist} splits={splits} "
           f"scattered={scattered} heads={heads}", flush=True)
     check(inp, heads=heads, splits=splits)
+
+
+# Batches: 2..16 requests with their own prefix lengths (0..2000) and tree sizes (1..64) over one pool, each request's
+# slice against the oracle run on that request alone; sometimes with a forced split count.
+@pytest.mark.parametrize("k", range(12))
+def test_random_batch(k):
+    from tests.test_gpu_batch import check_batch
+    rng = np.random.default_rng([2027, k])
+    dims = dict(si.KIMI_DIMS, num_heads=int(rng.choice([1, 8, 16, 64]))) if rng.random() < 0.6 else dict(si.TINY_DIMS)
+    C = int(rng.integers(2, 17))
+    Ts = [int(t) for t in rng.choice([1, 3, 9, 15, 32, 33, 64], size=C)]
+    Ls = [int(x) for x in (rng.integers(0, 2000, size=C) * (rng.random(C) < 0.8))]
+    dist = str(rng.choice(["literal", "unit"]))
+    splits = int(rng.choice([2, 5])) if rng.random() < 0.25 else None
+    H = dims["num_heads"]
+    heads = None if H <= 4 else [0, H - 1]
+    print(f"batch {k}: H={H} R={dims['kv_lora_rank']} C={C} L={Ls} T={Ts} {dist} splits={splits}", flush=True)
+    check_batch(si.batch_inputs(dims, Ls, Ts, seed=2000 + k, dist=dist), heads=heads, splits=splits)
