@@ -284,15 +284,14 @@ int32_t kdv_verify_num_splits(const kdv_mla_dims* d, int32_t T, int32_t L);
 
 /* Number of kernels one kdv_verify_mla_attn call launches for these arguments: 3 (absorption, split-KV,
  * combine), or 1 (the short-sequence kernel) when L + T <= 64 and T <= 32 and KDV_SPLITS is unset; 0 if
- * unsupported.  The prefix-only call and batches of two or more requests always
- * launch 3. */
+ * unsupported.  The prefix-only call and batches of two or more requests always launch 3. */
 int32_t kdv_verify_kernel_count(const kdv_mla_dims* d, int32_t T, int32_t L);
 
-/* DIAGNOSTIC ONLY, not part of the attention path: a measurement aid for the benchmark.  Launches `blocks` workgroups of 256 threads in which every wave issues `iters`
- * rounds of four independent 32x32x16 bf16 MFMA chains (4 * iters * 32768 flop per wave), the issue-rate
- * ceiling the verify kernels are compared with.  sink: device float [blocks * 256], written (zeros).  Time
- * it with events on `stream`.  Returns KDV_OK, KDV_ERR_NULL, KDV_ERR_SHAPE (iters < 1, blocks outside
- * [1, 2^20]), KDV_ERR_ALIGN, KDV_ERR_HIP. */
+/* DIAGNOSTIC ONLY, not part of the attention path: a measurement aid for the benchmark.  Launches `blocks`
+ * workgroups of 256 threads in which every wave issues `iters` rounds of four independent 32x32x16 bf16 MFMA
+ * chains (4 * iters * 32768 flop per wave), the issue-rate ceiling the verify kernels are compared with.
+ * sink: device float [blocks * 256], written (zeros).  Time it with events on `stream`.  Returns KDV_OK,
+ * KDV_ERR_NULL, KDV_ERR_SHAPE (iters < 1, blocks outside [1, 2^20]), KDV_ERR_ALIGN, KDV_ERR_HIP. */
 int kdv_mfma_probe(int32_t iters, float* sink, int32_t blocks, void* stream);
 
 /* Static English description of a kdv_status value. */
