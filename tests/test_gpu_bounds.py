@@ -1,0 +1,258 @@
+"""GPU: every verify entry point writes only the buffers it is given and reads its inputs without changing them,
+and independent calls on two streams give the bits of the same calls made one after the other.
+
+Guard bytes: each output (out, lse, the workspace; the mask and status of the tree-building call) is a view into a
+larger allocation whose 4 KiB before and after the view hold a fixed byte pattern, and the workspace is exactly
+the size the library asks for.  After the call every guard byte is unchanged, every input tensor is equal to a
+copy taken before it, and the results pass the oracle's parity criterion (sampled heads).  Cases: the
+short-sequence kernel, the three-kernel path at the Kimi shape and at the 64-wide test shape, a 64-node tree with
+8 heads (two mask words, a partial query tile), a three-request batch, the prefix-only call, the tree-building
+call, the no-allocation entry point and the LSE merge.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth_inputs as si
+from tests.parity import lse_passes, lse_tolerance, out_passes
+from tests.test_gpu_batch import _b16
+
+pytestmark = pytest.mark.gpu
+
+kdv = pytest.importorskip("speculative_decoding_tree_parent_amd")
+
+PAD = 4096
+GUARD = 0xA5
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+class Guarded:
+    """A tensor of `shape` and `dtype` placed PAD bytes into an allocation filled with the guard pattern."""
+
+    def __init__(self, shape, dtype, fill=None):
+        nbytes = int(np.prod(shape)) * torch.empty((), dtype=dtype).element_size()
+        self.base = torch.full((PAD + nbytes + PAD,), GUARD, dtype=torch.uint8, device="cuda")
+        self.nbytes = nbytes
+        self.t = self.base[PAD:PAD + nbytes].view(dtype).view(shape)
+        if fill is not None:
+            self.t.fill_(fill)
+
+    def intact(self):
+        b = self.base.cpu().numpy()
+        return bool(np.all(b[:PAD] == GUARD) and np.all(b[PAD + self.nbytes:] == GUARD))
+
+
+def _snapshot(dev):
+    return {k: v.clone() for k, v in dev.items()}
+
+
+def _unchanged(dev, snap):
+    return all(torch.equal(dev[k], snap[k]) for k in snap)
+
+
+def _heads(H):
+    return None if H <= 4 else [0, H // 2, H - 1]
+
+
+def _check(inp, out, lse, heads=None, ref=None):
+    ref_o, ref_l = oracle.verify_inputs(inp, heads=heads) if ref is None else ref
+    got = out.float().cpu().numpy().astype(np.float64)
+    sel = slice(None) if heads is None else (slice(None), list(heads))
+    ok, err = out_passes(got[sel], ref_o[sel])
+    assert ok, f"output parity: {err}"
+    if lse is not None:
+        lok, ratio = lse_passes(lse.cpu().numpy()[sel], ref_l[sel], lse_tolerance(inp, heads)[sel])
+        assert lok, f"lse parity: max |dlse| / bound = {ratio:.3f}"
+
+
+CASES = {
+    "short": lambda: si.kimi(L=13, T=15, seed=1, dist="unit"),
+    "kimi": lambda: si.kimi(L=700, T=15, seed=2, dist="unit"),
+    "tiny": lambda: si.make_inputs(**si.TINY_DIMS, L=300, T=7, seed=3, dist="unit", parent=[-1, 0, 0, 1, 1, 2, 2]),
+    "t64": lambda: si.make_inputs(**dict(si.KIMI_DIMS, num_heads=8), L=300, T=64, seed=4, dist="unit"),
+}
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_verify_writes_only_its_buffers(case):
+    inp = CASES[case]()
+    dev = si.to_device(inp)
+    mask, _ = kdv.build_tree_mask(dev["parent"])
+    dev["mask"] = mask
+    torch.cuda.synchronize()
+    snap = _snapshot(dev)
+    dims = kdv.make_dims(**inp.dims())
+    out = Guarded((inp.T, inp.H, inp.Dv), torch.bfloat16)
+    lse = Guarded((inp.T, inp.H), torch.float32)
+    ws = Guarded((kdv.verify_workspace_bytes(dims, inp.T, inp.L),), torch.uint8, fill=0)
+    kdv.verify_mla_attn(dims, dev["q_nope"], dev["q_rope"], dev["w_uk"], dev["w_uv"], dev["c_kv"], dev["k_pe"],
+                        dev["page_table"], inp.L, mask, out=out.t, lse=lse.t, workspace=ws.t)
+    torch.cuda.synchronize()
+    assert out.intact() and lse.intact() and ws.intact()
+    assert _unchanged(dev, snap)
+    _check(inp, out.t, lse.t, _heads(inp.H))
+
+
+def test_tree_call_writes_only_its_buffers():
+    inp = si.kimi(L=700, T=33, seed=5, dist="unit")
+    dev = si.to_device(inp)
+    snap = _snapshot(dev)
+    dims = kdv.make_dims(**inp.dims())
+    W = (inp.T + 31) // 32
+    mask = Guarded((inp.T, W), torch.int32)
+    status = Guarded((1,), torch.int32)
+    out = Guarded((inp.T, inp.H, inp.Dv), torch.bfloat16)
+    lse = Guarded((inp.T, inp.H), torch.float32)
+    ws = Guarded((kdv.verify_workspace_bytes(dims, inp.T, inp.L),), torch.uint8, fill=0)
+    kdv.verify_mla_attn_tree(dims, dev["q_nope"], dev["q_rope"], dev["w_uk"], dev["w_uv"], dev["c_kv"],
+                             dev["k_pe"], dev["page_table"], inp.L, dev["parent"], mask=mask.t, status=status.t,
+                             out=out.t, lse=lse.t, workspace=ws.t)
+    torch.cuda.synchronize()
+    assert all(g.intact() for g in (mask, status, out, lse, ws))
+    assert _unchanged(dev, snap)
+    assert int(status.t.item()) == 0
+    ref_mask, _ = oracle.tree_mask(inp.parent)
+    assert np.array_equal(mask.t.cpu().numpy().view(np.uint32), ref_mask)
+    _check(inp, out.t, lse.t, _heads(inp.H))
+
+
+def test_batch_writes_only_its_buffers():
+    reqs = si.batch_inputs(si.KIMI_DIMS, [900, 0, 64], [15, 9, 33], seed=6, dist="unit")
+    r0 = reqs[0]
+    dims = kdv.make_dims(**r0.dims())
+    Ls, Ts = [r.L for r in reqs], [r.T for r in reqs]
+    dev = dict(q_nope=_b16([r.q_nope for r in reqs]), q_rope=_b16([r.q_rope for r in reqs]),
+               w_uk=_b16([r0.w_uk]), w_uv=_b16([r0.w_uv]), c_kv=_b16([r0.c_kv]), k_pe=_b16([r0.k_pe]),
+               page_table=torch.from_numpy(np.concatenate([r.page_table for r in reqs]).astype(np.int32)).cuda())
+    mask, status = kdv.build_tree_masks([torch.from_numpy(r.parent.astype(np.int32)).cuda() for r in reqs])
+    dev["mask"] = mask
+    torch.cuda.synchronize()
+    snap = _snapshot(dev)
+    n = sum(Ts)
+    out = Guarded((n, r0.H, r0.Dv), torch.bfloat16)
+    lse = Guarded((n, r0.H), torch.float32)
+    ws = Guarded((kdv.verify_batch_workspace_bytes(dims, Ls, Ts),), torch.uint8, fill=0)
+    kdv.verify_mla_attn_batch(dims, dev["q_nope"], dev["q_rope"], dev["w_uk"], dev["w_uv"], dev["c_kv"],
+                              dev["k_pe"], dev["page_table"], Ls, Ts, mask, out=out.t, lse=lse.t, workspace=ws.t)
+    torch.cuda.synchronize()
+    assert out.intact() and lse.intact() and ws.intact()
+    assert _unchanged(dev, snap)
+    assert np.all(status.cpu().numpy() == 0)
+    n0 = 0
+    for r in reqs:
+        _check(r, out.t[n0:n0 + r.T], lse.t[n0:n0 + r.T], _heads(r.H))
+        n0 += r.T
+
+
+def test_prefix_call_writes_only_its_buffers():
+    inp = si.kimi(L=700, T=15, seed=7, dist="unit")
+    dev = si.to_device(inp)
+    snap = _snapshot(dev)
+    dims = kdv.make_dims(**inp.dims())
+    out = Guarded((inp.T, inp.H, inp.Dv), torch.bfloat16)
+    lse = Guarded((inp.T, inp.H), torch.float32)
+    n = kdv.kdv_prefix_workspace_bytes(dims, inp.T, inp.L)
+    ws = Guarded((n,), torch.uint8, fill=0)
+    kdv.prefix_mla_attn(dims, dev["q_nope"], dev["q_rope"], dev["w_uk"], dev["w_uv"], dev["c_kv"], dev["k_pe"],
+                        dev["page_table"][:inp.L], inp.L, out=out.t, lse=lse.t, workspace=ws.t)
+    torch.cuda.synchronize()
+    assert out.intact() and lse.intact() and ws.intact()
+    assert _unchanged(dev, snap)
+    heads = _heads(inp.H)
+    f = inp.f32
+    ref = oracle.prefix_mla_absorbed(f("q_nope"), f("q_rope"), f("w_uk"), f("w_uv"), f("c_kv"), f("k_pe"),
+                                     inp.page_table, inp.L, inp.sm_scale, heads=heads)
+    _check(inp, out.t, lse.t, heads, ref=ref)
+
+
+def test_noalloc_writes_only_its_buffers():
+    inp = si.kimi(L=700, T=15, seed=8, dist="unit")
+    dev = si.to_device(inp)
+    mask, _ = kdv.build_tree_mask(dev["parent"])
+    dev["mask"] = mask
+    torch.cuda.synchronize()
+    snap = _snapshot(dev)
+    dims = kdv.make_dims(**inp.dims())
+    out = Guarded((inp.T, inp.H, inp.Dv), torch.bfloat16)
+    lse = Guarded((inp.T, inp.H), torch.float32)
+    p = [dev[k].data_ptr() for k in ("q_nope", "q_rope", "w_uk", "w_uv", "c_kv", "k_pe")]
+    rc = kdv.kdv_verify_mla_attn_noalloc(dims, *p, inp.pool_slots, dev["page_table"].data_ptr(), inp.L, inp.T,
+                                         mask.data_ptr(), out.t.data_ptr(), lse.t.data_ptr(),
+                                         torch.cuda.current_stream().cuda_stream)
+    assert rc == kdv.KDV_OK, kdv.kdv_status_string(rc)
+    torch.cuda.synchronize()
+    assert out.intact() and lse.intact()
+    assert _unchanged(dev, snap)
+    _check(inp, out.t, lse.t, _heads(inp.H))
+
+
+def test_merge_writes_only_its_buffers():
+    rng = np.random.default_rng(9)
+    rows, dv = 15 * 64, 128
+    a = torch.from_numpy(rng.standard_normal((rows, dv)).astype(np.float32)).to(torch.bfloat16).cuda()
+    b = torch.from_numpy(rng.standard_normal((rows, dv)).astype(np.float32)).to(torch.bfloat16).cuda()
+    la = torch.from_numpy(rng.standard_normal(rows).astype(np.float32)).cuda()
+    lb = torch.from_numpy(rng.standard_normal(rows).astype(np.float32)).cuda()
+    ins = dict(a=a, b=b, la=la, lb=lb)
+    snap = _snapshot(ins)
+    out = Guarded((rows, dv), torch.bfloat16)
+    lse = Guarded((rows,), torch.float32)
+    kdv.merge_attn_states(a, la, b, lb, out=out.t, lse=lse.t)
+    torch.cuda.synchronize()
+    assert out.intact() and lse.intact()
+    assert _unchanged(ins, snap)
+    ref_o, ref_l = oracle.merge_attn_states(a.float().cpu().numpy().astype(np.float64), la.cpu().numpy().astype(np.float64),
+                                            b.float().cpu().numpy().astype(np.float64), lb.cpu().numpy().astype(np.float64))
+    got = out.t.float().cpu().numpy()
+    assert np.max(np.abs(got - ref_o)) <= 2 ** -8 * np.max(np.abs(ref_o)) + 1e-6
+    assert np.max(np.abs(lse.t.cpu().numpy() - ref_l)) <= 1e-5 * max(1.0, np.max(np.abs(ref_l)))
+
+
+def test_two_streams_match_sequential_calls():
+    """Two independent calls (their own inputs, workspaces and outputs) issued alternately on two streams, five
+    times each: every result bit-identical to the same call made alone."""
+    cases = [si.kimi(L=700, T=15, seed=10, dist="unit"), si.kimi(L=2000, T=9, seed=11, dist="unit")]
+    devs, masks, dims, wss = [], [], [], []
+    for inp in cases:
+        d = si.to_device(inp)
+        m, _ = kdv.build_tree_mask(d["parent"])
+        dm = kdv.make_dims(**inp.dims())
+        devs.append(d)
+        masks.append(m)
+        dims.append(dm)
+        wss.append(torch.zeros((kdv.verify_workspace_bytes(dm, inp.T, inp.L),), dtype=torch.uint8, device="cuda"))
+
+    def call(i, out, lse, stream=None):
+        inp, d = cases[i], devs[i]
+        kdv.verify_mla_attn(dims[i], d["q_nope"], d["q_rope"], d["w_uk"], d["w_uv"], d["c_kv"], d["k_pe"],
+                            d["page_table"], inp.L, masks[i], out=out, lse=lse, workspace=wss[i], stream=stream)
+
+    alone = []
+    for i, inp in enumerate(cases):
+        o = torch.empty((inp.T, inp.H, inp.Dv), dtype=torch.bfloat16, device="cuda")
+        lz = torch.empty((inp.T, inp.H), dtype=torch.float32, device="cuda")
+        call(i, o, lz)
+        torch.cuda.synchronize()
+        alone.append((o.clone(), lz.clone()))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    results = [[], []]
+    for _ in range(5):
+        for i, inp in enumerate(cases):
+            with torch.cuda.stream(streams[i]):
+                o = torch.full((inp.T, inp.H, inp.Dv), float("nan"), dtype=torch.bfloat16, device="cuda")
+                lz = torch.full((inp.T, inp.H), float("nan"), dtype=torch.float32, device="cuda")
+                call(i, o, lz, stream=streams[i])
+            results[i].append((o, lz))
+    torch.cuda.synchronize()
+    for i in range(2):
+        for o, lz in results[i]:
+            assert torch.equal(o, alone[i][0]) and torch.equal(lz, alone[i][1])
+    _check(cases[0], alone[0][0], alone[0][1], _heads(cases[0].H))
