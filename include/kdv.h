@@ -61,7 +61,9 @@ typedef enum kdv_status {
   KDV_ERR_TREE = -3,      /* parent array is not a rooted tree in topological order (device side) */
   KDV_ERR_ALIGN = -4,     /* a bf16/fp32 array or the workspace is not 16-byte aligned            */
   KDV_ERR_WORKSPACE = -5, /* workspace smaller than kdv_verify_workspace_bytes()                  */
-  KDV_ERR_HIP = -6,       /* a HIP launch or query failed                                         */
+  KDV_ERR_HIP = -6,       /* a HIP launch or query of this call failed (every entry point clears   */
+                          /* HIP's per-thread last error before it launches, so an error left by  */
+                          /* earlier work is not reported as this call's; it is not kept either)  */
   KDV_ERR_PAGE = -7       /* a page-table entry outside [0, pool_slots) (device side, KDV_DEBUG)  */
 } kdv_status;
 

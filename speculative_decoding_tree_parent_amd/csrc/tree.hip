@@ -21,8 +21,9 @@ __global__ __launch_bounds__(64) void tree_mask_kernel(const int32_t* __restrict
 //
 // One wave; lane j holds candidate slot j and, once node j exists, node j's score.  Each step the best
 // candidate is found by a wave-wide max of its orderable score bits and, only on an exact tie, a min of
-// (depth, parent, rank), which is unique per candidate.  Every step removes one candidate and adds at most two, so at most budget <= 64 slots
-// are ever in use; the new sibling takes the winner's slot and the new child the lowest free slot.
+// (depth, parent, rank), which is unique per candidate.  Every step removes one candidate and adds at most two,
+// so at most budget <= 64 slots are ever in use; the new sibling takes the winner's slot and the new child the
+// lowest free slot.
 __device__ __forceinline__ uint32_t orderable(float f) {
   const uint32_t u = __float_as_uint(f + 0.f);  // -0 -> +0: equal scores compare equal
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
@@ -182,6 +183,7 @@ extern "C" int kdv_build_tree_mask(const int32_t* parent, int32_t T, uint32_t* m
   if ((reinterpret_cast<uintptr_t>(parent) & 3) || (reinterpret_cast<uintptr_t>(mask) & 3) ||
       (reinterpret_cast<uintptr_t>(status) & 3))
     return KDV_ERR_ALIGN;
+  (void)hipGetLastError();  // (an error left by earlier work is not this call's)
   hipLaunchKernelGGL(kdv::tree_mask_kernel, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream), parent, T,
                      mask, status);
   return hipGetLastError() == hipSuccess ? KDV_OK : KDV_ERR_HIP;
@@ -196,6 +198,7 @@ extern "C" int kdv_tree_accept(const int32_t* parent, const int32_t* tokens, con
   const void* ptrs[] = {parent, tokens, pred, path, n_path, next_token, status};
   for (const void* q : ptrs)
     if (reinterpret_cast<uintptr_t>(q) & 3) return KDV_ERR_ALIGN;
+  (void)hipGetLastError();  // (an error left by earlier work is not this call's)
   hipLaunchKernelGGL(kdv::tree_accept_kernel, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream), parent,
                      tokens, pred, T, path, n_path, next_token, status);
   return hipGetLastError() == hipSuccess ? KDV_OK : KDV_ERR_HIP;
@@ -213,6 +216,7 @@ extern "C" int kdv_build_draft_tree(const float* logp, const int32_t* tok, int32
   const void* ptrs[] = {logp, tok, root_token, parent, tokens, n_nodes};
   for (const void* q : ptrs)
     if (reinterpret_cast<uintptr_t>(q) & 3) return KDV_ERR_ALIGN;
+  (void)hipGetLastError();  // (an error left by earlier work is not this call's)
   hipLaunchKernelGGL(kdv::draft_tree_kernel, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream), logp, tok,
                      block, K, budget, root_token, parent, tokens, n_nodes);
   return hipGetLastError() == hipSuccess ? KDV_OK : KDV_ERR_HIP;

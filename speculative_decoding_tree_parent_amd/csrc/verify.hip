@@ -17,6 +17,7 @@
 // block of output columns) the absorption, the scores, an exact one-tile softmax, P V and the W_UV product.
 #include <hip/hip_ext.h>
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 #include <mutex>
 #include <math.h>
@@ -406,9 +407,10 @@ __device__ __forceinline__ void tile_compute(const char* tile, const bf16x8 (&q)
   }
 }
 
-// The part of a split-KV segment after its prologue: the query tile (staged in LDS at qbuf) into registers, the loop over the segment's KV tiles (the first one already
-// gathered into the first KV buffer, the next tile's page-table slice in slot_v), and the partial (O / l, max,
-// sum) of the segment into partial slot `split`.  All threads of the workgroup call it together.
+// The part of a split-KV segment after its prologue: the query tile (staged in LDS at qbuf) into registers, the
+// loop over the segment's KV tiles (the first one already gathered into the first KV buffer, the next tile's
+// page-table slice in slot_v), and the partial (O / l, max, sum) of the segment into partial slot `split`.  All
+// threads of the workgroup call it together.
 template <int R, int DR>
 __device__ __forceinline__ void seg_body(char* kvbuf, const char* qbuf, uint4 (*pbuf)[2][2][64], float (*mxch)[2][32],
                                          float (*psum)[2][32], TileDma<R, DR>& dma, int slot_v,
@@ -734,7 +736,8 @@ __global__ __launch_bounds__(NTHREADS) void q_absorb_kernel(const uint16_t* __re
                                                             const int32_t* __restrict__ dbg) {
   if (dbg != nullptr && *dbg != KDV_OK && blockIdx.x != H) return;  // page table failed its check (uniform)
   if (blockIdx.x == H) {  // a call that builds its own tree mask has one extra column of blocks (uniform exit)
-    if (blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x < 64) build_ancestor_mask(parent, T, mask, status, threadIdx.x);
+    if (blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x < 64)
+      build_ancestor_mask(parent, T, mask, status, threadIdx.x);
     return;
   }
   __shared__ __attribute__((aligned(1024))) char w_s[DN * 128 * 2];
@@ -1416,10 +1419,15 @@ static ShapeId shape_of(const kdv_mla_dims* d) {
 
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Compute units of the current device, queried once per device (a plan is made on every call).
 static int device_cu_count() {
+  constexpr int MAX_DEV = 64;
+  static std::atomic<int> cached[MAX_DEV];  // 0: not queried yet
   int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return -1;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
+  if (dev < MAX_DEV && (cus = cached[dev].load(std::memory_order_relaxed)) > 0) return cus;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return -1;
+  if (dev < MAX_DEV) cached[dev].store(cus, std::memory_order_relaxed);
   return cus;
 }
 
@@ -1613,9 +1621,9 @@ static void launch_all(const Plan& pl, float sm_scale, const uint16_t* q_nope, c
   }
   // The query absorption is per node: the packed nodes of all requests in one grid.  With `parent` (one
   // request) an extra block builds the tree mask the split-KV kernel then reads.
-  launch(q_absorb_kernel<DN, R, DR>, dim3(pl.H + (parent != nullptr ? 1 : 0), (R + 127) / 128, (pl.nodes + 31) / 32), st,
-         ev ? ev + 0 : nullptr, q_nope, q_rope, w_uk, q_cat, pl.nodes, pl.H, parent, const_cast<uint32_t*>(mask),
-         status, dbg);
+  const dim3 qa_grid(pl.H + (parent != nullptr ? 1 : 0), (R + 127) / 128, (pl.nodes + 31) / 32);
+  launch(q_absorb_kernel<DN, R, DR>, qa_grid, st, ev ? ev + 0 : nullptr, q_nope, q_rope, w_uk, q_cat, pl.nodes, pl.H,
+         parent, const_cast<uint32_t*>(mask), status, dbg);
   if (pl.ba.n == 1) {
     BatchArgs<1> one;
     one.n = 1;
