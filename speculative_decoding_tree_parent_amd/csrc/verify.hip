@@ -159,6 +159,8 @@ struct TileDma {
   uint32_t lbase;
   int slot_v, wave, lane;
   uint32_t voff[4];  // per-lane offsets of a latent row (64-chunk rows: the swizzle repeats every 4 rows)
+  int kp_slot[NKP];  // pool slot of this lane's rotary row in each rotary instruction, taken from slot_v by
+                     // target(), so that the cross-lane read's latency passes before the instruction is issued
 
   __device__ __forceinline__ TileDma(const uint16_t* ckv, const uint16_t* kpe, int wave_, int lane_)
       : c_kv(reinterpret_cast<const char*>(ckv)), k_pe(reinterpret_cast<const char*>(kpe)), lbase(0), slot_v(0),
@@ -169,6 +171,8 @@ struct TileDma {
   __device__ __forceinline__ void target(const char* buf, int slots) {
     lbase = lds_address(buf);
     slot_v = slots;
+#pragma unroll
+    for (int k = 0; k < NKP; ++k) kp_slot[k] = __shfl(slots, ((wave + 4 * k) * 64 + lane) / TL::CP);
   }
   __device__ __forceinline__ void issue(int k) const {
     if (k < NKC) {
@@ -185,8 +189,7 @@ struct TileDma {
       const int j = wave + 4 * (k - NKC);
       if (TL::CP % 4 == 0 || j < TL::CP) {
         const int flat = j * 64 + lane, row = flat / TL::CP, pos = flat % TL::CP;
-        const int slot = __shfl(slot_v, row);
-        dma16_lane_addr(k_pe + (size_t)slot * (DR * 2) + ((pos ^ swz<TL::CP>(row)) << 4),
+        dma16_lane_addr(k_pe + (size_t)kp_slot[k - NKC] * (DR * 2) + ((pos ^ swz<TL::CP>(row)) << 4),
                         lbase + TL::CKV_BYTES + j * 1024);
       }
     }
