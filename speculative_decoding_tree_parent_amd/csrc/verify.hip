@@ -847,9 +847,10 @@ __device__ __forceinline__ void combine_block(const uint16_t* __restrict__ part_
 #pragma unroll
       for (int q = 0; q < CH; ++q) gm = (sp + (s0 + q) * SP < S) ? fmaxf(gm, ml[q].x) : gm;
       const float mn = fmaxf(mx, gm);
-      if (mn == -INFINITY) continue;  // nothing visible in any split so far
+      // (no early exit when nothing is visible yet, mn = -inf: the sums are 0 and every weight below is 0, and
+      // without a branch here the partials' loads go out with the (max, sum) loads instead of after them)
       if (s0 > 0) {
-        const float a = fast_exp2(mx - mn);  // mx = -inf -> 0 (the sums are still 0)
+        const float a = (mn == -INFINITY) ? 1.f : fast_exp2(mx - mn);  // mx = -inf < mn -> 0 (the sums are 0)
         den *= a;
 #pragma unroll
         for (int u = 0; u < CPT; ++u)
