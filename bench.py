@@ -207,10 +207,12 @@ def setup_workload(name, torch, si, dev):
     return S
 
 
-def measure(S, args, torch, kdv, dev, hip, stream, sh, note, K, Wm, full=True):
+def measure(S, args, torch, kdv, dev, hip, stream, sh, note, K, Wm, full=True, reps=1):
     """Times one workload: K steps of the cold rotation and of one hot buffer set, each captured in one HIP graph,
-    and the kernels of each call over eager cold steps (kernel-stamped HIP events).  Returns (result dict, state for
-    the extra rows of the headline)."""
+    and the kernels of each call over eager cold steps (kernel-stamped HIP events).  With reps > 1 each graph is
+    replayed reps times after its untimed replay and the median replay is taken (the other configurations of the
+    metric, whose K steps last well under a millisecond).  Returns (result dict, state for the extra rows of the
+    headline)."""
     H, Dn, Dr, R, Dv, L, T = S.H, S.Dn, S.Dr, S.R, S.Dv, S.L, S.T
     lps = S.layers_per_step
     dims = kdv.make_dims(H, Dn, Dr, R, Dv, S.scale)
@@ -253,8 +255,8 @@ def measure(S, args, torch, kdv, dev, hip, stream, sh, note, K, Wm, full=True):
         for i in range(n):
             fn(sets[i % len(sets)])
 
-    def timed(sets, n, fn=step):
-        """Device time (ms) of n steps: graph-captured unless --no-graph."""
+    def timed(sets, n, fn=step, r=1):
+        """Device time (ms) of n steps: graph-captured unless --no-graph; the median of r timed replays."""
         e0, e1 = hip.event(), hip.event()
         if args.no_graph:
             torch.cuda.synchronize()
@@ -267,22 +269,24 @@ def measure(S, args, torch, kdv, dev, hip, stream, sh, note, K, Wm, full=True):
             run_steps(sets, n, fn)
         g.replay()                       # untimed replay: graph upload, first-touch
         torch.cuda.synchronize()
-        hip.record(e0, sh)
-        g.replay()
-        hip.record(e1, sh)
-        ms = hip.elapsed_ms(e0, e1)
+        ms = []
+        for _ in range(r):
+            hip.record(e0, sh)
+            g.replay()
+            hip.record(e1, sh)
+            ms.append(hip.elapsed_ms(e0, e1))
         torch.cuda.synchronize()
-        return ms
+        return float(np.median(ms))
 
     per_step = {n: lps for n in names}  # (the mask is built inside the first call)
     per_step_eager = dict(tree_mask=1, **per_step)
 
-    def note_timed(what, counts, n):
+    def note_timed(what, counts, n, r=1):
         if args.no_graph:
             note(f"{S.name}: {what}, eager", counts, n)
         else:
             note(f"{S.name}: graph {what}, upload replay", counts, n)
-            note(f"{S.name}: graph {what}, timed replay", counts, n)
+            note(f"{S.name}: graph {what}, timed replay", counts, n * r)
 
     log(f"[bench] {S.name}: warmup {Wm} steps")
     torch.cuda.synchronize()
@@ -292,11 +296,11 @@ def measure(S, args, torch, kdv, dev, hip, stream, sh, note, K, Wm, full=True):
         raise SystemExit("tree status not OK")
     note(f"{S.name}: warm-up", per_step, Wm)
     log(f"[bench] {S.name}: timing {K} steps (cold)")
-    ms_cold = timed(cold_ptrs, K)
-    note_timed("cold", per_step, K)
+    ms_cold = timed(cold_ptrs, K, r=reps)
+    note_timed("cold", per_step, K, reps)
     log(f"[bench] {S.name}: timing {K} steps (hot)")
-    ms_hot = timed(hot_ptrs, K)
-    note_timed("hot", per_step, K)
+    ms_hot = timed(hot_ptrs, K, r=reps)
+    note_timed("hot", per_step, K, reps)
 
     # per-kernel device time and per-step spread: events stamped by each kernel's own dispatch, eager launches
     # queued behind a spin kernel so that they run back to back as in the graph
@@ -351,7 +355,8 @@ def measure(S, args, torch, kdv, dev, hip, stream, sh, note, K, Wm, full=True):
         "buffers": (f"cold: {S.n_cold} distinct layer buffer sets of {S.set_bytes / 2**20:.1f} MiB in rotation, "
                     f"{touched / 2**20:.0f} MiB touched by the {K} timed steps; hot: one set" if lps == 1 else
                     f"cold: 61 distinct layers ({S.set_bytes / 2**30:.2f} GiB) per step; hot: layer 0 61 times"),
-        "timing": ("one HIP graph of K steps" if not args.no_graph else "eager") +
+        "timing": ("eager" if args.no_graph else "one HIP graph of K steps" if reps == 1 else
+                   f"one HIP graph of K steps, median of {reps} replays") +
                   "; eager p10/p50/p90: first kernel's start to last kernel's end of each layer, kernel-stamped events",
     }
     state = dict(dims=dims, fx=fx, ws_bytes=ws_bytes, cold_ptrs=cold_ptrs, out_t=out_t, lse_t=lse_t, wk=wk,
@@ -594,7 +599,7 @@ def run(args, torch, si, kdv, dev, hip, stream, sh):
         for Lx in SWEEP_L:
             for Tx in SWEEP_T:
                 Sx = setup_workload(f"kimi:{Lx}:{Tx}", torch, si, dev)
-                r, _ = measure(Sx, args, torch, kdv, dev, hip, stream, sh, note, Ke, We)
+                r, _ = measure(Sx, args, torch, kdv, dev, hip, stream, sh, note, Ke, We, reps=5)
                 r["bound"] = "hbm (weight streaming)" if Lx <= 1663 else "mfma"
                 sweep.append(r)
                 del Sx
@@ -603,7 +608,7 @@ def run(args, torch, si, kdv, dev, hip, stream, sh):
         for wname in ("long200k", "full61"):
             Sx = setup_workload(wname, torch, si, dev)
             r, _ = measure(Sx, args, torch, kdv, dev, hip, stream, sh, note, min(Ke, 10) if wname == "full61" else Ke,
-                           min(We, 2))
+                           min(We, 2), reps=3)
             extra[wname] = r
             del Sx
             torch.cuda.empty_cache()
