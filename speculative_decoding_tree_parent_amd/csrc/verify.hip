@@ -836,12 +836,27 @@ __device__ __forceinline__ void combine_block(const uint16_t* __restrict__ part_
     for (int s0 = 0; sp + s0 * SP < S; s0 += CH) {  // split of batch slot q: sp + (s0 + q) * SP
       float2 ml[CH];
       bf16x8 v[CH][CPT];
+      if constexpr (CPT == 1 && CPR == 64) {
+        // A row's 64 chunks fill a wave here, so the wave's lanes share one row and one split group: lane q loads
+        // slot q's (max, sum) and every lane reads the CH pairs back from lanes 0 .. CH - 1 (one load instruction
+        // per batch instead of CH).
+        const int sl = min(sp + (s0 + min(lane, CH - 1)) * SP, S - 1);  // past S: repeat split S - 1 (weight 0)
+        const float2 ml_l = part_ml[(size_t)sl * Mp + m];
 #pragma unroll
-      for (int q = 0; q < CH; ++q) {
-        const int sq = min(sp + (s0 + q) * SP, S - 1);  // past S: repeat split S - 1 (weight 0 below)
-        ml[q] = part_ml[(size_t)sq * Mp + m];
+        for (int q = 0; q < CH; ++q) v[q][0] = src[min(sp + (s0 + q) * SP, S - 1) * stride];
 #pragma unroll
-        for (int u = 0; u < CPT; ++u) v[q][u] = src[sq * stride + u];
+        for (int q = 0; q < CH; ++q) {
+          ml[q].x = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ml_l.x), q));
+          ml[q].y = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ml_l.y), q));
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < CH; ++q) {
+          const int sq = min(sp + (s0 + q) * SP, S - 1);  // past S: repeat split S - 1 (weight 0 below)
+          ml[q] = part_ml[(size_t)sq * Mp + m];
+#pragma unroll
+          for (int u = 0; u < CPT; ++u) v[q][u] = src[sq * stride + u];
+        }
       }
       float gm = -INFINITY;
 #pragma unroll
