@@ -585,12 +585,36 @@ __device__ __forceinline__ void splitkv_segment(const uint16_t* __restrict__ q_c
                   scale_log2, mt, split, Mp, part_o, part_ml);
 }
 
+// Blocks past the split-KV blocks of a single request run on CUs the split plan leaves idle; they read W_UV into
+// the caches ahead of the combine, which gathers W_UV[h] on XCD h mod 8.  Block split_blocks + 8 r + x is XCD x's
+// r-th of cnt and reads its share of the heads x, x + 8, ... (whole 16-byte chunks; the loaded words are folded
+// into one register that an empty asm statement takes, so they are waited for but nothing is stored).
+// hch: 16-byte chunks per head (Dv * R / 8).
+__device__ __forceinline__ void wuv_prefetch(const uint16_t* __restrict__ w_uv, int hch, int H, int x, int r, int cnt) {
+  constexpr int U = 16;  // loads in flight per thread
+  const int nh = (H - x + NUM_XCD - 1) / NUM_XCD;
+  const int tot = nh * hch, per = (tot + cnt - 1) / cnt, c0 = r * per, c1 = min(tot, c0 + per);
+  uint32_t acc = 0;
+  for (int cc = c0 + (int)threadIdx.x; cc < c1; cc += NTHREADS * U) {
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int idx = min(cc + u * NTHREADS, c1 - 1);  // (past the share: repeat its last chunk)
+      const int h = x + NUM_XCD * (idx / hch);
+      v[u] = *reinterpret_cast<const uint4*>(w_uv + ((size_t)h * hch + idx % hch) * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  asm volatile("" ::"v"(acc));
+}
+
 template <int R, int DR, int NB>
 __global__ __launch_bounds__(NTHREADS, 1) void splitkv_kernel(
     const uint16_t* __restrict__ q_cat_all, const uint16_t* __restrict__ c_kv, const uint16_t* __restrict__ k_pe,
     const int32_t* __restrict__ page_table_all, const uint32_t* __restrict__ mask_all, const BatchArgs<NB> ba,
     float scale_log2, uint16_t* __restrict__ part_o_all, float2* __restrict__ part_ml_all,
-    const int32_t* __restrict__ dbg) {
+    const int32_t* __restrict__ dbg, const uint16_t* __restrict__ w_uv_pf, int pf_hch) {
   using TL = TileLayout<R, DR>;
   if (dbg != nullptr && *dbg != KDV_OK) return;  // page table failed its check: no gather (uniform)
   __shared__ __attribute__((aligned(1024))) char kvbuf[2 * TL::BYTES];
@@ -638,7 +662,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void splitkv_kernel(
   const int kl = xcd * rq.lin + j;
   const int split = rq.lin > 0 ? kl / m_tiles : (xcd - rq.xoff + NUM_XCD) % NUM_XCD + NUM_XCD * (j / m_tiles);
   const int mt = rq.lin > 0 ? kl % m_tiles : j % m_tiles;
-  if (split >= rq.splits) return;  // padding block (uniform; before any barrier)
+  // A padding block, or one past the split blocks (only with a single request), which reads W_UV ahead (uniform; before
+  // any barrier; the test comes after the placement so that its argument loads go out with the others)
+  if (split >= rq.splits || (NB == 1 && (int)blockIdx.x >= ba.blk_split[1])) {
+    if (NB == 1 && (int)blockIdx.x >= ba.blk_split[1] && w_uv_pf != nullptr) {
+      const int e = blockIdx.x - ba.blk_split[1];
+      wuv_prefetch(w_uv_pf, pf_hch, ba.H, e % NUM_XCD, e / NUM_XCD, (gridDim.x - ba.blk_split[1]) / NUM_XCD);
+    }
+    return;
+  }
   const int ntiles = (rq.N + KV_TILE - 1) / KV_TILE;
   const int tile_begin = split * rq.tiles_per_split;
   const int tile_end = min(tile_begin + rq.tiles_per_split, ntiles);
@@ -1653,15 +1685,20 @@ static void launch_all(const Plan& pl, float sm_scale, const uint16_t* q_nope, c
     one.blk_split[1] = pl.ba.blk_split[1];
     one.blk_comb[1] = pl.ba.blk_comb[1];
     one.r[0] = pl.ba.r[0];
-    launch(splitkv_kernel<R, DR, 1>, dim3(pl.split_blocks), st, ev ? ev + 2 : nullptr, (const uint16_t*)q_cat, c_kv,
-           k_pe, page_table, mask, one, scale_log2, part_o, part_ml, dbg);
+    // CUs the split plan leaves idle (in whole XCD rounds) read W_UV ahead of the combine
+    const int cus = device_cu_count();
+    const int pf_blocks = cus > pl.split_blocks ? (cus - pl.split_blocks) / NUM_XCD * NUM_XCD : 0;
+    launch(splitkv_kernel<R, DR, 1>, dim3(pl.split_blocks + pf_blocks), st, ev ? ev + 2 : nullptr,
+           (const uint16_t*)q_cat, c_kv, k_pe, page_table, mask, one, scale_log2, part_o, part_ml, dbg,
+           pf_blocks > 0 ? w_uv : (const uint16_t*)nullptr, DV * R / 8);
     auto comb = pl.comb_rt == 1 ? combine_up_kernel<R, DV, 1, 1>
                 : pl.comb_rt == 2 ? combine_up_kernel<R, DV, 1, 2> : combine_up_kernel<R, DV, 1, 4>;
     launch_n(comb, dim3(pl.comb_blocks), COMB_THREADS, st, ev ? ev + 4 : nullptr, (const uint16_t*)part_o,
              (const float2*)part_ml, one, w_uv, out, lse, dbg);
   } else {
     launch(splitkv_kernel<R, DR, MAX_BATCH>, dim3(pl.split_blocks), st, ev ? ev + 2 : nullptr,
-           (const uint16_t*)q_cat, c_kv, k_pe, page_table, mask, pl.ba, scale_log2, part_o, part_ml, dbg);
+           (const uint16_t*)q_cat, c_kv, k_pe, page_table, mask, pl.ba, scale_log2, part_o, part_ml, dbg,
+           (const uint16_t*)nullptr, 0);
     launch_n(pl.comb_rt == 16 ? combine_up_kernel<R, DV, MAX_BATCH, 16> : combine_up_kernel<R, DV, MAX_BATCH, 4>,
              dim3(pl.comb_blocks), COMB_THREADS, st, ev ? ev + 4 : nullptr,
              (const uint16_t*)part_o, (const float2*)part_ml, pl.ba, w_uv, out, lse, dbg);
