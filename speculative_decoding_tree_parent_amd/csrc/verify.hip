@@ -587,26 +587,22 @@ __device__ __forceinline__ void splitkv_segment(const uint16_t* __restrict__ q_c
 
 // Blocks past the split-KV blocks of a single request run on CUs the split plan leaves idle; they read W_UV into
 // the caches ahead of the combine, which gathers W_UV[h] on XCD h mod 8.  Block split_blocks + 8 r + x is XCD x's
-// r-th of cnt and reads its share of the heads x, x + 8, ... (whole 16-byte chunks; the loaded words are folded
-// into one register that an empty asm statement takes, so they are waited for but nothing is stored).
-// hch: 16-byte chunks per head (Dv * R / 8).
-__device__ __forceinline__ void wuv_prefetch(const uint16_t* __restrict__ w_uv, int hch, int H, int x, int r, int cnt) {
-  constexpr int U = 16;  // loads in flight per thread
+// r-th of cnt and reads its share of the heads x, x + 8, ... in whole 64-chunk instructions, by LDS DMA into a
+// 1 KB sink per wave that nothing reads, so that all of a wave's loads are in flight together; the wave waits
+// for them once, at the end.  hch_log2: log2 of the 16-byte chunks per head (Dv * R / 8, a power of two).
+__device__ __forceinline__ void wuv_prefetch(const uint16_t* __restrict__ w_uv, int hch_log2, int H, int x, int r,
+                                             int cnt, char* sink) {
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nh = (H - x + NUM_XCD - 1) / NUM_XCD;
-  const int tot = nh * hch, per = (tot + cnt - 1) / cnt, c0 = r * per, c1 = min(tot, c0 + per);
-  uint32_t acc = 0;
-  for (int cc = c0 + (int)threadIdx.x; cc < c1; cc += NTHREADS * U) {
-    uint4 v[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int idx = min(cc + u * NTHREADS, c1 - 1);  // (past the share: repeat its last chunk)
-      const int h = x + NUM_XCD * (idx / hch);
-      v[u] = *reinterpret_cast<const uint4*>(w_uv + ((size_t)h * hch + idx % hch) * 8);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  const int tot = nh << hch_log2, per = ((tot + cnt - 1) / cnt + 63) & ~63;
+  const int c0 = r * per, c1 = min(tot, c0 + per);
+  const uint32_t sl = lds_address(sink) + wave * 1024;
+  for (int i = c0 + wave * 64; i < c1; i += NTHREADS) {  // (uniform) chunks i .. i + 63, lane l takes i + l
+    const int idx = min(i + lane, c1 - 1);
+    const int h = x + NUM_XCD * (idx >> hch_log2);
+    dma16_lane_addr(w_uv + (((size_t)h << hch_log2) + (idx & ((1 << hch_log2) - 1))) * 8, sl);
   }
-  asm volatile("" ::"v"(acc));
+  wait_vmem_all();
 }
 
 template <int R, int DR, int NB>
@@ -614,7 +610,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void splitkv_kernel(
     const uint16_t* __restrict__ q_cat_all, const uint16_t* __restrict__ c_kv, const uint16_t* __restrict__ k_pe,
     const int32_t* __restrict__ page_table_all, const uint32_t* __restrict__ mask_all, const BatchArgs<NB> ba,
     float scale_log2, uint16_t* __restrict__ part_o_all, float2* __restrict__ part_ml_all,
-    const int32_t* __restrict__ dbg, const uint16_t* __restrict__ w_uv_pf, int pf_hch) {
+    const int32_t* __restrict__ dbg, const uint16_t* __restrict__ w_uv_pf, int pf_hch_log2) {
   using TL = TileLayout<R, DR>;
   if (dbg != nullptr && *dbg != KDV_OK) return;  // page table failed its check: no gather (uniform)
   __shared__ __attribute__((aligned(1024))) char kvbuf[2 * TL::BYTES];
@@ -667,7 +663,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void splitkv_kernel(
   if (split >= rq.splits || (NB == 1 && (int)blockIdx.x >= ba.blk_split[1])) {
     if (NB == 1 && (int)blockIdx.x >= ba.blk_split[1] && w_uv_pf != nullptr) {
       const int e = blockIdx.x - ba.blk_split[1];
-      wuv_prefetch(w_uv_pf, pf_hch, ba.H, e % NUM_XCD, e / NUM_XCD, (gridDim.x - ba.blk_split[1]) / NUM_XCD);
+      wuv_prefetch(w_uv_pf, pf_hch_log2, ba.H, e % NUM_XCD, e / NUM_XCD, (gridDim.x - ba.blk_split[1]) / NUM_XCD,
+                   kvbuf);
     }
     return;
   }
@@ -1687,10 +1684,11 @@ static void launch_all(const Plan& pl, float sm_scale, const uint16_t* q_nope, c
     one.r[0] = pl.ba.r[0];
     // CUs the split plan leaves idle (in whole XCD rounds) read W_UV ahead of the combine
     const int cus = device_cu_count();
+    static_assert(((DV * R / 8) & (DV * R / 8 - 1)) == 0, "W_UV chunks per head: a power of two");
     const int pf_blocks = cus > pl.split_blocks ? (cus - pl.split_blocks) / NUM_XCD * NUM_XCD : 0;
     launch(splitkv_kernel<R, DR, 1>, dim3(pl.split_blocks + pf_blocks), st, ev ? ev + 2 : nullptr,
            (const uint16_t*)q_cat, c_kv, k_pe, page_table, mask, one, scale_log2, part_o, part_ml, dbg,
-           pf_blocks > 0 ? w_uv : (const uint16_t*)nullptr, DV * R / 8);
+           pf_blocks > 0 ? w_uv : (const uint16_t*)nullptr, __builtin_ctz(DV * R / 8));
     auto comb = pl.comb_rt == 1 ? combine_up_kernel<R, DV, 1, 1>
                 : pl.comb_rt == 2 ? combine_up_kernel<R, DV, 1, 2> : combine_up_kernel<R, DV, 1, 4>;
     launch_n(comb, dim3(pl.comb_blocks), COMB_THREADS, st, ev ? ev + 4 : nullptr, (const uint16_t*)part_o,
