@@ -207,8 +207,8 @@ def test_merge_writes_only_its_buffers():
     torch.cuda.synchronize()
     assert out.intact() and lse.intact()
     assert _unchanged(ins, snap)
-    ref_o, ref_l = oracle.merge_attn_states(a.float().cpu().numpy().astype(np.float64), la.cpu().numpy().astype(np.float64),
-                                            b.float().cpu().numpy().astype(np.float64), lb.cpu().numpy().astype(np.float64))
+    f64 = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
+    ref_o, ref_l = oracle.merge_attn_states(f64(a), f64(la), f64(b), f64(lb))
     got = out.t.float().cpu().numpy()
     assert np.max(np.abs(got - ref_o)) <= 2 ** -8 * np.max(np.abs(ref_o)) + 1e-6
     assert np.max(np.abs(lse.t.cpu().numpy() - ref_l)) <= 1e-5 * max(1.0, np.max(np.abs(ref_l)))

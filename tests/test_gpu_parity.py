@@ -1,8 +1,8 @@
 """GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the same seeded inputs.
 
 Mask: bit-exact.  Outputs: tests/parity.py (max|diff| <= 2e-2 relative to max(1, max|ref|) and <= 1% of
-max|ref|); lse within the bf16-rounding bound derived in tests/parity.py.  Sizes span several 64-row KV tiles with ragged tails, every tree-size edge
-(1, 32/33 -> two mask words, 64 = maximum), head counts that leave a partial 64-row query tile, forced
+max|ref|); lse within the bf16-rounding bound derived in tests/parity.py.  Sizes span several 64-row KV tiles
+with ragged tails, every tree-size edge (1, 32/33 -> two mask words, 64 = maximum), head counts that leave a partial 64-row query tile, forced
 split counts, the full Kimi-shape workload (64 heads, 15 nodes, 5553-token prefix) in the launch
 configuration the benchmark times, the context sweep (also over seeds 0-9 with unit and peaked scores, and a
 one-bit mask mutation caught at 16384 tokens), a 200k-token prefix scattered over a 262144-slot

@@ -32,7 +32,8 @@ def test_oversized_call_rejected(monkeypatch):
 def test_null_and_shape_errors_before_device_work():
     d = kdv.make_dims(**si.KIMI_DIMS, sm_scale=0.072)
     A = 1 << 20
-    assert kdv.kdv_verify_mla_attn_noalloc(d, A, A, A, A, A, A, 1 << 20, A, 100, 65, A, A, None, None) == kdv.KDV_ERR_SHAPE
+    assert kdv.kdv_verify_mla_attn_noalloc(d, A, A, A, A, A, A, 1 << 20, A, 100, 65, A, A, None, None) \
+        == kdv.KDV_ERR_SHAPE
     assert kdv.kdv_verify_mla_attn_noalloc(d, None, A, A, A, A, A, 1 << 20, A, 100, 15, A, A, None, None) \
         == kdv.KDV_ERR_NULL
 
