@@ -520,7 +520,7 @@ __device__ __forceinline__ void splitkv_segment(const uint16_t* __restrict__ q_c
                                                 char* kvbuf, uint4 (*pbuf)[2][2][64], float (*mxch)[2][32],
                                                 float (*psum)[2][32]) {
   using TL = TileLayout<R, DR>;
-  constexpr int DQ = R + DR, KB = DQ / 16;
+  constexpr int DQ = R + DR;
   const int L = rq.L, T = rq.T, M = rq.T * H, N = rq.N, Mp = rq.Mp;
   const uint16_t* q_cat = q_cat_all + (size_t)rq.node0 * H * DQ;
   const int32_t* page_table = page_table_all + rq.pt0;
@@ -533,8 +533,7 @@ __device__ __forceinline__ void splitkv_segment(const uint16_t* __restrict__ q_c
   float2* part_ml = part_ml_all + pml;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wi = wave >> 1, wj = wave & 1;
-  const int g = lane >> 5, c = lane & 31;
+  const int wi = wave >> 1, c = lane & 31;
   const int m = mt * M_TILE + wi * 32 + c;
 
 
@@ -1006,24 +1005,14 @@ __global__ __launch_bounds__(COMB_THREADS) void combine_up_kernel(const uint16_t
                                                               uint16_t* __restrict__ out_all,
                                                               float* __restrict__ lse_all,
                                                               const int32_t* __restrict__ dbg) {
+  // LDS sizes (combine_block holds the layout and checks the shapes)
   constexpr int CPR = R / 8;                 // 16-byte chunks per latent row
-  constexpr int KS = R / 16;                 // MFMA k-steps
   constexpr int OP = R + 8;                  // LDS pitch of a merged row (elements)
-  constexpr int NFW = 4;                     // fetching waves (4..7); waves 0..3 merge
   constexpr int RC = RT * CPR;               // chunks of the workgroup's rows
   constexpr int CPT = RC > 256 ? RC / 256 : 1;  // chunks per merging thread (16 nodes: 4)
   constexpr int RCT = RC / CPT;              // merging threads per split group
   constexpr int SP = 256 / RCT >= 4 ? 4 : (256 / RCT >= 2 ? 2 : 1);  // split groups merged side by side
-  constexpr int MT = RCT * SP;               // merging threads (in waves 0..3)
-  // splits whose loads are in flight together (17: the most the plan gives 15 query tiles on 256 CUs; fewer
-  // when a thread merges several chunks, to bound its registers)
-  constexpr int CH = CPT == 1 ? 17 : 16 / CPT;
-  constexpr int WSW = CPR < 16 ? CPR : 16;   // W_UV staging swizzle width (chunks)
   constexpr int WBYTES = DV * R * 2;         // all of W_UV[h]
-  constexpr int WINS = WBYTES / 1024 / NFW;  // DMA instructions per fetching wave
-  static_assert(RC % CPT == 0 && CPR % CPT == 0 && MT <= 256 && (CPT == 1 || SP == 1), "merging threads");
-  static_assert(DV % 32 == 0 && DV / 32 <= 4, "one merging wave per 32 output columns");
-  static_assert(WBYTES % (1024 * NFW) == 0, "W_UV must split evenly over the fetching waves");
   __shared__ __attribute__((aligned(16))) uint16_t o_s[RT * OP];
   __shared__ __attribute__((aligned(1024))) char w_s[WBYTES];
   __shared__ float gx[(SP > 1 ? SP * RCT : 1) * 10];  // per split group: max, sum, 8 numerators
