@@ -130,3 +130,21 @@ def test_workload_names():
     assert bench.profile_tag("kimi:16384:15") == "kimi_L16384_T15"
     with pytest.raises(SystemExit):
         bench.parse_workload("sweep:1")
+
+
+def test_committed_profiles_match_the_kernel_source():
+    """The kernel-trace and HBM-traffic summaries under profiles/ were taken from the kernel source as it stands:
+    each names the source hash it was measured on, and roofline.traffic is only read back while that hash
+    matches.  A kernel change makes this fail until the profiles are taken again (profile_bench.sh on the GPU)."""
+    pdir = os.path.join(bench.ROOT, "profiles")
+    names = sorted(f for f in os.listdir(pdir) if f.endswith("_kernel_trace.md") or f.endswith("_hbm_traffic.md"))
+    assert len(names) >= 2, "no profile summaries"
+    want = bench.source_hash()
+    for name in names:
+        text = open(os.path.join(pdir, name)).read()
+        if name.endswith("_kernel_trace.md"):
+            assert f"Kernel source sha256 (first 16 hex): `{want}`" in text, name
+        else:
+            rec = json.loads(text.split("```json\n", 1)[1].split("\n```", 1)[0])
+            assert rec["source_sha256"] == want, name
+    assert bench.traffic_from_profile("kimi5553", "splitkv") is not None
